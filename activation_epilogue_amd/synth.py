@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs for out = act(A@B + bias).
+
+This module only draws random numbers and stores them in the I/O dtype; it
+holds none of the method's arithmetic.  The same bytes feed the device path
+and the FP64 oracle.
+
+Recipe: ``numpy.random.default_rng(seed)`` (PCG64), draws in float64 in the
+order A, B, bias, Y; A and B ~ N(0, 1/K) (1/K is the variance, so the standard
+deviation is K**-0.5), bias ~ N(0, bias_var), Y ~ U(-1, 1) (gate only); each
+array is then stored in the dtype with round-to-nearest-even (numpy's cast for
+fp32/fp16, torch's fp32->bf16 cast for bf16).  Storage: fp32 as float32, fp16
+as float16, bf16 as the uint16 bit pattern.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str
+    act: str
+    bias_var: float = 1.0
+    seed: int = 0
+
+    @property
+    def flops(self) -> int:
+        """GEMM flops 2*M*N*K (epilogue flops are not counted)."""
+        return 2 * self.M * self.N * self.K
+
+
+# The synthetic workloads: named by what they compute and their sizes.
+WORKLOADS = {w.name: w for w in [
+    Workload("relu_f32_127x129x96", 127, 129, 96, "f32", "relu"),
+    Workload("relu_f32_4096x4096x4096", 4096, 4096, 4096, "f32", "relu"),
+    Workload("relu_f16_4096x4096x4096", 4096, 4096, 4096, "f16", "relu"),
+    Workload("relu_bf16_4097x3071x1537", 4097, 3071, 1537, "bf16", "relu"),
+    Workload("glu_f16_1024x21568x4096", 1024, 21568, 4096, "f16", "glu"),
+    Workload("gelu_bf16_8192x14336x4096", 8192, 14336, 4096, "bf16", "gelu_tanh", bias_var=0.1),
+]}
+
+
+def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Store float64 data in the dtype's raw numpy storage, RNE."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x64, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(x64.astype(np.float16))
+    if dtype == "bf16":
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError(dtype)
+
+
+def draw(M, N, K, dtype, act, bias_var=1.0, seed=0, with_bias=True):
+    """Return dict(A, B, bias, Y) of raw storage arrays (Y None unless gate)."""
+    rng = np.random.default_rng(seed)
+    sd = 1.0 / np.sqrt(K) if K > 0 else 1.0
+    A = rng.standard_normal((M, K)) * sd
+    B = rng.standard_normal((K, N)) * sd
+    bias = rng.standard_normal(N) * np.sqrt(bias_var) if with_bias else None
+    Y = rng.uniform(-1.0, 1.0, (M, N)) if act == "glu" else None
+    return {
+        "A": to_storage(A, dtype),
+        "B": to_storage(B, dtype),
+        "bias": None if bias is None else to_storage(bias, dtype),
+        "Y": None if Y is None else to_storage(Y, dtype),
+    }
+
+
+def draw_workload(w: Workload, with_bias=True):
+    return draw(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed, with_bias)
+
+
+def draw_integer(M, N, K, dtype, act, seed=0, amax=2, bias_max=4):
+    """Small-integer inputs: A, B in {-amax..amax}, integer bias, Y in {-1,0,1}.
+
+    With K small enough every partial sum, the bias add and the epilogue are
+    exact in fp32 and the result is representable in the out dtype, so any
+    summation order gives the same bits."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(-amax, amax + 1, (M, K)).astype(np.float64)
+    B = rng.integers(-amax, amax + 1, (K, N)).astype(np.float64)
+    bias = rng.integers(-bias_max, bias_max + 1, N).astype(np.float64)
+    Y = rng.integers(-1, 2, (M, N)).astype(np.float64) if act == "glu" else None
+    return {
+        "A": to_storage(A, dtype),
+        "B": to_storage(B, dtype),
+        "bias": to_storage(bias, dtype),
+        "Y": None if Y is None else to_storage(Y, dtype),
+    }

@@ -1,0 +1,203 @@
+"""FP64 CPU oracle for out = act(A@B + bias) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package.  The product path (the HIP library and its binding)
+never imports, links or calls it, and shares no code with it.
+
+The arithmetic lives in ``fused_linear_oracle.c`` (plain C, FP64, OpenMP over
+output rows, no blocking or fusion).  This module loads it with ctypes,
+building it with gcc first when the shared object is missing or stale, and
+adds the tolerance check used to compare a device result with the oracle.
+
+Sources (page title, section):
+  * "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)": opening formula,
+    per-column bias added once after the K loop, then max(0, .).
+  * "I3. Fuse a GEMM epilogue and change tile scheduling": FP64 reference
+    rounded once at the end ("Why the baseline uses FP32"); grouped program
+    map ("Tiles and grouped ownership").
+  * "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block": the
+    gate X + X*Y.
+  * GELU(tanh): not printed on the pages; Hendrycks & Gimpel (2016).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "fused_linear_oracle.c")
+LIB = os.path.join(HERE, "liborc_fused_linear.so")
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
+# raw numpy storage of each dtype; bf16 travels as its uint16 bit pattern
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+# |dev - ref| <= atol + rtol * |ref|, from the stated parity bar
+TOLERANCE = {"f32": (1e-4, 1e-4), "f16": (4e-3, 1e-2), "bf16": (4e-3, 1e-2)}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain x86-64, -O2, OpenMP)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-D_DEFAULT_SOURCE", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(LIB)
+            p, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            for name in ("orc_fused_linear", "orc_unfused_chain"):
+                f = getattr(lib, name)
+                f.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
+                f.restype = c_int
+            lib.orc_element.argtypes = [c_int, c_int, p, p, p, p, i64, i64, i64, i64, i64, p]
+            lib.orc_element.restype = c_int
+            lib.orc_decode.argtypes = [c_int, p, i64, p]
+            lib.orc_encode.argtypes = [c_int, p, i64, p]
+            lib.orc_tile_of_pid.argtypes = [i64, i64, i64, i64, p, p]
+            lib.orc_gelu_tanh.argtypes = [ctypes.c_double]
+            lib.orc_gelu_tanh.restype = ctypes.c_double
+            lib.orc_max_threads.restype = c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _raw(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != STORAGE[dtype]:
+        raise TypeError(f"{dtype} data must be stored as {STORAGE[dtype].__name__}, got {a.dtype}")
+    return a
+
+
+def _call(fname, A, B, bias, Y, act, dtype, rows, threads, want_x):
+    lib = _load()
+    A, B, bias, Y = (_raw(x, dtype) for x in (A, B, bias, Y))
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("A is (M,K) and B is (K,N)")
+    if bias is not None and bias.shape != (N,):
+        raise ValueError("bias is (N,)")
+    if act == "glu" and (Y is None or Y.shape != (M, N)):
+        raise ValueError("the gate needs Y of shape (M,N)")
+    if rows is None:
+        nrows, rows_arr = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    out = np.empty((nrows, N), dtype=STORAGE[dtype])
+    x = np.empty((nrows, N), dtype=np.float64) if want_x else None
+    st = getattr(lib, fname)(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(Y),
+                             _ptr(out), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(x))
+    if st != 0:
+        raise RuntimeError(f"{fname} failed with status {st}")
+    return (out, x) if want_x else out
+
+
+def fused_linear(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None, want_x=False):
+    """round_once(act(A@B + bias)) in the storage type of ``dtype``.
+
+    ``rows`` selects output rows (the result then has len(rows) rows).
+    ``want_x`` also returns the unrounded FP64 epilogue value."""
+    return _call("orc_fused_linear", A, B, bias, Y, act, dtype, rows, threads, want_x)
+
+
+def unfused_chain(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None):
+    """round(act(round(round(A@B) + bias))): separate stages, each stored in dtype."""
+    return _call("orc_unfused_chain", A, B, bias, Y, act, dtype, rows, threads, False)
+
+
+def element(A, B, bias, Y, act, dtype, i, j):
+    """Unrounded FP64 act(A[i,:]@B[:,j] + bias[j])."""
+    lib = _load()
+    A, B, bias, Y = (_raw(x, dtype) for x in (A, B, bias, Y))
+    M, K = A.shape
+    N = B.shape[1]
+    v = ctypes.c_double()
+    st = lib.orc_element(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(Y),
+                         M, N, K, int(i), int(j), ctypes.addressof(v))
+    if st != 0:
+        raise RuntimeError("orc_element failed")
+    return v.value
+
+
+def decode(raw, dtype):
+    raw = _raw(np.asarray(raw), dtype)
+    out = np.empty(raw.shape, dtype=np.float64)
+    _load().orc_decode(DTYPES[dtype], _ptr(raw), raw.size, _ptr(out))
+    return out
+
+
+def encode(x, dtype):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=STORAGE[dtype])
+    _load().orc_encode(DTYPES[dtype], _ptr(x), x.size, _ptr(out))
+    return out
+
+
+def gelu_tanh(x):
+    f = _load().orc_gelu_tanh
+    return np.vectorize(lambda v: f(float(v)), otypes=[np.float64])(x)
+
+
+def tile_of_pid(pid, tiles_m, tiles_n, group):
+    m, n = ctypes.c_int64(), ctypes.c_int64()
+    st = _load().orc_tile_of_pid(pid, tiles_m, tiles_n, group, ctypes.addressof(m), ctypes.addressof(n))
+    if st != 0:
+        raise ValueError("pid or tiling out of range")
+    return m.value, n.value
+
+
+def max_threads():
+    return _load().orc_max_threads()
+
+
+def compare(dev_raw, ref_raw, dtype, atol=None, rtol=None):
+    """Element-wise |dev - ref| <= atol + rtol*|ref| in FP64.
+
+    Both arguments are raw storage arrays of ``dtype``; ``ref`` is the oracle's
+    once-rounded output.  Returns a dict with ok, max_abs, max_rel, violations
+    and the index of the worst violation (or None).  NaN anywhere fails."""
+    d_atol, d_rtol = TOLERANCE[dtype]
+    atol = d_atol if atol is None else atol
+    rtol = d_rtol if rtol is None else rtol
+    dev = decode(np.asarray(dev_raw), dtype)
+    ref = decode(np.asarray(ref_raw), dtype)
+    if dev.shape != ref.shape:
+        raise ValueError(f"shape mismatch {dev.shape} vs {ref.shape}")
+    diff = np.abs(dev - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(diff <= bound)  # NaN compares false -> counted as a violation
+    nviol = int(bad.sum())
+    rel = diff / np.maximum(np.abs(ref), 1e-30)
+    worst = None
+    if nviol:
+        worst = tuple(int(v) for v in np.unravel_index(np.argmax(np.where(bad, diff - bound, -np.inf)), dev.shape))
+    return {
+        "ok": nviol == 0,
+        "max_abs": float(np.nanmax(diff)) if diff.size else 0.0,
+        "max_rel": float(np.nanmax(rel)) if rel.size else 0.0,
+        "violations": nviol,
+        "worst": worst,
+    }

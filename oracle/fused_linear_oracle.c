@@ -1,0 +1,312 @@
+/*
+ * fused_linear_oracle.c -- plain FP64 CPU oracle for out = act(A@B + bias).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or helper with
+ * the HIP library: it has its own fp16/bf16 decoders and encoders, its own
+ * tile map and its own GELU.
+ *
+ * What it computes (the plain definition, written out, no blocking, no
+ * fusion, no reordering):
+ *   X[i,j]   = sum_k A[i,k] * B[k,j]              (FP64, k ascending)
+ *   X[i,j]  += bias[j]                            (once, by column)
+ *   out[i,j] = act(X[i,j]) (or X + X*Y for the gate)
+ *   out      = round_to_nearest_even(out, dtype)  (once, at the end)
+ *
+ * Sources (page title, section):
+ *   - "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", opening formula
+ *     and the note under it: per-column bias broadcast over rows, added once
+ *     after the K loop, then max(0, .).
+ *   - "Epilogue concept", "Where the accumulator is finally correct": the
+ *     loop nest acc=0; acc += A*B over k; epilogue; one store.
+ *   - "I3. Fuse a GEMM epilogue and change tile scheduling", intro and
+ *     "Why the baseline uses FP32": the correctness reference is an FP64
+ *     GEMM+bias+activation rounded once at the end; the output dtype is the
+ *     input dtype.  "Tiles and grouped ownership": the grouped program-id map
+ *     with actual_group = min(GROUP, tiles_m - first_m).
+ *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block":
+ *     X = A@B + bias, out = X + X*Y.
+ *   - GELU: the pages name it as a fusable activation but print no formula;
+ *     this file uses the tanh form of Hendrycks & Gimpel (2016),
+ *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with libm tanh.
+ *
+ * Rounding: round-to-nearest, ties-to-even (the IEEE default; the pages do
+ * not name a mode), computed directly from FP64 with rint(), including
+ * subnormals and overflow to infinity.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_NONE = 0, ORC_RELU = 1, ORC_GELU_TANH = 2, ORC_GLU = 3 };
+
+/* ---------------------------------------------------------------- decode */
+
+static double dec_f16(uint16_t h) {
+    int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-14 * 2^-10 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/2^10) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+static double dec_bf16(uint16_t b) {
+    /* bf16 is the top half of a binary32: widen the bit pattern. */
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double dec_one(int dtype, const void *p, int64_t i) {
+    if (dtype == ORC_F32) return (double)((const float *)p)[i];
+    if (dtype == ORC_F16) return dec_f16(((const uint16_t *)p)[i]);
+    return dec_bf16(((const uint16_t *)p)[i]);
+}
+
+int orc_decode(int dtype, const void *src, int64_t n, double *dst) {
+    if (dtype < 0 || dtype > 2 || n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = dec_one(dtype, src, i);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- encode */
+
+/* Round x to a binary format with p significand bits (implicit bit included),
+ * minimum normal exponent emin and maximum exponent emax; RNE; overflow to
+ * +-inf.  Returns the rounded value as a double (exactly representable). */
+static double round_fmt(double x, int p, int emin, int emax) {
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    int e2;
+    frexp(x, &e2);              /* x = f * 2^e2, 0.5 <= |f| < 1 */
+    int E = e2 - 1;             /* unbiased exponent of x */
+    if (E < emin) E = emin;     /* below the normal range the quantum is fixed */
+    int q = E - (p - 1);        /* exponent of one unit in the last place */
+    double r = ldexp(rint(ldexp(x, -q)), q);
+    if (fabs(r) >= ldexp(1.0, emax + 1)) return copysign(INFINITY, x);
+    return r;
+}
+
+static uint16_t enc_small(double x, int ebits, int mbits) {
+    /* x must already be rounded to the format. */
+    int bias = (1 << (ebits - 1)) - 1;
+    int emin = 1 - bias;
+    uint16_t s = signbit(x) ? 1 : 0;
+    uint16_t sign = (uint16_t)(s << (ebits + mbits));
+    uint16_t expmask = (uint16_t)(((1 << ebits) - 1) << mbits);
+    if (isnan(x)) return (uint16_t)(expmask | (1 << (mbits - 1)));
+    if (isinf(x)) return (uint16_t)(sign | expmask);
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    if (E < emin) { /* subnormal */
+        uint16_t m = (uint16_t)ldexp(a, -(emin - mbits));
+        return (uint16_t)(sign | m);
+    }
+    uint16_t m = (uint16_t)(ldexp(a, mbits - E) - ldexp(1.0, mbits));
+    return (uint16_t)(sign | ((E + bias) << mbits) | m);
+}
+
+static void enc_one(int dtype, double x, void *p, int64_t i) {
+    if (dtype == ORC_F32) {
+        ((float *)p)[i] = (float)round_fmt(x, 24, -126, 127); /* exact */
+    } else if (dtype == ORC_F16) {
+        ((uint16_t *)p)[i] = enc_small(round_fmt(x, 11, -14, 15), 5, 10);
+    } else {
+        ((uint16_t *)p)[i] = enc_small(round_fmt(x, 8, -126, 127), 8, 7);
+    }
+}
+
+int orc_encode(int dtype, const double *src, int64_t n, void *dst) {
+    if (dtype < 0 || dtype > 2 || n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i) enc_one(dtype, src[i], dst, i);
+    return 0;
+}
+
+/* ------------------------------------------------------------ activation */
+
+double orc_gelu_tanh(double x) {
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+}
+
+static double apply_act(int act, double x, double y) {
+    switch (act) {
+    case ORC_RELU: return x > 0.0 ? x : 0.0;  /* max(0, x) */
+    case ORC_GELU_TANH: return orc_gelu_tanh(x);
+    case ORC_GLU: return x + x * y;           /* the gate X + X*Y */
+    default: return x;
+    }
+}
+
+/* ------------------------------------------------------- fused reference */
+
+/* One output row i of X = A@B (FP64, k ascending), into acc[0..N). */
+static void row_product(const double *A64row, const double *B64, double *acc,
+                        int64_t N, int64_t K) {
+    for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double a = A64row[k];
+        const double *b = B64 + k * N;
+        for (int64_t j = 0; j < N; ++j) acc[j] += a * b[j];
+    }
+}
+
+static int check_args(int dtype, int act, const void *A, const void *B,
+                      const void *Y, const void *out, int64_t M, int64_t N,
+                      int64_t K) {
+    if (dtype < 0 || dtype > 2 || act < 0 || act > 3) return 1;
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (!out && M * N > 0) return 1;
+    if ((!A && M * K > 0) || (!B && K * N > 0)) return 1;
+    if (act == ORC_GLU && !Y && M * N > 0) return 1;
+    return 0;
+}
+
+/*
+ * out (nrows x N, dtype) = round(act(A[rows]@B + bias)).
+ * rows == NULL computes every row (nrows must equal M).  bias may be NULL
+ * (counts as zero).  Y is (M, N) and read only for the gate.  x_out, when not
+ * NULL, receives the unrounded FP64 value after the epilogue (nrows x N).
+ * unfused != 0 switches to the three-stage chain that rounds after every
+ * stage: round(act(round(round(A@B) + bias))), which is what separate
+ * GEMM, bias and activation kernels each storing in dtype compute.
+ */
+static int run(int dtype, int act, const void *A, const void *B,
+               const void *bias, const void *Y, void *out, int64_t M,
+               int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+               int nthreads, double *x_out, int unfused) {
+    if (check_args(dtype, act, A, B, Y, out, M, N, K)) return 1;
+    if (!rows) nrows = M;
+    if (nrows < 0) return 1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M) return 1;
+    if (nrows == 0 || N == 0) return 0;
+
+    double *B64 = (double *)malloc(sizeof(double) * (size_t)(K * N + 1));
+    double *bias64 = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!B64 || !bias64) { free(B64); free(bias64); return 2; }
+    orc_decode(dtype, B, K * N, B64);
+    for (int64_t j = 0; j < N; ++j) bias64[j] = bias ? dec_one(dtype, bias, j) : 0.0;
+
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+        double *arow = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+        if (!acc || !arow) {
+#pragma omp atomic write
+            status = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t i = rows ? rows[r] : r;
+                for (int64_t k = 0; k < K; ++k) arow[k] = dec_one(dtype, A, i * K + k);
+                row_product(arow, B64, acc, N, K);
+                for (int64_t j = 0; j < N; ++j) {
+                    double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
+                    double x = acc[j], v;
+                    if (!unfused) {
+                        v = apply_act(act, x + bias64[j], y);
+                    } else {
+                        double tmp[1];
+                        uint16_t h[2];
+                        float f[1];
+                        void *slot = (dtype == ORC_F32) ? (void *)f : (void *)h;
+                        /* stage 1: the GEMM stores X in dtype */
+                        tmp[0] = x; orc_encode(dtype, tmp, 1, slot); orc_decode(dtype, slot, 1, tmp);
+                        /* stage 2: the bias pass stores X + bias in dtype */
+                        tmp[0] = tmp[0] + bias64[j]; orc_encode(dtype, tmp, 1, slot); orc_decode(dtype, slot, 1, tmp);
+                        /* stage 3: the activation pass */
+                        v = apply_act(act, tmp[0], y);
+                    }
+                    if (x_out) x_out[r * N + j] = v;
+                    enc_one(dtype, v, out, r * N + j);
+                }
+            }
+        }
+        free(acc);
+        free(arow);
+    }
+    free(B64);
+    free(bias64);
+    return status;
+}
+
+int orc_fused_linear(int dtype, int act, const void *A, const void *B,
+                     const void *bias, const void *Y, void *out, int64_t M,
+                     int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                     int nthreads, double *x_out) {
+    return run(dtype, act, A, B, bias, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0);
+}
+
+int orc_unfused_chain(int dtype, int act, const void *A, const void *B,
+                      const void *bias, const void *Y, void *out, int64_t M,
+                      int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                      int nthreads, double *x_out) {
+    return run(dtype, act, A, B, bias, Y, out, M, N, K, rows, nrows, nthreads, x_out, 1);
+}
+
+/* Single output element (i, j), FP64, unrounded: act(sum_k A[i,k]B[k,j] + bias[j]). */
+int orc_element(int dtype, int act, const void *A, const void *B,
+                const void *bias, const void *Y, int64_t M, int64_t N,
+                int64_t K, int64_t i, int64_t j, double *value) {
+    if (check_args(dtype, act, A, B, Y, value, M, N, K)) return 1;
+    if (i < 0 || i >= M || j < 0 || j >= N) return 1;
+    double x = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        x += dec_one(dtype, A, i * K + k) * dec_one(dtype, B, k * N + j);
+    x += bias ? dec_one(dtype, bias, j) : 0.0;
+    double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
+    *value = apply_act(act, x, y);
+    return 0;
+}
+
+/* --------------------------------------------------------------- tile map */
+
+/*
+ * Grouped program-id -> (m_tile, n_tile) map ("Tiles and grouped
+ * ownership"): programs sweep a band of `group` M-tiles down each N column
+ * before moving right; the last band may hold fewer M-tiles, so the band
+ * height is min(group, tiles_m - first_m) before the remainder/quotient.
+ */
+int orc_tile_of_pid(int64_t pid, int64_t tiles_m, int64_t tiles_n,
+                    int64_t group, int64_t *m_tile, int64_t *n_tile) {
+    if (tiles_m <= 0 || tiles_n <= 0 || group <= 0) return 1;
+    if (pid < 0 || pid >= tiles_m * tiles_n) return 1;
+    int64_t per_band = group * tiles_n;
+    int64_t band = pid / per_band;
+    int64_t first_m = band * group;
+    int64_t height = tiles_m - first_m;
+    if (height > group) height = group;
+    int64_t r = pid % per_band;
+    *m_tile = first_m + r % height;
+    *n_tile = r / height;
+    return 0;
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
