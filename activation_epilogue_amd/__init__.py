@@ -1,0 +1,204 @@
+"""activation_epilogue_amd -- gfx950 fused linear layer, out = act(A@B + bias).
+
+Thin ctypes binding over ``libfused_linear.so`` (C ABI in
+``include/fused_linear.h``).  This module only marshals arguments: it checks
+tensor shapes, dtypes and devices, takes raw device pointers and the current
+HIP stream from PyTorch, and calls the library.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback.  If the library has
+not been built, importing works but every call raises ``LibraryNotBuilt``.
+
+Entry points (same names as the C ABI, without the ``fl_`` prefix):
+  fused_linear(A, B, bias=None, Y=None, act="relu", out=None, **options)
+  gemm(A, B, X=None)                      # unfused step 1: X = A@B
+  bias_add(X, bias)                       # unfused step 2: X += bias (in place)
+  activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
+  tile_grid(M, N, K, dtype, **options), tile_of_program(...), version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfused_linear.so")
+
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
+EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_gemm", "fl_bias_add", "fl_activation",
+           "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class FusedLinearError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Options(ctypes.Structure):
+    """Mirror of fl_options."""
+    _fields_ = [("group_m", ctypes.c_int32), ("persistent", ctypes.c_int32), ("tile_cfg", ctypes.c_int32),
+                ("no_xcd_remap", ctypes.c_int32), ("debug_tile_count", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load (once) and return the ctypes handle of libfused_linear.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                              " or `python activation_epilogue_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    lib.fl_fused_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp]
+    lib.fl_fused_linear_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, ctypes.POINTER(Options)]
+    lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
+    lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
+    lib.fl_activation.argtypes = [vp, vp, vp, i64, i64, c_int, c_int, vp]
+    lib.fl_tile_grid.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(Options), P_i32, P_i32, P_i32, P_i32]
+    lib.fl_tile_of_program.argtypes = [i32, i32, i32, i32, i32, i32, P_i32, P_i32]
+    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_gemm", "fl_bias_add", "fl_activation",
+              "fl_tile_grid", "fl_tile_of_program"):
+        getattr(lib, f).restype = c_int
+    lib.fl_status_string.argtypes = [c_int]
+    lib.fl_status_string.restype = ctypes.c_char_p
+    lib.fl_last_error.restype = ctypes.c_char_p
+    lib.fl_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise FusedLinearError(status, load_library().fl_last_error().decode())
+
+
+def _dtype_code(dtype):
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}; use float32, float16 or bfloat16")
+    return codes[dtype]
+
+
+def _dev_ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr() or None
+
+
+def _stream(t, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _options(group_m=0, persistent=0, tile_cfg=0, no_xcd_remap=0, debug_tile_count=None):
+    ptr = None
+    if debug_tile_count is not None:
+        import torch
+        if debug_tile_count.dtype != torch.int32 or not debug_tile_count.is_cuda:
+            raise TypeError("debug_tile_count must be an int32 device tensor")
+        ptr = debug_tile_count.data_ptr()
+    return Options(int(group_m), int(persistent), int(tile_cfg), int(no_xcd_remap), ptr)
+
+
+def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, stream=None, **options):
+    """out = act(A@B + bias) in one kernel.  A (M,K), B (K,N), bias (N,),
+    Y (M,N) for act="glu" (out = X + X*Y).  Returns out (allocated with torch
+    if not given).  Keyword options map to fl_options (group_m, persistent,
+    tile_cfg, no_xcd_remap, debug_tile_count)."""
+    import torch
+    lib = load_library()
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError("A must be (M,K) and B (K,N)")
+    M, K = A.shape
+    N = B.shape[1]
+    dt = A.dtype
+    code = _dtype_code(dt)
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=A.device)
+    args = (_dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(bias, "bias", dt, (N,)),
+            _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", dt, (M, N)), M, N, K, ACTS[act], code,
+            _stream(A, stream))
+    if options:
+        opt = _options(**options)
+        _check(lib.fl_fused_linear_ex(*args, ctypes.byref(opt)))
+    else:
+        _check(lib.fl_fused_linear(*args))
+    return out
+
+
+def gemm(A, B, X=None, *, stream=None):
+    """Unfused step 1: X = A@B, stored in the I/O dtype."""
+    import torch
+    lib = load_library()
+    M, K = A.shape
+    N = B.shape[1]
+    dt = A.dtype
+    if X is None:
+        X = torch.empty((M, N), dtype=dt, device=A.device)
+    _check(lib.fl_gemm(_dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(X, "X", dt, (M, N)),
+                       M, N, K, _dtype_code(dt), _stream(A, stream)))
+    return X
+
+
+def bias_add(X, bias, *, stream=None):
+    """Unfused step 2: X[i,j] += bias[j] in place."""
+    lib = load_library()
+    M, N = X.shape
+    dt = X.dtype
+    _check(lib.fl_bias_add(_dev_ptr(X, "X", dt), _dev_ptr(bias, "bias", dt, (N,)), M, N, _dtype_code(dt),
+                           _stream(X, stream)))
+    return X
+
+
+def activation(X, Y=None, out=None, act="relu", *, stream=None):
+    """Unfused step 3: out = act(X) (or X + X*Y for act="glu"); out may be X."""
+    import torch
+    lib = load_library()
+    M, N = X.shape
+    dt = X.dtype
+    if out is None:
+        out = torch.empty_like(X)
+    _check(lib.fl_activation(_dev_ptr(X, "X", dt), _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", dt, (M, N)),
+                             M, N, ACTS[act], _dtype_code(dt), _stream(X, stream)))
+    return out
+
+
+def tile_grid(M, N, K, dtype_code, **options):
+    """(block_m, block_n, tiles_m, tiles_n) the fused kernel uses."""
+    lib = load_library()
+    opt = _options(**options)
+    vals = [ctypes.c_int32() for _ in range(4)]
+    _check(lib.fl_tile_grid(M, N, K, dtype_code, ctypes.byref(opt), *[ctypes.byref(v) for v in vals]))
+    return tuple(v.value for v in vals)
+
+
+def tile_of_program(program, grid, tiles_m, tiles_n, group_m, xcd_remap):
+    """(m_tile, n_tile) computed by program `program` (host copy of the device map)."""
+    lib = load_library()
+    m, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.fl_tile_of_program(program, grid, tiles_m, tiles_n, group_m, xcd_remap, ctypes.byref(m),
+                                  ctypes.byref(n)))
+    return m.value, n.value
+
+
+def version():
+    return load_library().fl_version()

@@ -1,0 +1,348 @@
+// fused_linear.hip -- host side of the C ABI declared in include/fused_linear.h:
+// argument validation, tile/launch selection and kernel launches on the
+// caller's stream.  All device code is in fl_kernels.hpp.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "fl_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+fl_status fail(fl_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+size_t elem_size(int dtype) { return dtype == FL_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == FL_F32 || d == FL_F16 || d == FL_BF16; }
+bool valid_act(int a) { return a >= FL_ACT_NONE && a <= FL_ACT_GLU; }
+
+bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
+    if (!a || !b || abytes == 0 || bbytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+// Per-device compute-unit count, read once per device.
+int cu_count() {
+    static std::mutex mu;
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// ---------------------------------------------------------- launch tables
+
+// The fused kernels of each dtype are compiled in their own translation unit
+// (fl_fused_inst.hip built once per dtype) so the build runs in parallel.
+fl::fused_launcher pick_fused(int dtype, int act, bool vec) {
+    if (dtype == FL_F32) return fl::pick_fused_for<FL_F32>(act, vec);
+    if (dtype == FL_F16) return fl::pick_fused_for<FL_F16>(act, vec);
+    return fl::pick_fused_for<FL_BF16>(act, vec);
+}
+
+struct TileShape {
+    int bm, bn;
+};
+
+fl_status tile_shape(const fl_options *opt, TileShape &t) {
+    const int cfg = opt ? opt->tile_cfg : 0;
+    if (cfg == 0 || cfg == 1) {
+        t = {256, 256};
+        return FL_OK;
+    }
+    return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+}
+
+int grid_elementwise(int64_t work_items) {
+    int64_t blocks = (work_items + fl::kThreads - 1) / fl::kThreads;
+    const int64_t cap = (int64_t)cu_count() * 16;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return (int)blocks;
+}
+
+fl_status check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FL_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return FL_OK;
+}
+
+fl_status check_dims(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0)
+        return fail(FL_ERR_INVALID_ARG, "negative size (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N,
+                    (long long)K);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(FL_ERR_UNSUPPORTED, "sizes above 2^31-1 are not supported");
+    return FL_OK;
+}
+
+// Shared validation of the GEMM-shaped entry points.
+fl_status validate_gemm(const void *A, const void *B, const void *bias, const void *Y, const void *out, int64_t M,
+                        int64_t N, int64_t K, int act, int dtype, const fl_options *opt) {
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", act);
+    fl_status s = check_dims(M, N, K);
+    if (s != FL_OK) return s;
+    if (opt) {
+        if (opt->group_m < 0) return fail(FL_ERR_INVALID_ARG, "group_m must be >= 1 (0 = default)");
+        if (opt->persistent != 0 && opt->persistent != 1)
+            return fail(FL_ERR_INVALID_ARG, "persistent must be 0 or 1");
+        if (opt->no_xcd_remap != 0 && opt->no_xcd_remap != 1)
+            return fail(FL_ERR_INVALID_ARG, "no_xcd_remap must be 0 or 1");
+        TileShape t;
+        s = tile_shape(opt, t);
+        if (s != FL_OK) return s;
+    }
+    const size_t es = elem_size(dtype);
+    // In-tile byte offsets are 32-bit: 256 rows of A, of Y and of out must span < 2^31 bytes.
+    if ((size_t)K * es * 256 >= 0x80000000ull || (size_t)N * es * 256 >= 0x80000000ull)
+        return fail(FL_ERR_UNSUPPORTED, "K or N too large (256 rows must span < 2 GiB)");
+    const size_t a_bytes = (size_t)M * K * es, b_bytes = (size_t)K * N * es, o_bytes = (size_t)M * N * es;
+    const size_t bias_bytes = bias ? (size_t)N * es : 0;
+    if (!A && a_bytes) return fail(FL_ERR_INVALID_ARG, "A is NULL");
+    if (!B && b_bytes) return fail(FL_ERR_INVALID_ARG, "B is NULL");
+    if (!out && o_bytes) return fail(FL_ERR_INVALID_ARG, "out is NULL");
+    if (act == FL_ACT_GLU && !Y && o_bytes) return fail(FL_ERR_INVALID_ARG, "the gate needs Y");
+    if (act != FL_ACT_GLU && Y) return fail(FL_ERR_INVALID_ARG, "Y is only used by the gate (FL_ACT_GLU)");
+    const void *ptrs[5] = {A, B, bias, Y, out};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, es)) return fail(FL_ERR_INVALID_ARG, "pointer %p is not aligned to the element size", p);
+    if (overlaps(out, o_bytes, A, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
+    if (overlaps(out, o_bytes, B, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
+    if (overlaps(out, o_bytes, bias, bias_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps bias");
+    if (Y && Y != out && overlaps(out, o_bytes, Y, o_bytes))
+        return fail(FL_ERR_INVALID_ARG, "Y partially overlaps out (only Y == out is allowed)");
+    return FL_OK;
+}
+
+fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M, int64_t N,
+                      int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
+    if (M == 0 || N == 0) return FL_OK;
+    TileShape t;
+    fl_status s = tile_shape(opt, t);
+    if (s != FL_OK) return s;
+    const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
+    if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
+    const int es = (int)elem_size(dtype);
+    const int vec = 16 / es;
+    const bool vector_path = (K % vec == 0) && (N % vec == 0) && aligned(A, 16) && aligned(B, 16) &&
+                             aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16));
+    fl::GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.bias = bias;
+    a.Y = Y;
+    a.out = out;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)tiles_m;
+    a.tiles_n = (int)tiles_n;
+    a.group = (opt && opt->group_m > 0) ? opt->group_m : 8;
+    a.xcd_remap = (opt && opt->no_xcd_remap) ? 0 : 1;
+    a.persistent = (opt && opt->persistent) ? 1 : 0;
+    a.tile_count = opt ? opt->debug_tile_count : nullptr;
+    const int ntiles = (int)(tiles_m * tiles_n);
+    int grid = ntiles;
+    if (a.persistent) {
+        const int slots = cu_count();
+        grid = ntiles < slots ? ntiles : slots;
+    }
+    pick_fused(dtype, act, vector_path)(a, grid, static_cast<hipStream_t>(stream));
+    return check_launch("fused_linear");
+}
+
+}  // namespace
+
+extern "C" {
+
+fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M,
+                             int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream,
+                             const fl_options *opt) {
+    clear_error();
+    fl_status s = validate_gemm(A, B, bias, Y, out, M, N, K, act, dtype, opt);
+    if (s != FL_OK) return s;
+    return launch_gemm(A, B, bias, Y, out, M, N, K, act, dtype, stream, opt);
+}
+
+fl_status fl_fused_linear(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M,
+                          int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream) {
+    return fl_fused_linear_ex(A, B, bias, Y, out, M, N, K, act, dtype, stream, nullptr);
+}
+
+fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,
+                  void *stream) {
+    clear_error();
+    fl_status s = validate_gemm(A, B, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, nullptr);
+    if (s != FL_OK) return s;
+    return launch_gemm(A, B, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, stream, nullptr);
+}
+
+fl_status fl_bias_add(void *X, const void *bias, int64_t M, int64_t N, fl_dtype dtype, void *stream) {
+    clear_error();
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    fl_status s = check_dims(M, N, 0);
+    if (s != FL_OK) return s;
+    const size_t es = elem_size(dtype);
+    const size_t x_bytes = (size_t)M * N * es;
+    if (!x_bytes) return FL_OK;
+    if (!X) return fail(FL_ERR_INVALID_ARG, "X is NULL");
+    if (!bias) return fail(FL_ERR_INVALID_ARG, "bias is NULL");
+    if (!aligned(X, es) || !aligned(bias, es)) return fail(FL_ERR_INVALID_ARG, "pointer not aligned to element size");
+    if (overlaps(X, x_bytes, bias, (size_t)N * es)) return fail(FL_ERR_INVALID_ARG, "X overlaps bias");
+    const int vec = 16 / (int)es;
+    const bool v = (N % vec == 0) && aligned(X, 16) && aligned(bias, 16);
+    const int64_t items = v ? M * N / vec : M * N;
+    const int grid = grid_elementwise(items);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+#define FL_BIAS_LAUNCH(DT)                                                                          \
+    if (v)                                                                                          \
+        hipLaunchKernelGGL((fl::bias_add_kernel<DT, true>), dim3(grid), dim3(fl::kThreads), 0, st, X, bias, M, N); \
+    else                                                                                            \
+        hipLaunchKernelGGL((fl::bias_add_kernel<DT, false>), dim3(grid), dim3(fl::kThreads), 0, st, X, bias, M, N);
+    if (dtype == FL_F32) {
+        FL_BIAS_LAUNCH(FL_F32)
+    } else if (dtype == FL_F16) {
+        FL_BIAS_LAUNCH(FL_F16)
+    } else {
+        FL_BIAS_LAUNCH(FL_BF16)
+    }
+#undef FL_BIAS_LAUNCH
+    return check_launch("bias_add");
+}
+
+}  // extern "C"
+
+namespace {
+
+template <int DT, int ACT>
+void launch_act(bool v, int grid, hipStream_t st, const void *X, const void *Y, void *out, int64_t total) {
+    if (v)
+        hipLaunchKernelGGL((fl::activation_kernel<DT, ACT, true>), dim3(grid), dim3(fl::kThreads), 0, st, X, Y, out,
+                           total);
+    else
+        hipLaunchKernelGGL((fl::activation_kernel<DT, ACT, false>), dim3(grid), dim3(fl::kThreads), 0, st, X, Y, out,
+                           total);
+}
+
+template <int DT>
+void launch_act_dt(int act, bool v, int grid, hipStream_t st, const void *X, const void *Y, void *out,
+                   int64_t total) {
+    switch (act) {
+    case FL_ACT_NONE: launch_act<DT, FL_ACT_NONE>(v, grid, st, X, Y, out, total); break;
+    case FL_ACT_RELU: launch_act<DT, FL_ACT_RELU>(v, grid, st, X, Y, out, total); break;
+    case FL_ACT_GELU_TANH: launch_act<DT, FL_ACT_GELU_TANH>(v, grid, st, X, Y, out, total); break;
+    default: launch_act<DT, FL_ACT_GLU>(v, grid, st, X, Y, out, total); break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+fl_status fl_activation(const void *X, const void *Y, void *out, int64_t M, int64_t N, fl_act act, fl_dtype dtype,
+                        void *stream) {
+    clear_error();
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    fl_status s = check_dims(M, N, 0);
+    if (s != FL_OK) return s;
+    const size_t es = elem_size(dtype);
+    const size_t bytes = (size_t)M * N * es;
+    if (act == FL_ACT_GLU && !Y && bytes) return fail(FL_ERR_INVALID_ARG, "the gate needs Y");
+    if (act != FL_ACT_GLU && Y) return fail(FL_ERR_INVALID_ARG, "Y is only used by the gate (FL_ACT_GLU)");
+    if (!bytes) return FL_OK;
+    if (!X || !out) return fail(FL_ERR_INVALID_ARG, "X or out is NULL");
+    if (!aligned(X, es) || !aligned(out, es) || (Y && !aligned(Y, es)))
+        return fail(FL_ERR_INVALID_ARG, "pointer not aligned to element size");
+    if (X != out && overlaps(X, bytes, out, bytes))
+        return fail(FL_ERR_INVALID_ARG, "X partially overlaps out (only X == out is allowed)");
+    if (Y && Y != out && overlaps(Y, bytes, out, bytes))
+        return fail(FL_ERR_INVALID_ARG, "Y partially overlaps out (only Y == out is allowed)");
+    const int vec = 16 / (int)es;
+    const bool v = aligned(X, 16) && aligned(out, 16) && (!Y || aligned(Y, 16));
+    const int64_t total = M * N;
+    const int grid = grid_elementwise(v ? total / vec + 1 : total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == FL_F32)
+        launch_act_dt<FL_F32>(act, v, grid, st, X, Y, out, total);
+    else if (dtype == FL_F16)
+        launch_act_dt<FL_F16>(act, v, grid, st, X, Y, out, total);
+    else
+        launch_act_dt<FL_BF16>(act, v, grid, st, X, Y, out, total);
+    return check_launch("activation");
+}
+
+fl_status fl_tile_grid(int64_t M, int64_t N, int64_t K, fl_dtype dtype, const fl_options *opt, int32_t *block_m,
+                       int32_t *block_n, int32_t *tiles_m, int32_t *tiles_n) {
+    clear_error();
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    fl_status s = check_dims(M, N, K);
+    if (s != FL_OK) return s;
+    TileShape t;
+    s = tile_shape(opt, t);
+    if (s != FL_OK) return s;
+    if (!block_m || !block_n || !tiles_m || !tiles_n) return fail(FL_ERR_INVALID_ARG, "NULL output pointer");
+    *block_m = t.bm;
+    *block_n = t.bn;
+    *tiles_m = (int32_t)((M + t.bm - 1) / t.bm);
+    *tiles_n = (int32_t)((N + t.bn - 1) / t.bn);
+    return FL_OK;
+}
+
+fl_status fl_tile_of_program(int32_t program, int32_t grid, int32_t tiles_m, int32_t tiles_n, int32_t group_m,
+                             int32_t xcd_remap, int32_t *m_tile, int32_t *n_tile) {
+    clear_error();
+    if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || grid <= 0 || !m_tile || !n_tile)
+        return fail(FL_ERR_INVALID_ARG, "bad tile-map arguments");
+    if ((int64_t)tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many tiles");
+    if (grid != tiles_m * tiles_n) return fail(FL_ERR_INVALID_ARG, "grid must equal tiles_m*tiles_n");
+    if (program < 0 || program >= grid) return fail(FL_ERR_INVALID_ARG, "program out of range");
+    const int pid = xcd_remap ? fl::xcd_logical(program, grid) : program;
+    int m, n;
+    fl::grouped_tile(pid, tiles_m, tiles_n, group_m, m, n);
+    *m_tile = m;
+    *n_tile = n;
+    return FL_OK;
+}
+
+const char *fl_status_string(fl_status s) {
+    switch (s) {
+    case FL_OK: return "ok";
+    case FL_ERR_INVALID_ARG: return "invalid argument";
+    case FL_ERR_UNSUPPORTED: return "unsupported";
+    case FL_ERR_LAUNCH: return "launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *fl_last_error(void) { return g_err; }
+
+int fl_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused linear layer out = act(A@B + bias) on one MI355X.
+
+One step = one fused_linear call (bias, activation, cast and store fused into
+the GEMM) over the workload's synthetic inputs, already resident in HBM.
+Prints ONE JSON line with the throughput (TFLOP/s = 2*M*N*K / step time),
+the roofline of the fused kernel (measured with HIP events on the stream the
+kernels run on), the unfused three-kernel chain for comparison, and the
+FP64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--no-unfused]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+bias+act TFLOP/s and % of MFMA peak (fp16, 4096^3) on 1 MI355X"
+DEFAULT_WORKLOAD = "relu_f16_4096x4096x4096"
+# MI355X dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s): 256 CUs at
+# 2.4 GHz; fp16/bf16 4096 flop/clk/CU, fp32 256 flop/clk/CU.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    p.add_argument("--group-m", type=int, default=0)
+    p.add_argument("--persistent", type=int, default=0)
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "activation_epilogue_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_loop(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(w, d, target_s):
+    """Time the FP64 oracle (as it is) on a bounded sample of output rows,
+    growing the sample until one call takes at least half of target_s."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    nrows = min(threads, w.M)
+    while True:
+        rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or nrows >= w.M:
+            break
+        nrows = int(min(w.M, nrows * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
+    flops = 2.0 * nrows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} of {w.M} output rows of {w.name}, FP64, evenly spaced; "
+                      f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
+              "path (the layer shards by output columns or rows with no communication; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import activation_epilogue_amd as fl
+    from activation_epilogue_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fl.load_library()
+    w = synth.WORKLOADS[args.workload]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    d = synth.draw_workload(w)
+
+    def dev(raw):
+        if raw is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(raw))
+        if w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to("cuda")
+
+    A, B, bias, Y = dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["Y"])
+    out = torch.empty((w.M, w.N), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+    opts = {}
+    if args.group_m:
+        opts["group_m"] = args.group_m
+    if args.persistent:
+        opts["persistent"] = 1
+
+    def step():
+        fl.fused_linear(A, B, bias, Y, act=w.act, out=out, **opts)
+
+    ms_event, ms_wall = time_loop(step, args.steps, args.warmup, stream)
+    flops = w.flops
+    tflops = flops / (ms_wall * 1e-3) / 1e12
+    achieved = flops / (ms_event * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    es = ES[w.dtype]
+    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * (2 if w.act == "glu" else 1)) * es
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s)" % (
+            w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else ""),
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "io_dtype": w.dtype,
+                   "accumulate": "f32", "tile": "256x256", "group_m": args.group_m or 8,
+                   "persistent": bool(args.persistent)},
+        "frac_of_peak": round(tflops / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "fused_linear_kernel", "avg_launch_ms": round(ms_event, 4),
+                     "algorithmic_bytes": alg_bytes},
+    }
+
+    if not args.no_unfused:
+        X = torch.empty_like(out)
+
+        def chain():
+            fl.gemm(A, B, X)
+            fl.bias_add(X, bias)
+            fl.activation(X, Y, out=X, act=w.act)
+
+        ms_chain, _ = time_loop(chain, args.steps, args.warmup, stream)
+        ms_gemm, _ = time_loop(lambda: fl.gemm(A, B, X), args.steps, args.warmup, stream)
+        ms_bias, _ = time_loop(lambda: fl.bias_add(X, bias), args.steps, args.warmup, stream)
+        ms_act, _ = time_loop(lambda: fl.activation(X, Y, out=X, act=w.act), args.steps, args.warmup, stream)
+        mn = w.M * w.N
+        bias_bytes = (2 * mn + w.N) * es
+        act_bytes = (3 if w.act == "glu" else 2) * mn * es
+        result["unfused"] = {
+            "ms_per_step": round(ms_chain, 4),
+            "fused_speedup": round(ms_chain / ms_event, 3),
+            "gemm_ms": round(ms_gemm, 4),
+            "bias_pass": {"ms": round(ms_bias, 4), "GB/s": round(bias_bytes / ms_bias / 1e6, 1),
+                          "frac_hbm": round(bias_bytes / ms_bias / 1e6 / PEAK_HBM_GBS, 3)},
+            "act_pass": {"ms": round(ms_act, 4), "GB/s": round(act_bytes / ms_act / 1e6, 1),
+                         "frac_hbm": round(act_bytes / ms_act / 1e6 / PEAK_HBM_GBS, 3)},
+            "activation_traffic_bytes": {"fused": (2 if w.act == "glu" else 1) * mn * es,
+                                         "unfused": (5 + (1 if w.act == "glu" else 0)) * mn * es},
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * fused_linear.h -- C ABI of the gfx950 fused linear layer
+ *
+ *     out = act(A @ B + bias)
+ *
+ * computed by one tiled MFMA GEMM whose epilogue runs on the fp32
+ * accumulators after the whole K reduction: a per-column bias broadcast over
+ * rows, then ReLU, GELU(tanh) or the gate X + X*Y, then one conversion to the
+ * I/O dtype and one store.
+ *
+ * Definitions followed (page title, section):
+ *   - "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)": the opening
+ *     formula out[i,j] = max(0, sum_k A[i,k] B[k,j] + bias[j]); the bias is per
+ *     column, broadcast across rows, added once after the K loop.
+ *   - "Epilogue concept", "Where the accumulator is finally correct": the
+ *     epilogue transforms the accumulator after the K loop, then one store.
+ *   - "I3. Fuse a GEMM epilogue and change tile scheduling": fp32 accumulate,
+ *     epilogue in fp32, conversion to the input dtype only at the store;
+ *     K = 0 still runs the epilogue ("Implement in stages"); grouped
+ *     program-id ownership with a short final group ("Tiles and grouped
+ *     ownership").
+ *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block":
+ *     X = A@B + bias, out = X + X*Y; the unfused path writes X and reads it
+ *     back, which the separate entry points below reproduce.
+ *   - GELU(tanh) is named as a fusable activation on the first page but not
+ *     written out; the tanh approximation of Hendrycks & Gimpel (2016),
+ *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), is used.
+ *
+ * Conventions shared by every entry point:
+ *   Layout     Row-major, contiguous: A is (M,K) with row stride K, B is (K,N)
+ *              with row stride N, Y/X/out are (M,N) with row stride N, bias is
+ *              (N,).  Strides are not supported.
+ *   Dtypes     A, B, bias, Y and out all use `dtype`; accumulation and the
+ *              epilogue are fp32; the single store rounds to nearest even.
+ *   Ownership  Every data pointer is a caller-owned DEVICE pointer.  The
+ *              library never allocates, frees or copies host<->device memory.
+ *   Async      Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *              stream) and the call returns; the library never synchronises.
+ *              Buffers must stay alive until the work has finished.
+ *   Aliasing   out must not overlap A, B or bias.  Y may be exactly out (each
+ *              element is read before it is written) but must not partially
+ *              overlap it.
+ *   Shapes     M, N, K >= 0 and <= 2^31-1.  M == 0 or N == 0 returns FL_OK
+ *              without launching.  K == 0 is valid: out = act(bias) on every
+ *              row (bias NULL counts as zero).
+ *   Alignment  Pointers must be aligned to the element size.  16-byte aligned
+ *              pointers with K and N multiples of 16 bytes / element size take
+ *              the vector-load path; everything else takes the element path.
+ *              Both produce the same results.
+ *   Errors     Arguments are validated before any HIP call; a bad argument
+ *              returns FL_ERR_INVALID_ARG (or FL_ERR_UNSUPPORTED for a
+ *              well-formed request the library does not implement) with no
+ *              launch and no write, and sets a thread-local message readable
+ *              with fl_last_error().  A failed launch returns FL_ERR_LAUNCH.
+ *   Threads    Stateless apart from the thread-local error message and a
+ *              per-device cache of the compute-unit count; safe to call from
+ *              several host threads.
+ */
+#ifndef FUSED_LINEAR_H
+#define FUSED_LINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FL_F32 = 0, FL_F16 = 1, FL_BF16 = 2 } fl_dtype;
+
+typedef enum {
+    FL_ACT_NONE = 0,      /* out = X                                  */
+    FL_ACT_RELU = 1,      /* out = max(X, 0)                          */
+    FL_ACT_GELU_TANH = 2, /* out = 0.5 X (1 + tanh(sqrt(2/pi)(X + 0.044715 X^3))) */
+    FL_ACT_GLU = 3        /* out = X + X*Y  (the gate; needs Y)       */
+} fl_act;
+
+typedef enum {
+    FL_OK = 0,
+    FL_ERR_INVALID_ARG = 1,
+    FL_ERR_UNSUPPORTED = 2,
+    FL_ERR_LAUNCH = 3
+} fl_status;
+
+/* Tuning and debug options of fl_fused_linear_ex.  Zero-initialise and set
+ * what you need; every field's zero means "default". */
+typedef struct {
+    int32_t group_m;    /* M-tiles per band of the grouped program map; 0 = 8.
+                           1 gives row-major tile order. */
+    int32_t persistent; /* 0 = one workgroup per output tile; 1 = a grid sized
+                           to the GPU whose workgroups loop over tiles. */
+    int32_t tile_cfg;   /* 0 = automatic; 1 = 256x256 tiles; 2 = 128x128. */
+    int32_t no_xcd_remap; /* 0 = place neighbouring tiles on one XCD; 1 = off */
+    uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
+                           counters (see fl_tile_grid); each output tile adds
+                           one when it is written.  Caller zeroes it. */
+} fl_options;
+
+/*
+ * out = act(A@B + bias).
+ *   A     (M,K) device pointer; may be NULL only if M*K == 0.
+ *   B     (K,N) device pointer; may be NULL only if K*N == 0.
+ *   bias  (N,) device pointer, or NULL for no bias.
+ *   Y     (M,N) device pointer, required when act == FL_ACT_GLU and NULL
+ *         otherwise (a non-NULL Y with another act is FL_ERR_INVALID_ARG).
+ *   out   (M,N) device pointer.
+ *   stream  hipStream_t to enqueue on.
+ * Uses the default options (grouped map with 8 M-tiles per band, automatic
+ * tile size, XCD-aware placement).
+ */
+fl_status fl_fused_linear(const void *A, const void *B, const void *bias,
+                          const void *Y, void *out, int64_t M, int64_t N,
+                          int64_t K, fl_act act, fl_dtype dtype, void *stream);
+
+/* As fl_fused_linear, with explicit options (opt may be NULL = defaults).
+ * Results are bitwise identical for every group_m, persistent and
+ * no_xcd_remap setting: they change which workgroup computes a tile, never
+ * the arithmetic of the tile.  tile_cfg changes the tile shape and may change
+ * the fp32 rounding order inside the MFMA sums (within tolerance). */
+fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias,
+                             const void *Y, void *out, int64_t M, int64_t N,
+                             int64_t K, fl_act act, fl_dtype dtype,
+                             void *stream, const fl_options *opt);
+
+/* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
+ * traffic": GEMM writes X, a bias pass reads and writes it, an activation
+ * pass reads and writes it).  Each call is one launch and stores its result
+ * in dtype.  Together they compute round(act(round(round(A@B) + bias))). */
+
+/* X = A@B, the fused kernel with no bias and no activation. */
+fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M,
+                  int64_t N, int64_t K, fl_dtype dtype, void *stream);
+
+/* X[i,j] += bias[j] in place (X is (M,N); bias (N,) must not be NULL). */
+fl_status fl_bias_add(void *X, const void *bias, int64_t M, int64_t N,
+                      fl_dtype dtype, void *stream);
+
+/* out = act(X) elementwise (out may equal X); Y (M,N) is required for
+ * FL_ACT_GLU (out = X + X*Y) and must be NULL otherwise.  FL_ACT_NONE copies. */
+fl_status fl_activation(const void *X, const void *Y, void *out, int64_t M,
+                        int64_t N, fl_act act, fl_dtype dtype, void *stream);
+
+/* Tile grid fl_fused_linear_ex would use for this problem (no GPU call).
+ * Writes the tile shape and the number of tiles along M and N. */
+fl_status fl_tile_grid(int64_t M, int64_t N, int64_t K, fl_dtype dtype,
+                       const fl_options *opt, int32_t *block_m,
+                       int32_t *block_n, int32_t *tiles_m, int32_t *tiles_n);
+
+/* Grouped program-id -> tile map used on the device, evaluated on the host
+ * for tests ("Tiles and grouped ownership").  xcd_remap selects whether the
+ * XCD placement step is applied first.  grid is the number of programs. */
+fl_status fl_tile_of_program(int32_t program, int32_t grid, int32_t tiles_m,
+                             int32_t tiles_n, int32_t group_m,
+                             int32_t xcd_remap, int32_t *m_tile,
+                             int32_t *n_tile);
+
+const char *fl_status_string(fl_status s);
+const char *fl_last_error(void); /* thread-local; "" when none */
+int fl_version(void);            /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSED_LINEAR_H */

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: exports, argument validation, host tile map.
+
+Validation runs before any HIP call, so every rejected call below returns its
+status without touching a device.  Fake device pointers are plain aligned
+integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import activation_epilogue_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fused_linear.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
+NONE, RELU, GELU, GLU = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fl.load_library()
+
+
+def test_header_symbols_are_exported(lib):
+    text = open(HEADER).read()
+    declared = sorted(set(re.findall(r"\b(fl_[a-z_]+)\s*\(", text)))
+    assert declared, "no declarations found"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+    assert set(declared) == set(fl.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fl_version() == 10000
+    assert lib.fl_status_string(0) == b"ok"
+    assert lib.fl_status_string(1) == b"invalid argument"
+    assert lib.fl_status_string(3) == b"launch failed"
+
+
+A_P, B_P, BIAS_P, Y_P, OUT_P = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _fused(lib, A=A_P, B=B_P, bias=BIAS_P, Y=None, out=OUT_P, M=64, N=64, K=64, act=RELU, dt=F16, opt=None):
+    if opt is None:
+        return lib.fl_fused_linear(A, B, bias, Y, out, M, N, K, act, dt, None)
+    return lib.fl_fused_linear_ex(A, B, bias, Y, out, M, N, K, act, dt, None, ctypes.byref(opt))
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(A=None), INVALID, "A is NULL"),
+    (dict(B=None), INVALID, "B is NULL"),
+    (dict(out=None), INVALID, "out is NULL"),
+    (dict(act=GLU), INVALID, "the gate needs Y"),
+    (dict(Y=Y_P), INVALID, "Y is only used by the gate"),
+    (dict(M=-1), INVALID, "negative size"),
+    (dict(K=-5), INVALID, "negative size"),
+    (dict(N=2 ** 31), UNSUPPORTED, "above 2^31-1"),
+    (dict(K=2 ** 22), UNSUPPORTED, "too large"),
+    (dict(act=7), INVALID, "unknown activation"),
+    (dict(dt=9), INVALID, "unknown dtype"),
+    (dict(A=A_P + 1), INVALID, "not aligned"),
+    (dict(out=A_P + 64), INVALID, "out overlaps A"),
+    (dict(out=B_P), INVALID, "out overlaps B"),
+    (dict(out=BIAS_P - 2), INVALID, "out overlaps bias"),
+    (dict(act=GLU, Y=OUT_P + 2), INVALID, "partially overlaps"),
+])
+def test_fused_rejects_bad_arguments(lib, kwargs, status, msg):
+    assert _fused(lib, **kwargs) == status
+    assert msg in lib.fl_last_error().decode()
+
+
+def test_degenerate_shapes_return_ok_without_launch(lib):
+    assert _fused(lib, M=0) == OK
+    assert _fused(lib, N=0) == OK
+    assert _fused(lib, A=None, M=0, K=0, N=5) == OK
+    assert lib.fl_last_error() == b""
+    assert lib.fl_bias_add(None, None, 0, 7, F16, None) == OK
+    assert lib.fl_activation(None, None, None, 3, 0, RELU, F32, None) == OK
+
+
+def test_bad_options(lib):
+    assert _fused(lib, opt=fl.Options(-1, 0, 0, 0, None)) == INVALID
+    assert _fused(lib, opt=fl.Options(0, 2, 0, 0, None)) == INVALID
+    assert _fused(lib, opt=fl.Options(0, 0, 99, 0, None)) == UNSUPPORTED
+    assert "tile_cfg" in lib.fl_last_error().decode()
+
+
+def test_unfused_entry_points_reject_bad_arguments(lib):
+    assert lib.fl_gemm(None, B_P, OUT_P, 8, 8, 8, F32, None) == INVALID
+    assert lib.fl_bias_add(OUT_P, None, 8, 8, F32, None) == INVALID
+    assert lib.fl_bias_add(OUT_P, OUT_P + 4, 8, 8, F32, None) == INVALID
+    assert lib.fl_activation(OUT_P, None, OUT_P + 2, 8, 8, RELU, F16, None) == INVALID
+    assert lib.fl_activation(OUT_P, None, OUT_P, 8, 8, GLU, F16, None) == INVALID
+    assert lib.fl_activation(OUT_P, Y_P, OUT_P, 8, 8, RELU, F16, None) == INVALID
+    assert lib.fl_activation(OUT_P, None, OUT_P, 8, 8, 4, F16, None) == INVALID
+
+
+def test_tile_grid(lib):
+    assert fl.tile_grid(4096, 4096, 4096, F16) == (256, 256, 16, 16)
+    assert fl.tile_grid(4097, 3071, 1537, BF16) == (256, 256, 17, 12)
+    assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 256, 4, 85)
+    assert fl.tile_grid(127, 129, 96, F32) == (256, 256, 1, 1)
+
+
+def test_host_tile_map_matches_oracle_without_xcd_step(lib):
+    # the printed six-program example and a brute-force sweep
+    assert [fl.tile_of_program(p, 6, 3, 2, 2, 0) for p in range(6)] == [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1)]
+    for tm in range(1, 18, 2):
+        for tn in range(1, 14, 3):
+            for g in (1, 2, 4, 8, 9):
+                for p in range(tm * tn):
+                    assert fl.tile_of_program(p, tm * tn, tm, tn, g, 0) == oracle.tile_of_pid(p, tm, tn, g)
+
+
+@pytest.mark.parametrize("tm,tn,g", [(16, 16, 8), (17, 12, 4), (17, 12, 8), (4, 85, 8), (32, 56, 8), (1, 1, 1),
+                                     (3, 5, 2), (33, 24, 8)])
+def test_host_tile_map_with_xcd_step_is_a_bijection(lib, tm, tn, g):
+    n = tm * tn
+    tiles = [fl.tile_of_program(p, n, tm, tn, g, 1) for p in range(n)]
+    assert sorted(tiles) == sorted((m, k) for m in range(tm) for k in range(tn))
+    # programs on one XCD (p % 8 equal) receive consecutive grouped positions
+    pos = {oracle.tile_of_pid(q, tm, tn, g): q for q in range(n)}
+    for x in range(min(8, n)):
+        qs = [pos[tiles[p]] for p in range(x, n, 8)]
+        assert qs == list(range(qs[0], qs[0] + len(qs)))

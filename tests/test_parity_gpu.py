@@ -1,0 +1,259 @@
+"""Parity of the HIP path (through the C ABI) with the FP64 oracle.
+
+Tolerance (|dev - ref| <= atol + rtol*|ref|, ref = the oracle's once-rounded
+output): (1e-4, 1e-4) for fp32 outputs and (4e-3, 1e-2) for fp16/bf16.
+Bit-exact where the inputs make all arithmetic exact (small integers).
+Every output buffer is prefilled with NaN and followed by a NaN guard band:
+an element left unwritten fails the comparison and a write past the end
+breaks the guard.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import activation_epilogue_amd as fl
+from activation_epilogue_amd import synth
+from gpu_util import say, to_dev, to_host, sentinel_out, guard_intact, sample_rows, TORCH_DT
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DTYPES = ["f32", "f16", "bf16"]
+
+
+def _run_fused(d, act, dtype, **opts):
+    M, K = d["A"].shape
+    N = d["B"].shape[1]
+    A, B, bias, Y = (to_dev(d[k], dtype) for k in ("A", "B", "bias", "Y"))
+    out, buf = sentinel_out(M, N, dtype)
+    fl.fused_linear(A, B, bias, Y, act=act, out=out, **opts)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, M, N), "write past the end of out"
+    return to_host(out, dtype)
+
+
+def _run_unfused(d, act, dtype):
+    M, K = d["A"].shape
+    N = d["B"].shape[1]
+    A, B, bias, Y = (to_dev(d[k], dtype) for k in ("A", "B", "bias", "Y"))
+    X, buf = sentinel_out(M, N, dtype)
+    fl.gemm(A, B, X)
+    if bias is not None:
+        fl.bias_add(X, bias)
+    out = fl.activation(X, Y, out=X, act=act)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, M, N)
+    return to_host(out, dtype)
+
+
+def _assert_close(dev, ref, dtype, what):
+    res = oracle.compare(dev, ref, dtype)
+    assert res["ok"], f"{what}: {res}"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    fl.load_library()
+
+
+# ------------------------------------------------------------ worked example
+
+def _golden_inputs(dtype):
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "worked_example_2x2.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, _, rhs = line.partition("=")
+            rows = [[float(v) for v in r.split()] for r in rhs.split(";")]
+            vals[k.strip()] = np.array(rows if len(rows) > 1 else rows[0])
+    return vals
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_worked_example_bit_exact(dtype):
+    g = _golden_inputs(dtype)
+    d = {"A": synth.to_storage(g["A"], dtype), "B": synth.to_storage(g["B"], dtype),
+         "bias": synth.to_storage(g["bias"], dtype), "Y": None}
+    say("worked example", dtype)
+    out = _run_fused(d, "relu", dtype)
+    assert np.array_equal(oracle.decode(out, dtype), g["relu"])
+    out = _run_unfused(d, "relu", dtype)
+    assert np.array_equal(oracle.decode(out, dtype), g["relu"])
+
+
+# ------------------------------------------------------------------- K = 0
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+def test_k0_gives_act_of_bias(dtype, act):
+    d = synth.draw(37, 300, 0, dtype, act, seed=1)
+    say("K=0", dtype, act)
+    out = _run_fused(d, act, dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    if act in ("none", "relu"):
+        # acc = 0, so X = bias exactly and the store returns the bias bits
+        assert np.array_equal(out.view(np.uint8), ref.view(np.uint8))
+    _assert_close(out, ref, dtype, f"K=0 {act}")
+
+
+# --------------------------------------------------- K=1 / K=3 and the chain
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("K", [1, 3])
+def test_k1_k3_fused_matches_unfused_and_oracle(dtype, K):
+    d = synth.draw(127, 129, K, dtype, "relu", seed=0)
+    say("K1/K3", dtype, K)
+    fused = _run_fused(d, "relu", dtype)
+    chain = _run_unfused(d, "relu", dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], act="relu", dtype=dtype)
+    ref_chain = oracle.unfused_chain(d["A"], d["B"], d["bias"], act="relu", dtype=dtype)
+    _assert_close(fused, ref, dtype, "fused vs oracle")
+    _assert_close(chain, ref_chain, dtype, "unfused chain vs oracle chain")
+    _assert_close(fused, chain, dtype, "fused vs unfused chain")
+
+
+# ------------------------------------------------------- exact integer data
+
+INT_SHAPES = [(1, 1, 1), (3, 5, 7), (2, 9, 0), (64, 64, 64), (67, 65, 70), (65, 8, 8), (31, 136, 64),
+              (257, 264, 40), (300, 520, 24), (513, 770, 33), (129, 1024, 16)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("shape", INT_SHAPES)
+def test_integer_inputs_bit_exact(dtype, act, shape):
+    M, N, K = shape
+    d = synth.draw_integer(M, N, K, dtype, act, seed=M + 7 * N + 13 * K, amax=1, bias_max=3)
+    say("integer", dtype, act, shape)
+    out = _run_fused(d, act, dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    assert np.array_equal(out.view(np.uint8), ref.view(np.uint8)), oracle.compare(out, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_integer_inputs_no_bias(dtype):
+    d = synth.draw_integer(70, 90, 50, dtype, "relu", seed=3)
+    d["bias"] = None
+    say("integer no bias", dtype)
+    out = _run_fused(d, "relu", dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], None, act="relu", dtype=dtype)
+    assert np.array_equal(out.view(np.uint8), ref.view(np.uint8))
+
+
+# ----------------------------------------------------- random data, tolerance
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("shape", [(127, 129, 96), (256, 512, 256), (300, 260, 1000), (513, 96, 72)])
+def test_random_inputs_within_tolerance(dtype, act, shape):
+    M, N, K = shape
+    d = synth.draw(M, N, K, dtype, act, bias_var=0.1 if act == "gelu_tanh" else 1.0, seed=5)
+    say("random", dtype, act, shape)
+    out = _run_fused(d, act, dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    _assert_close(out, ref, dtype, f"{dtype} {act} {shape}")
+
+
+def test_relu_f32_127x129x96_full():
+    w = synth.WORKLOADS["relu_f32_127x129x96"]
+    d = synth.draw_workload(w)
+    say(w.name)
+    out = _run_fused(d, w.act, w.dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], act=w.act, dtype=w.dtype)
+    _assert_close(out, ref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
+def test_unfused_chain_matches_oracle_chain(dtype, act):
+    d = synth.draw(200, 264, 136, dtype, act, seed=8)
+    say("unfused chain", dtype, act)
+    chain = _run_unfused(d, act, dtype)
+    ref = oracle.unfused_chain(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    _assert_close(chain, ref, dtype, "unfused chain")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_vector_and_element_paths_agree_bitwise(dtype):
+    """A misaligned copy of the same data takes the element path."""
+    M, N, K = 130, 264, 200
+    d = synth.draw(M, N, K, dtype, "relu", seed=12)
+    A, B, bias = (to_dev(d[k], dtype) for k in ("A", "B", "bias"))
+    say("vector vs element path", dtype)
+    out_v = fl.fused_linear(A, B, bias, act="relu")
+    A2 = torch.empty(M * K + 1, dtype=A.dtype, device="cuda")[1:].view(M, K)
+    A2.copy_(A)
+    out_e = fl.fused_linear(A2, B, bias, act="relu")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out_v, dtype).view(np.uint8), to_host(out_e, dtype).view(np.uint8))
+
+
+# ----------------------------------------------------------- the full sizes
+
+FULL = ["relu_f32_4096x4096x4096", "relu_f16_4096x4096x4096", "relu_bf16_4097x3071x1537",
+        "glu_f16_1024x21568x4096", "gelu_bf16_8192x14336x4096"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    """Default launch (as timed by the benchmark): every output written, no
+    write past the end, and sampled rows (every tile edge plus random rows)
+    equal to the oracle within tolerance."""
+    w = synth.WORKLOADS[name]
+    d = synth.draw_workload(w)
+    say("full size", name)
+    out = _run_fused(d, w.act, w.dtype)
+    assert not np.isnan(oracle.decode(out, w.dtype)).any(), "unwritten (NaN sentinel) outputs"
+    rows = sample_rows(w.M)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+    _assert_close(out[rows], ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["relu_bf16_4097x3071x1537", "glu_f16_1024x21568x4096"])
+def test_tile_order_does_not_change_bits(name):
+    """GROUP in {1,4,8}, XCD step on/off and persistent on/off change which
+    workgroup computes a tile, never its arithmetic; each tile is written
+    exactly once."""
+    w = synth.WORKLOADS[name]
+    d = synth.draw_workload(w)
+    A, B, bias, Y = (to_dev(d[k], w.dtype) for k in ("A", "B", "bias", "Y"))
+    code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    _, _, tm, tn = fl.tile_grid(w.M, w.N, w.K, code)
+    base = None
+    for opts in [dict(group_m=8), dict(group_m=1), dict(group_m=4), dict(group_m=8, no_xcd_remap=1),
+                 dict(group_m=8, persistent=1), dict(group_m=1, persistent=1, no_xcd_remap=1)]:
+        say("tile order", name, opts)
+        counts = torch.zeros(tm * tn, dtype=torch.int32, device="cuda")
+        out = fl.fused_linear(A, B, bias, Y, act=w.act, debug_tile_count=counts, **opts)
+        torch.cuda.synchronize()
+        assert bool((counts == 1).all().item()), f"tile written {counts.min().item()}..{counts.max().item()} times"
+        h = to_host(out, w.dtype).view(np.uint8)
+        if base is None:
+            base = h
+        else:
+            assert np.array_equal(h, base), opts
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = synth.WORKLOADS["relu_f16_4096x4096x4096"]
+    d = synth.draw_workload(w)
+    A, B, bias = (to_dev(d[k], w.dtype) for k in ("A", "B", "bias"))
+    say("determinism", w.name)
+    outs = [to_host(fl.fused_linear(A, B, bias, act="relu"), w.dtype) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_y_may_alias_out():
+    M, N, K = 300, 520, 64
+    d = synth.draw(M, N, K, "f16", "glu", seed=2)
+    A, B, bias, Y = (to_dev(d[k], "f16") for k in ("A", "B", "bias", "Y"))
+    say("Y aliases out")
+    fl.fused_linear(A, B, bias, Y, act="glu", out=Y)
+    torch.cuda.synchronize()
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act="glu", dtype="f16")
+    _assert_close(to_host(Y, "f16"), ref, "f16", "Y == out")
