@@ -1,0 +1,535 @@
+// fl_dma16.hpp -- fp16/bf16 fused GEMM with direct-to-LDS loads.
+//
+// Same contract and epilogue as FusedTile (fl_kernels.hpp); this variant is
+// used when A, B, out (and bias, Y) are 16-byte aligned and K, N are
+// multiples of 8.  Differences from the register-staged kernel:
+//
+//   * Global -> LDS copies use buffer_load_dwordx4 with the LDS bit: each
+//     instruction moves 64 x 16 bytes straight into 1 KB of LDS at
+//     M0 + lane*16, so no staging registers, no ds_write and no VALU
+//     transposes.  The XOR swizzle is applied on the global side: lane l of
+//     an instruction fetches the chunk that belongs at LDS position l.
+//   * B stays N-contiguous in LDS ([k][n] rows of 512 bytes) and its MFMA
+//     operand is read with ds_read_b64_tr_b16: within each 16-lane group,
+//     lane i receives element 16*j + i (j = 0..3) of the group's lane-major
+//     64 values, so 16 lanes that point at 4 k-rows x 16 columns (4 columns
+//     per lane) receive one column each with 4 consecutive k values -- the
+//     K-contiguous B operand of v_mfma_f32_32x32x16_{f16,bf16}.
+//   * A K stage of BK values (BK = 64: A rows are whole 128-byte lines)
+//     occupies one of NBUF LDS buffers (NBUF * BK KB = 128 KB).  The copies
+//     of a stage are issued right after the barrier that frees its buffer,
+//     so NBUF-1 stages are in flight while MFMAs run ("Optimizing GEMM +
+//     Activation on CDNA4 with TLX", "Version 3": a deeper buffer ring lets
+//     the wait keep loads in flight instead of draining them).
+//   * Each stage is BK/16 blocks of 16 MFMAs; the operand reads of the next
+//     block are slotted between the MFMAs of the current one, and the one
+//     barrier per stage sits before the last block, whose MFMA slots also
+//     carry the copies of the stage NBUF ahead.
+//   * The copies are inline asm, invisible to the compiler's wait-count
+//     pass; every wait on them is explicit (wait_vm).
+#pragma once
+
+#include "fl_kernels.hpp"
+
+namespace fl {
+
+#define FL_LDS __attribute__((address_space(3)))
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor in SGPRs (gfx9 layout: 48-bit base, stride 0,
+// num_records, word 3 = 32-bit data format) for the inline-asm copies.
+__device__ __forceinline__ i32x4_t sgpr_rsrc(const void *p, size_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane((int)n);
+    r.w = (int)kRsrcWord3;
+    return r;
+}
+
+// One 64 x 16-byte copy from global memory into LDS at lds_addr + lane*16
+// (byte address base + soffset + voffset; a voffset at or past num_records
+// writes zeros).  M0 is written here and used by nothing else in the
+// kernels that call this.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t voffset, uint32_t soffset, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(rsrc),
+                 "s"(soffset), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int DT, int ACT, int BK_>
+struct Dma16 {
+    using base = FusedTile<DT, ACT, true>;  // shares the epilogue
+    static constexpr int BM = 256, BN = 256, BK = BK_;
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static constexpr int NBUF = 128 / BK;            // 128 KB of LDS in the ring
+    static constexpr int KK = BK / 16;               // 16-MFMA blocks per stage
+    static constexpr int CA = BK / 8;                // 16-byte chunks per A row
+    static constexpr int A_BYTES = BM * BK * 2;      // rows of BK*2 bytes
+    static constexpr int B_BYTES = BK * BN * 2;      // rows of 512 bytes (32 chunks)
+    static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
+    static constexpr int NA = CA;                    // A copies per wave per stage
+    static constexpr int NB = BK / 8;                // B copies per wave per stage (2 rows each)
+    static constexpr int DMA_PER_WAVE = NA + NB;
+    static_assert(NA * 4 * A_ROWS_PER_COPY == BM, "A copies cover the tile");
+    static_assert(NB * 4 * 2 == BK, "B copies cover the stage");
+    static_assert(DMA_PER_WAVE <= 16, "copies fit the MFMA slots of one block");
+
+    // A swizzle: chunk c of row r sits at c ^ fa(r).  16-byte operand reads
+    // of 8 consecutive rows (8 lanes per cycle) and of 16 consecutive rows
+    // (16 lanes per cycle) both touch distinct bank groups.
+    __device__ __forceinline__ static int fa(int r) {
+        if constexpr (CA == 4)
+            return ((r >> 1) ^ (r >> 3)) & 3;
+        else
+            return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+    }
+    // B swizzle: chunk c (0..31) of k-row r sits at c ^ fb(r), fb in {0,6,12,10}
+    // by r % 4; conflict-free for the transposed 8-byte reads (4 rows x 2 or
+    // 4 chunks per 16 or 32 lanes).
+    __device__ __forceinline__ static int fb(int r) { return (0xAC60 >> (4 * (r & 3))) & 0xF; }
+
+    // Per-lane copy offsets and operand-read addresses, fixed for a tile.
+    // A is addressed through a descriptor based at row m0 and B through one
+    // based at column n0; a stage adds its K origin as the scalar offset
+    // (k0*2 bytes for A, k0*N*2 for B).  A lane whose chunk lies past K (or
+    // past N) uses kOob so the hardware range check writes zeros; rows past
+    // M are beyond num_records of A's descriptor.  Copy i of a wave covers
+    // A rows A_ROWS_PER_COPY*(wave*NA + i) + lane/CA and B k-rows
+    // 2*(wave*NB + i) + lane/32; the swizzle of those rows repeats with period
+    // 2 in i, so two offsets per operand plus a stride describe all copies.
+    struct Lane {
+        i32x4_t rA, rB;
+        uint32_t a_off[2];  // byte offset (k0 = 0) of copies i = 0, 1; +i/2 * a_step
+        int a_k[2];         // K index within the stage of those chunks
+        uint32_t b_off[2];  // same for B (kOob when the columns are past N); +i/2 * b_step
+        int b_k0;           // K row within the stage of copy 0 (copy i: + 2i)
+        uint32_t a_step, b_step;
+        int a_frag[KK];     // LDS byte address of A operand reads per kk (mi adds 32 rows)
+        int b_frag[4];      // LDS byte address of B operand reads per ni (kk adds 16 rows, h 4 rows)
+    };
+
+    __device__ __forceinline__ static void setup(const GemmArgs &a, int m0, int n0, int wave, int lane, int wm,
+                                                 int wn, Lane &L) {
+        const size_t a_org = (size_t)m0 * a.K;
+        L.rA = sgpr_rsrc(static_cast<const char *>(a.A) + a_org * 2, ((size_t)a.M * a.K - a_org) * 2);
+        L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * 2, ((size_t)a.K * a.N - n0) * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ra = A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
+            const int ca = (lane % CA) ^ fa(ra);
+            L.a_off[i] = (uint32_t)(ra * a.K + ca * 8) * 2;
+            L.a_k[i] = ca * 8;
+            const int rb = 2 * (wave * NB + i) + (lane >> 5);
+            const int cb = (lane & 31) ^ fb(rb);
+            L.b_off[i] = (n0 + cb * 8 < a.N) ? (uint32_t)(rb * a.N + cb * 8) * 2 : kOob;
+        }
+        L.b_k0 = 2 * wave * NB + (lane >> 5);
+        L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * 2;
+        L.b_step = (uint32_t)(4 * a.N) * 2;
+        const int lrow = lane & 31, lg = lane >> 5;
+        const int r = wm * 128 + lrow;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
+        const int g16 = lane >> 4, i16 = lane & 15;
+        const int rk = (g16 >> 1) * 8 + (i16 >> 2);  // k-row for kk = 0, h = 0
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int n = wn * 128 + ni * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+            L.b_frag[ni] = A_BYTES + rk * 512 + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
+        }
+    }
+
+    struct Stage {  // scalar state of the copies of one stage
+        int kleft;
+        uint32_t soa, sob;
+        uint32_t adst, bdst;  // LDS byte address of this wave's first A / B copy
+    };
+
+    __device__ __forceinline__ static Stage stage_of(const GemmArgs &a, int kt, int wave, uint32_t buf_addr) {
+        const int k0 = kt * BK;
+        Stage s;
+        s.kleft = a.K - k0;
+        s.soa = (uint32_t)k0 * 2;
+        s.sob = (uint32_t)k0 * (uint32_t)a.N * 2;
+        s.adst = __builtin_amdgcn_readfirstlane(buf_addr + wave * NA * 1024);
+        s.bdst = __builtin_amdgcn_readfirstlane(buf_addr + A_BYTES + wave * NB * 1024);
+        return s;
+    }
+
+    // Copy I (A copies first) of the stage described by s.  Stages at or past
+    // the end of K are issued too, with every lane out of range, so every
+    // stage issues the same number of copies and the wait counts are
+    // constants.
+    template <int I>
+    __device__ __forceinline__ static void copy_one(const Lane &L, const Stage &s) {
+        if constexpr (I < NA) {
+            const uint32_t off = L.a_off[I & 1] + (uint32_t)(I >> 1) * L.a_step;
+            lds_copy16(L.rA, L.a_k[I & 1] < s.kleft ? off : kOob, s.soa, s.adst + I * 1024);
+        } else {
+            constexpr int i = I - NA;
+            const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
+            const bool ok = (L.b_k0 + 2 * i < s.kleft) && (L.b_off[i & 1] != kOob);
+            lds_copy16(L.rB, ok ? off : kOob, s.sob, s.bdst + i * 1024);
+        }
+    }
+
+    template <int I = 0>
+    __device__ __forceinline__ static void copy_all(const Lane &L, const Stage &s) {
+        if constexpr (I < DMA_PER_WAVE) {
+            copy_one<I>(L, s);
+            copy_all<I + 1>(L, s);
+        }
+    }
+
+    struct Frags {
+        u32x4_t a[4];     // A operand per mi
+        s16x4_t b[4][2];  // B operand per ni, two halves of 4 k values
+    };
+
+    // Operand read number P of the 12 that make up one kk block, in the order
+    // the MFMAs of a block consume them: a0, b0 (2 halves), b1, b2, b3, a1..a3.
+    template <int P>
+    __device__ __forceinline__ static void read_piece(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
+        if constexpr (P == 0) {
+            f.a[0] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk]);
+        } else if constexpr (P <= 8) {
+            constexpr int ni = (P - 1) / 2, h = (P - 1) % 2;
+            f.b[ni][h] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 8192 + h * 2048));
+        } else {
+            constexpr int mi = P - 8;
+            f.a[mi] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk] + mi * 32 * BK * 2);
+        }
+    }
+
+    template <int P = 0>
+    __device__ __forceinline__ static void read_all(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
+        if constexpr (P < 12) {
+            read_piece<P>(L, buf, kk, f);
+            read_all<P + 1>(L, buf, kk, f);
+        }
+    }
+
+    template <int I>
+    __device__ __forceinline__ static void mma_one(const Frags &f, f32x16_t (&acc)[4][4]) {
+        constexpr int mi = I / 4, ni = I % 4;
+        const s16x8_t bv = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (DT == FL_F16)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bv),
+                                                                 __builtin_bit_cast(f16x8_t, f.a[mi]), acc[mi][ni], 0,
+                                                                 0, 0);
+        else
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv),
+                                                                  __builtin_bit_cast(bf16x8_t, f.a[mi]), acc[mi][ni],
+                                                                  0, 0, 0);
+    }
+
+    // One block: the 16 MFMAs on `use`, with the 12 operand reads of block
+    // kk_next of buffer `src` (into `fill`) slotted after MFMAs 4..15 and,
+    // when COPY, the copies of a look-ahead stage after MFMAs
+    // 0..DMA_PER_WAVE-1.  Without copies the reads follow MFMAs 0..11.
+    template <int I, bool COPY>
+    __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next, const Stage &s,
+                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][4]) {
+        if constexpr (I < 16) {
+            mma_one<I>(use, acc);
+            if constexpr (COPY && I < DMA_PER_WAVE) copy_one<I>(L, s);
+            constexpr int R = COPY ? I - 4 : I;
+            if constexpr (R >= 0 && R < 12) read_piece<R>(L, src, kk_next, fill);
+            __builtin_amdgcn_sched_barrier(0);
+            block<I + 1, COPY>(L, src, kk_next, s, use, fill, acc);
+        }
+    }
+
+    // vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
+    template <int N>
+    __device__ __forceinline__ static void wait_vm() {
+        static_assert(N >= 0 && N < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    }
+
+    // Blocks J..KK-1 of stage kt, held in buffer B.  On entry the operands of
+    // block J are in f[J & 1].  Before the last block: wait until this
+    // wave's copies of stage kt+1 have landed (those of stages kt+2 ..
+    // kt+NBUF-1 stay in flight) and barrier, after which stage kt+1 is
+    // visible to every wave and buffer B has been read by all of them, so
+    // the last block refills it with stage kt+NBUF while reading stage
+    // kt+1's first operands.
+    template <int B, int J = 0>
+    __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
+                                                 uint32_t lds_addr, int kt, int wave, Frags (&f)[2],
+                                                 f32x16_t (&acc)[4][4]) {
+        if constexpr (J < KK - 1) {
+            const Stage none{};
+            block<0, false>(L, lds + B * BUF_BYTES, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
+            stage<B, J + 1>(a, L, lds, lds_addr, kt, wave, f, acc);
+        } else {
+            wait_vm<(NBUF - 2) * DMA_PER_WAVE>();
+            __syncthreads();
+            const Stage s = stage_of(a, kt + NBUF, wave, lds_addr + B * BUF_BYTES);
+            block<0, true>(L, lds + ((B + 1) % NBUF) * BUF_BYTES, 0, s, f[J & 1], f[(J + 1) & 1], acc);
+        }
+    }
+
+    template <int B>
+    __device__ __forceinline__ static void stage_group(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
+                                                       uint32_t lds_addr, int kt, int wave, Frags (&f)[2],
+                                                       f32x16_t (&acc)[4][4]) {
+        if constexpr (B < NBUF) {
+            stage<B>(a, L, lds, lds_addr, kt + B, wave, f, acc);
+            stage_group<B + 1>(a, L, lds, lds_addr, kt, wave, f, acc);
+        }
+    }
+
+    // Remaining stages kt.. nk-1 (fewer than NBUF), buffers 0.. in order.
+    template <int B>
+    __device__ __forceinline__ static void stage_tail(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
+                                                      uint32_t lds_addr, int kt, int nk, int wave, Frags (&f)[2],
+                                                      f32x16_t (&acc)[4][4]) {
+        if constexpr (B < NBUF - 1) {
+            if (kt + B < nk) {
+                stage<B>(a, L, lds, lds_addr, kt + B, wave, f, acc);
+                stage_tail<B + 1>(a, L, lds, lds_addr, kt, nk, wave, f, acc);
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave >> 1, wn = wave & 1;
+        int tm, tn;
+        grouped_tile(pid, a.tiles_m, a.tiles_n, a.group, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const FL_LDS char *lds = (const FL_LDS char *)smem;
+        const uint32_t lds_addr = (uint32_t)(uintptr_t)(FL_LDS void *)smem;
+
+        f32x16_t acc[4][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+
+        const int nk = (a.K + BK - 1) / BK;
+        if (nk > 0) {
+            Lane L;
+            setup(a, m0, n0, wave, lane, wm, wn, L);
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) copy_all(L, stage_of(a, b, wave, lds_addr + b * BUF_BYTES));
+            wait_vm<(NBUF - 1) * DMA_PER_WAVE>();
+            __syncthreads();
+            Frags f[2];
+            read_all(L, lds, 0, f[0]);
+            int kt = 0;
+            // Whole groups of NBUF stages, no branch inside, so the buffer of
+            // every stage is a compile-time constant.
+            for (; kt + NBUF <= nk; kt += NBUF) stage_group<0>(a, L, lds, lds_addr, kt, wave, f, acc);
+            stage_tail<0>(a, L, lds, lds_addr, kt, nk, wave, f, acc);
+            // The look-ahead copies (past the end of K) must land before this
+            // workgroup's LDS is reused.
+            wait_vm<0>();
+            __syncthreads();
+        }
+        base::epilogue(a, m0, n0, wm, wn, lane, acc);
+        if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
+    }
+};
+
+// Register-staged variant of the same pipeline (NBUF = 2, BK = 64): the
+// copies of a stage go global -> VGPR (buffer_load_dwordx4, 16 per wave)
+// -> LDS (ds_write_b128 at the position the direct copy would have used),
+// so the LDS layout, the operand reads and the MFMA order -- and therefore
+// the results, bit for bit -- are those of Dma16.  Loads of stage kt+2 are
+// issued in the last block of stage kt (right after the barrier that
+// follows the writes of stage kt+1); their writes go into the free buffer
+// during block 2 of stage kt+1, before the barrier that publishes them.
+template <int DT, int ACT>
+struct Stg16 : Dma16<DT, ACT, 64> {
+    using D = Dma16<DT, ACT, 64>;
+    using typename D::Frags;
+    using typename D::Lane;
+    using typename D::Stage;
+    static constexpr int NA = D::NA, NB = D::NB, NC = D::DMA_PER_WAVE, KK = D::KK, BUF_BYTES = D::BUF_BYTES;
+    static constexpr int A_BYTES = D::A_BYTES;
+
+    struct Regs {
+        u32x4_t v[NC];
+    };
+
+    template <int I>
+    __device__ __forceinline__ static void load_one(const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
+                                                    const __amdgpu_buffer_rsrc_t &rB, const Stage &s, Regs &r) {
+        if constexpr (I < NA) {
+            const uint32_t off = L.a_off[I & 1] + (uint32_t)(I >> 1) * L.a_step;
+            r.v[I] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, L.a_k[I & 1] < s.kleft ? off : kOob, s.soa, 0));
+        } else {
+            constexpr int i = I - NA;
+            const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
+            const bool ok = (L.b_k0 + 2 * i < s.kleft) && (L.b_off[i & 1] != kOob);
+            r.v[I] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? off : kOob, s.sob, 0));
+        }
+    }
+
+    // LDS byte address of copy I of this wave's lane within a buffer.
+    template <int I>
+    __device__ __forceinline__ static int store_addr(int wave, int lane) {
+        if constexpr (I < NA)
+            return (wave * NA + I) * 1024 + lane * 16;
+        else
+            return A_BYTES + (wave * NB + (I - NA)) * 1024 + lane * 16;
+    }
+
+    // Block of 16 MFMAs on `use` with the reads of (src, kk_next) into fill,
+    // plus one load (MODE 1) or one LDS write (MODE 2) per MFMA slot.
+    template <int I, int MODE>
+    __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next,
+                                                 const __amdgpu_buffer_rsrc_t &rA, const __amdgpu_buffer_rsrc_t &rB,
+                                                 const Stage &s, FL_LDS char *wbuf, int wave, int lane, Regs &r,
+                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][4]) {
+        if constexpr (I < 16) {
+            D::template mma_one<I>(use, acc);
+            if constexpr (MODE == 1) load_one<I>(L, rA, rB, s, r);
+            if constexpr (MODE == 2) *(FL_LDS u32x4_t *)(wbuf + store_addr<I>(wave, lane)) = r.v[I];
+            constexpr int R = (MODE == 1) ? I - 4 : I;
+            if constexpr (R >= 0 && R < 12) D::template read_piece<R>(L, src, kk_next, fill);
+            __builtin_amdgcn_sched_barrier(0);
+            block<I + 1, MODE>(L, src, kk_next, rA, rB, s, wbuf, wave, lane, r, use, fill, acc);
+        }
+    }
+
+    // Stage kt in buffer B (operands of block 0 in f[0]; loads of stage kt+1
+    // in flight in r).
+    template <int B>
+    __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
+                                                 const __amdgpu_buffer_rsrc_t &rB, FL_LDS char *lds, int kt,
+                                                 int wave, int lane, Regs &r, Frags (&f)[2], f32x16_t (&acc)[4][4]) {
+        FL_LDS char *cur = lds + B * BUF_BYTES;
+        FL_LDS char *nxt = lds + (B ^ 1) * BUF_BYTES;
+        const Stage none{};
+        block<0, 0>(L, cur, 1, rA, rB, none, nullptr, wave, lane, r, f[0], f[1], acc);
+        block<0, 0>(L, cur, 2, rA, rB, none, nullptr, wave, lane, r, f[1], f[0], acc);
+        block<0, 2>(L, cur, 3, rA, rB, none, nxt, wave, lane, r, f[0], f[1], acc);
+        __syncthreads();  // stage kt+1 written by every wave; buffer B fully read
+        const Stage s = D::stage_of(a, kt + 2, wave, 0);
+        block<0, 1>(L, nxt, 0, rA, rB, s, nullptr, wave, lane, r, f[1], f[0], acc);
+    }
+
+    __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave >> 1, wn = wave & 1;
+        int tm, tn;
+        grouped_tile(pid, a.tiles_m, a.tiles_n, a.group, tm, tn);
+        const int m0 = tm * D::BM, n0 = tn * D::BN;
+        FL_LDS char *lds = (FL_LDS char *)smem;
+
+        f32x16_t acc[4][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+
+        const int nk = (a.K + D::BK - 1) / D::BK;
+        if (nk > 0) {
+            Lane L;
+            D::setup(a, m0, n0, wave, lane, wm, wn, L);
+            const size_t a_org = (size_t)m0 * a.K;
+            const __amdgpu_buffer_rsrc_t rA =
+                make_rsrc(static_cast<const char *>(a.A) + a_org * 2, ((size_t)a.M * a.K - a_org) * 2);
+            const __amdgpu_buffer_rsrc_t rB =
+                make_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * 2, ((size_t)a.K * a.N - n0) * 2);
+            Regs r;
+            // stage 0 -> buffer 0, then stage 1 loads in flight
+            const Stage s0 = D::stage_of(a, 0, wave, 0);
+            load_all(L, rA, rB, s0, r);
+            store_all(lds, wave, lane, r);
+            const Stage s1 = D::stage_of(a, 1, wave, 0);
+            load_all(L, rA, rB, s1, r);
+            __syncthreads();
+            Frags f[2];
+            D::read_all(L, lds, 0, f[0]);
+            int kt = 0;
+            for (; kt + 2 <= nk; kt += 2) {
+                stage<0>(a, L, rA, rB, lds, kt, wave, lane, r, f, acc);
+                stage<1>(a, L, rA, rB, lds, kt + 1, wave, lane, r, f, acc);
+            }
+            if (kt < nk) stage<0>(a, L, rA, rB, lds, kt, wave, lane, r, f, acc);
+            // the look-ahead loads past the end of K are still in flight
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        D::base::epilogue(a, m0, n0, wm, wn, lane, acc);
+        if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
+    }
+
+    template <int I = 0>
+    __device__ __forceinline__ static void load_all(const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
+                                                    const __amdgpu_buffer_rsrc_t &rB, const Stage &s, Regs &r) {
+        if constexpr (I < NC) {
+            load_one<I>(L, rA, rB, s, r);
+            load_all<I + 1>(L, rA, rB, s, r);
+        }
+    }
+    template <int I = 0>
+    __device__ __forceinline__ static void store_all(FL_LDS char *buf, int wave, int lane, const Regs &r) {
+        if constexpr (I < NC) {
+            *(FL_LDS u32x4_t *)(buf + store_addr<I>(wave, lane)) = r.v[I];
+            store_all<I + 1>(buf, wave, lane, r);
+        }
+    }
+};
+
+template <int DT, int ACT>
+__global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArgs a) {
+    using T = Stg16<DT, ACT>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * T::BUF_BYTES];
+    const int ntiles = a.tiles_m * a.tiles_n;
+    if (!a.persistent) {
+        const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+        T::run_tile(a, pid, smem);
+    } else {
+        const int G = gridDim.x;
+        const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
+        for (int base = 0; base < ntiles; base += G) {
+            const int pid = base + slot;
+            if (pid < ntiles) T::run_tile(a, pid, smem);
+            __syncthreads();
+        }
+    }
+}
+
+template <int DT, int ACT, int BK>
+__global__ void __launch_bounds__(kThreads, 1) fused_linear_dma16_kernel(GemmArgs a) {
+    using T = Dma16<DT, ACT, BK>;
+    __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF_BYTES];
+    const int ntiles = a.tiles_m * a.tiles_n;
+    if (!a.persistent) {
+        const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+        T::run_tile(a, pid, smem);
+    } else {
+        const int G = gridDim.x;
+        const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
+        for (int base = 0; base < ntiles; base += G) {
+            const int pid = base + slot;
+            if (pid < ntiles) T::run_tile(a, pid, smem);
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace fl

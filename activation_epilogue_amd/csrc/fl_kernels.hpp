@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fused_linear.h"
 
 namespace fl {
@@ -340,35 +342,41 @@ struct FusedTile {
         }
     }
 
-    // Four consecutive elements at byte offset off (vector path: one 8- or
-    // 16-byte access) or element by element with per-element validity.
-    __device__ __forceinline__ static void load4(__amdgpu_buffer_rsrc_t r, uint32_t off, bool full, int valid,
-                                                 float (&v)[4]) {
-        if (VECTOR && full) {
-            if constexpr (ES == 2) {
-                const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-                v[0] = io::to_f32(raw(w[0] & 0xffffu));
-                v[1] = io::to_f32(raw(w[0] >> 16));
-                v[2] = io::to_f32(raw(w[1] & 0xffffu));
-                v[3] = io::to_f32(raw(w[1] >> 16));
-            } else {
-                const f32x4_t w = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = w[e];
-            }
+    // Raw bits of 4 consecutive elements (8 bytes for fp16/bf16, 16 for fp32).
+    using quad_t = typename std::conditional<ES == 2, u32x2_t, u32x4_t>::type;
+
+    // Load 4 consecutive elements at byte offset off: one 8- or 16-byte access
+    // when all 4 are in range on the vector path, else element by element
+    // (elements past `valid`, or the whole group when off is kOob, read 0).
+    __device__ __forceinline__ static quad_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+        if (VECTOR && valid >= 4) {
+            if constexpr (ES == 2)
+                return __builtin_bit_cast(quad_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+            else
+                return __builtin_bit_cast(quad_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         } else {
+            bits e[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bits b = load_elem<ES>(r, e < valid ? off + e * ES : kOob);
-                v[e] = io::to_f32(__builtin_bit_cast(raw, b));
-            }
+            for (int i = 0; i < 4; ++i) e[i] = load_elem<ES>(r, i < valid ? off + i * ES : kOob);
+            return __builtin_bit_cast(quad_t, e);
         }
+    }
+
+    __device__ __forceinline__ static float elem_f32(const quad_t &q, int i) {
+        if constexpr (ES == 2)
+            return io::to_f32(raw((i & 1) ? (q[i >> 1] >> 16) : (q[i >> 1] & 0xffffu)));
+        else
+            return __builtin_bit_cast(f32x4_t, q)[i];
     }
 
     // --- epilogue: bias, activation, one conversion, one masked store ---
     // Lane (lrow, lg) of wave (wm, wn) holds, for block (mi, ni) and group q,
     // out[m0 + wm*128 + mi*32 + lrow][n0 + wn*128 + ni*32 + q*8 + lg*4 + 0..3]
     // in acc[mi][ni][q*4 + 0..3].  Offsets are relative to (m0, n0).
+    // gfx9 counts stores in vmcnt, so a load issued after a store makes its
+    // consumer wait for that store too.  The bias of all 16 column groups is
+    // therefore loaded before any store, and the gate operand of row block
+    // mi+1 is loaded before the stores of row block mi.
     __device__ __forceinline__ static void epilogue(const GemmArgs &a, int m0, int n0, int wm, int wn, int lane,
                                                     const f32x16_t (&acc)[4][4]) {
         const size_t o_org = (size_t)m0 * a.N + n0;
@@ -380,39 +388,58 @@ struct FusedTile {
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * ES : nullptr,
                       a.bias ? (size_t)(a.N - n0) * ES : 0);
         const int lrow = lane & 31, lg = lane >> 5;
+        int col[16], valid[16];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+        for (int g = 0; g < 16; ++g) {
+            col[g] = wn * 128 + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
+            valid[g] = a.N - n0 - col[g];
+        }
+        quad_t bq[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wn * 128 + ni * 32 + q * 8 + lg * 4;  // within the tile
-                const int valid = a.N - n0 - col;                   // elements left in the row
-                const bool full = valid >= 4;
-                float b[4] = {0.f, 0.f, 0.f, 0.f};
-                if (a.bias) load4(rBias, valid > 0 ? (uint32_t)col * ES : kOob, full, valid, b);
+        for (int g = 0; g < 16; ++g) {
+            bq[g] = quad_t{};
+            if (a.bias) bq[g] = load4(rBias, valid[g] > 0 ? (uint32_t)col[g] * ES : kOob, valid[g]);
+        }
+        auto offset = [&](int mi, int g) -> uint32_t {
+            const int row = wm * 128 + mi * 32 + lrow;
+            return (m0 + row < a.M && valid[g] > 0) ? (uint32_t)(row * a.N + col[g]) * ES : kOob;
+        };
+        quad_t yq[2][16];
+        if constexpr (ACT == FL_ACT_GLU) {
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    const int row = wm * 128 + mi * 32 + lrow;
-                    const bool ok = (m0 + row < a.M) && valid > 0;
-                    const uint32_t off = ok ? (uint32_t)(row * a.N + col) * ES : kOob;
-                    float y[4] = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (ACT == FL_ACT_GLU) load4(rY, off, full, valid, y);
-                    bits o[4];
+            for (int g = 0; g < 16; ++g) yq[0][g] = load4(rY, offset(0, g), valid[g]);
+        }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = __builtin_bit_cast(bits, io::from_f32(activate<ACT>(acc[mi][ni][q * 4 + e] + b[e], y[e])));
-                    if (VECTOR && full) {
-                        if constexpr (ES == 2) {
-                            u32x2_t w;
-                            w[0] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                            w[1] = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, w), rO, off, 0, 0);
-                        } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, o), rO, off, 0, 0);
-                        }
+        for (int mi = 0; mi < 4; ++mi) {
+            if constexpr (ACT == FL_ACT_GLU) {
+                if (mi + 1 < 4) {
+#pragma unroll
+                    for (int g = 0; g < 16; ++g) yq[(mi + 1) & 1][g] = load4(rY, offset(mi + 1, g), valid[g]);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                const int ni = g >> 2, q = g & 3;
+                const uint32_t off = offset(mi, g);
+                bits o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = (ACT == FL_ACT_GLU) ? elem_f32(yq[mi & 1][g], e) : 0.0f;
+                    const float x = acc[mi][ni][q * 4 + e] + elem_f32(bq[g], e);
+                    o[e] = __builtin_bit_cast(bits, io::from_f32(activate<ACT>(x, y)));
+                }
+                if (VECTOR && valid[g] >= 4) {
+                    if constexpr (ES == 2) {
+                        u32x2_t w;
+                        w[0] = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                        w[1] = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, w), rO, off, 0, 0);
                     } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) store_elem<ES>(o[e], rO, e < valid ? off + e * ES : kOob);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, o), rO, off, 0, 0);
                     }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) store_elem<ES>(o[e], rO, e < valid[g] ? off + e * ES : kOob);
                 }
             }
         }
@@ -550,9 +577,11 @@ __global__ void __launch_bounds__(kThreads) activation_kernel(const void *Xv, co
 
 typedef void (*fused_launcher)(const GemmArgs &, int grid, hipStream_t);
 
-// Returns the launcher of fused_linear_kernel<DT, act, vec>; defined in the
-// per-dtype instantiation unit.
+// Returns the launcher of the fused kernel for (DT, act): the direct-to-LDS
+// fp16/bf16 kernel when `vec` and variant != 1 (variant 2: 32-deep K stages),
+// else the register-staged kernel with the vector or element load path.  Defined in the per-dtype
+// instantiation unit.
 template <int DT>
-fused_launcher pick_fused_for(int act, bool vec);
+fused_launcher pick_fused_for(int act, bool vec, int variant);
 
 }  // namespace fl

@@ -59,10 +59,10 @@ int cu_count() {
 
 // The fused kernels of each dtype are compiled in their own translation unit
 // (fl_fused_inst.hip built once per dtype) so the build runs in parallel.
-fl::fused_launcher pick_fused(int dtype, int act, bool vec) {
-    if (dtype == FL_F32) return fl::pick_fused_for<FL_F32>(act, vec);
-    if (dtype == FL_F16) return fl::pick_fused_for<FL_F16>(act, vec);
-    return fl::pick_fused_for<FL_BF16>(act, vec);
+fl::fused_launcher pick_fused(int dtype, int act, bool vec, int variant) {
+    if (dtype == FL_F32) return fl::pick_fused_for<FL_F32>(act, vec, variant);
+    if (dtype == FL_F16) return fl::pick_fused_for<FL_F16>(act, vec, variant);
+    return fl::pick_fused_for<FL_BF16>(act, vec, variant);
 }
 
 struct TileShape {
@@ -71,7 +71,7 @@ struct TileShape {
 
 fl_status tile_shape(const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg == 0 || cfg == 1) {
+    if (cfg >= 0 && cfg <= 5 && cfg != 2) {
         t = {256, 256};
         return FL_OK;
     }
@@ -173,7 +173,10 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
     }
-    pick_fused(dtype, act, vector_path)(a, grid, static_cast<hipStream_t>(stream));
+    // variant: 0 = default kernel for the dtype/path, 1 = register-staged,
+    // 2 = direct-to-LDS with 32-deep K stages, 3 = same pipeline staged through VGPRs
+    const int variant = !opt ? 0 : opt->tile_cfg == 3 ? 1 : opt->tile_cfg == 4 ? 2 : opt->tile_cfg == 5 ? 3 : 0;
+    pick_fused(dtype, act, vector_path, variant)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
 }
 

@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
@@ -149,6 +151,15 @@ def main():
         fl.fused_linear(A, B, bias, Y, act=w.act, out=out, **opts)
 
     ms_event, ms_wall = time_loop(step, args.steps, args.warmup, stream)
+    if args.calib_copy_mib:
+        # A plain copy of known size, outside the timed region, so that memory
+        # counters taken over this run can be scaled to bytes.
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     flops = w.flops
     tflops = flops / (ms_wall * 1e-3) / 1e12
     achieved = flops / (ms_event * 1e-3) / 1e12

@@ -88,7 +88,12 @@ typedef struct {
                            1 gives row-major tile order. */
     int32_t persistent; /* 0 = one workgroup per output tile; 1 = a grid sized
                            to the GPU whose workgroups loop over tiles. */
-    int32_t tile_cfg;   /* 0 = automatic; 1 = 256x256 tiles; 2 = 128x128. */
+    int32_t tile_cfg;   /* 0 = automatic (= 1); 1 = 256x256 tiles, for
+                           16-byte aligned fp16/bf16 direct-to-LDS copies
+                           with 64-deep K stages; 3 = 256x256 with
+                           register-staged loads (the fp32 and unaligned
+                           path) for every dtype; 4 = as 1 with 32-deep K
+                           stages.  Any other value is FL_ERR_UNSUPPORTED. */
     int32_t no_xcd_remap; /* 0 = place neighbouring tiles on one XCD; 1 = off */
     uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
                            counters (see fl_tile_grid); each output tile adds
