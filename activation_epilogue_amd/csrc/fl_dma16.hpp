@@ -1,8 +1,12 @@
 // fl_dma16.hpp -- fp16/bf16 fused GEMM with direct-to-LDS loads.
 //
-// Same contract and epilogue as FusedTile (fl_kernels.hpp); this variant is
-// used when A, B, out (and bias, Y) are 16-byte aligned and K, N are
-// multiples of 8.  Differences from the register-staged kernel:
+// Same contract and epilogue as FusedTile (fl_kernels.hpp); this variant
+// serves every fp16/bf16 problem.  Pointers need only element alignment:
+// 16-byte buffer loads and the 8-byte epilogue accesses may be unaligned on
+// gfx950.  With N % 8 != 0 a B chunk that crosses N brings in the next row's
+// first values, which only reach output columns >= N (never stored); with
+// K % 8 != 0 the straddling A chunk is zeroed in LDS (fix_k_tail) and B's
+// rows >= K are read as zeros.  Differences from the register-staged kernel:
 //
 //   * Global -> LDS copies use buffer_load_dwordx4 with the LDS bit: each
 //     instruction moves 64 x 16 bytes straight into 1 KB of LDS at
@@ -191,6 +195,60 @@ struct Dma16 {
         }
     }
 
+    // Fix-up of the last K stage (origin kt*BK) when K or N is not a
+    // multiple of 8, run by each wave on the chunks it copied, after its
+    // copies have landed and before the barrier that publishes them:
+    //  * an A chunk that straddles K also holds the first values of the next
+    //    row; the values at or past K are zeroed so that only k < K reaches
+    //    the accumulators;
+    //  * a copy that runs past the end of A (or B) is range-checked per
+    //    dword, so the dword that holds the buffer's last element can read as
+    //    zero.  The lane whose chunk holds A[M-1][K-1] (B[K-1][N-1]) reloads
+    //    that element with a 2-byte load and writes it into LDS.
+    __device__ __forceinline__ static void fix_k_tail(const GemmArgs &a, const Lane &L, int m0, int n0, int kt,
+                                                      int wave, int lane, FL_LDS char *buf) {
+        const int k0 = kt * BK, kleft = a.K - k0;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, (size_t)a.M * a.K * 2);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, (size_t)a.K * a.N * 2);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int kb = L.a_k[i & 1];
+            const int valid = kleft - kb;  // values of this chunk below K
+            if (valid > 0 && valid < 8) {
+                FL_LDS char *p = buf + (wave * NA + i) * 1024 + lane * 16;
+                u32x4_t v = *(FL_LDS u32x4_t *)p;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t keep = (2 * d + 1 < valid) ? 0xffffffffu : (2 * d < valid) ? 0x0000ffffu : 0u;
+                    v[d] &= keep;
+                }
+                const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
+                if (row == a.M - 1) {
+                    const uint32_t e = (uint32_t)(valid - 1);
+                    const uint32_t x =
+                        (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rA, (uint32_t)((size_t)a.M * a.K - 1) * 2, 0, 0);
+                    v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
+                }
+                *(FL_LDS u32x4_t *)p = v;
+            }
+        }
+        if (a.N & 7) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int rb = L.b_k0 + 2 * i;  // K row within the stage
+                const int cb = (lane & 31) ^ fb(rb);
+                const int col = n0 + cb * 8;
+                if (rb == kleft - 1 && col <= a.N - 1 && a.N - 1 < col + 8) {
+                    const int e = a.N - 1 - col;
+                    FL_LDS uint16_t *q =
+                        (FL_LDS uint16_t *)(buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16 + 2 * e);
+                    *q = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)((size_t)a.K * a.N - 1) * 2, 0,
+                                                                         0);
+                }
+            }
+        }
+    }
+
     struct Frags {
         u32x4_t a[4];     // A operand per mi
         s16x4_t b[4][2];  // B operand per ni, two halves of 4 k values
@@ -251,11 +309,14 @@ struct Dma16 {
         }
     }
 
-    // vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
+    // vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).  The
+    // copies are invisible to the compiler, so the wait is also a compiler
+    // memory barrier: no LDS access may be moved above it.
     template <int N>
     __device__ __forceinline__ static void wait_vm() {
         static_assert(N >= 0 && N < 64, "vmcnt range");
         __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        asm volatile("" ::: "memory");
     }
 
     // Blocks J..KK-1 of stage kt, held in buffer B.  On entry the operands of
@@ -267,14 +328,17 @@ struct Dma16 {
     // kt+1's first operands.
     template <int B, int J = 0>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                 uint32_t lds_addr, int kt, int wave, Frags (&f)[2],
+                                                 uint32_t lds_addr, int m0, int n0, int kt, int wave, Frags (&f)[2],
                                                  f32x16_t (&acc)[4][4]) {
         if constexpr (J < KK - 1) {
             const Stage none{};
             block<0, false>(L, lds + B * BUF_BYTES, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
-            stage<B, J + 1>(a, L, lds, lds_addr, kt, wave, f, acc);
+            stage<B, J + 1>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
         } else {
             wait_vm<(NBUF - 2) * DMA_PER_WAVE>();
+            if (((a.K | a.N) & 7) && kt + 2 == (a.K + BK - 1) / BK)
+                fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63,
+                           (FL_LDS char *)lds + ((B + 1) % NBUF) * BUF_BYTES);
             __syncthreads();
             const Stage s = stage_of(a, kt + NBUF, wave, lds_addr + B * BUF_BYTES);
             block<0, true>(L, lds + ((B + 1) % NBUF) * BUF_BYTES, 0, s, f[J & 1], f[(J + 1) & 1], acc);
@@ -283,23 +347,23 @@ struct Dma16 {
 
     template <int B>
     __device__ __forceinline__ static void stage_group(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                       uint32_t lds_addr, int kt, int wave, Frags (&f)[2],
-                                                       f32x16_t (&acc)[4][4]) {
+                                                       uint32_t lds_addr, int m0, int n0, int kt, int wave,
+                                                       Frags (&f)[2], f32x16_t (&acc)[4][4]) {
         if constexpr (B < NBUF) {
-            stage<B>(a, L, lds, lds_addr, kt + B, wave, f, acc);
-            stage_group<B + 1>(a, L, lds, lds_addr, kt, wave, f, acc);
+            stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
+            stage_group<B + 1>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
         }
     }
 
     // Remaining stages kt.. nk-1 (fewer than NBUF), buffers 0.. in order.
     template <int B>
     __device__ __forceinline__ static void stage_tail(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                      uint32_t lds_addr, int kt, int nk, int wave, Frags (&f)[2],
-                                                      f32x16_t (&acc)[4][4]) {
+                                                      uint32_t lds_addr, int m0, int n0, int kt, int nk, int wave,
+                                                      Frags (&f)[2], f32x16_t (&acc)[4][4]) {
         if constexpr (B < NBUF - 1) {
             if (kt + B < nk) {
-                stage<B>(a, L, lds, lds_addr, kt + B, wave, f, acc);
-                stage_tail<B + 1>(a, L, lds, lds_addr, kt, nk, wave, f, acc);
+                stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
+                stage_tail<B + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, wave, f, acc);
             }
         }
     }
@@ -329,14 +393,15 @@ struct Dma16 {
 #pragma unroll
             for (int b = 0; b < NBUF; ++b) copy_all(L, stage_of(a, b, wave, lds_addr + b * BUF_BYTES));
             wait_vm<(NBUF - 1) * DMA_PER_WAVE>();
+            if (((a.K | a.N) & 7) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
             __syncthreads();
             Frags f[2];
             read_all(L, lds, 0, f[0]);
             int kt = 0;
             // Whole groups of NBUF stages, no branch inside, so the buffer of
             // every stage is a compile-time constant.
-            for (; kt + NBUF <= nk; kt += NBUF) stage_group<0>(a, L, lds, lds_addr, kt, wave, f, acc);
-            stage_tail<0>(a, L, lds, lds_addr, kt, nk, wave, f, acc);
+            for (; kt + NBUF <= nk; kt += NBUF) stage_group<0>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
+            stage_tail<0>(a, L, lds, lds_addr, m0, n0, kt, nk, wave, f, acc);
             // The look-ahead copies (past the end of K) must land before this
             // workgroup's LDS is reused.
             wait_vm<0>();
@@ -347,7 +412,8 @@ struct Dma16 {
     }
 };
 
-// Register-staged variant of the same pipeline (NBUF = 2, BK = 64): the
+// Register-staged variant of the same pipeline (NBUF = 2, BK = 64, K and N
+// multiples of 8): the
 // copies of a stage go global -> VGPR (buffer_load_dwordx4, 16 per wave)
 // -> LDS (ds_write_b128 at the position the direct copy would have used),
 // so the LDS layout, the operand reads and the MFMA order -- and therefore

@@ -150,8 +150,10 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
     const int es = (int)elem_size(dtype);
     const int vec = 16 / es;
-    const bool vector_path = (K % vec == 0) && (N % vec == 0) && aligned(A, 16) && aligned(B, 16) &&
-                             aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16));
+    // fp16/bf16 take the direct-to-LDS kernel at any alignment (variant 0, 2);
+    // the register-staged kernel needs 16-byte aligned rows for its vector path.
+    const bool aligned_rows = (K % vec == 0) && (N % vec == 0) && aligned(A, 16) && aligned(B, 16) &&
+                              aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16));
     fl::GemmArgs a;
     a.A = A;
     a.B = B;
@@ -176,7 +178,10 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     // variant: 0 = default kernel for the dtype/path, 1 = register-staged,
     // 2 = direct-to-LDS with 32-deep K stages, 3 = same pipeline staged through VGPRs
     const int variant = !opt ? 0 : opt->tile_cfg == 3 ? 1 : opt->tile_cfg == 4 ? 2 : opt->tile_cfg == 5 ? 3 : 0;
-    pick_fused(dtype, act, vector_path, variant)(a, grid, static_cast<hipStream_t>(stream));
+    const bool direct = dtype != FL_F32 && (variant == 0 || variant == 2);
+    const bool use_vec = direct || aligned_rows;
+    if (variant == 3 && !aligned_rows) return fail(FL_ERR_UNSUPPORTED, "tile_cfg 5 needs 16-byte aligned rows");
+    pick_fused(dtype, act, use_vec, variant)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
 }
 
