@@ -84,7 +84,7 @@ typedef enum {
 /* Tuning and debug options of fl_fused_linear_ex.  Zero-initialise and set
  * what you need; every field's zero means "default". */
 typedef struct {
-    int32_t group_m;    /* M-tiles per band of the grouped program map; 0 = 8.
+    int32_t group_m;    /* M-tiles per band of the grouped program map; 0 = 4.
                            1 gives row-major tile order. */
     int32_t persistent; /* 0 = one workgroup per output tile; 1 = a grid sized
                            to the GPU whose workgroups loop over tiles. */
@@ -109,7 +109,7 @@ typedef struct {
  *         otherwise (a non-NULL Y with another act is FL_ERR_INVALID_ARG).
  *   out   (M,N) device pointer.
  *   stream  hipStream_t to enqueue on.
- * Uses the default options (grouped map with 8 M-tiles per band, automatic
+ * Uses the default options (grouped map with 4 M-tiles per band, automatic
  * tile size, XCD-aware placement).
  */
 fl_status fl_fused_linear(const void *A, const void *B, const void *bias,
