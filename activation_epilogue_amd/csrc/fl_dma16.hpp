@@ -368,6 +368,102 @@ struct Dma16 {
         }
     }
 
+    // --- epilogue through LDS ---
+    // Phase 1 (registers): bias, activation and the one conversion, exactly
+    // as FusedTile::epilogue computes them (same arithmetic, same order);
+    // each lane writes its 4-value groups into the wave's private LDS area
+    // (128 rows of 256 bytes, rows padded to EPI_ROW bytes so the 32 rows a
+    // write instruction touches fall in different banks).  Phase 2: each
+    // lane reads 16 bytes of a row back and stores them, so a store
+    // instruction writes 4 whole rows of 256 bytes (full 128-byte lines).
+    static constexpr int EPI_ROW = 256 + 16;
+    static constexpr int EPI_WAVE = 128 * EPI_ROW;
+    static constexpr int EPI_BYTES = 4 * EPI_WAVE;
+
+    __device__ __forceinline__ static void epilogue_lds(const GemmArgs &a, int m0, int n0, int wave, int wm, int wn,
+                                                        int lane, const f32x16_t (&acc)[4][4], FL_LDS char *lds) {
+        using io = Io<DT>;
+        using quad_t = u32x2_t;
+        const size_t o_org = (size_t)m0 * a.N + n0;
+        const size_t o_bytes = ((size_t)a.M * a.N - o_org) * 2;
+        const __amdgpu_buffer_rsrc_t rO = make_rsrc(static_cast<char *>(a.out) + o_org * 2, o_bytes);
+        const __amdgpu_buffer_rsrc_t rY =
+            make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * 2 : nullptr, a.Y ? o_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rBias =
+            make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * 2 : nullptr,
+                      a.bias ? (size_t)(a.N - n0) * 2 : 0);
+        FL_LDS char *wbuf = lds + wave * EPI_WAVE;
+        const int lrow = lane & 31, lg = lane >> 5;
+        int col[16], valid[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            col[g] = wn * 128 + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
+            valid[g] = a.N - n0 - col[g];
+        }
+        quad_t bq[16];
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            bq[g] = quad_t{};
+            if (a.bias) bq[g] = base::load4(rBias, valid[g] > 0 ? (uint32_t)col[g] * 2 : kOob, valid[g]);
+        }
+        auto yoff = [&](int mi, int g) -> uint32_t {
+            const int row = wm * 128 + mi * 32 + lrow;
+            return (m0 + row < a.M && valid[g] > 0) ? (uint32_t)(row * a.N + col[g]) * 2 : kOob;
+        };
+        quad_t yq[2][16];
+        if constexpr (ACT == FL_ACT_GLU) {
+#pragma unroll
+            for (int g = 0; g < 16; ++g) yq[0][g] = base::load4(rY, yoff(0, g), valid[g]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if constexpr (ACT == FL_ACT_GLU) {
+                if (mi + 1 < 4) {
+#pragma unroll
+                    for (int g = 0; g < 16; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                const int ni = g >> 2, q = g & 3;
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
+                    const float x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
+                    o[e] = io::from_f32(activate<ACT>(x, y));
+                }
+                u32x2_t w;
+                w[0] = o[0] | (o[1] << 16);
+                w[1] = o[2] | (o[3] << 16);
+                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's 128x128
+                *(FL_LDS u32x2_t *)(wbuf + r * EPI_ROW + c * 2) = w;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
+        asm volatile("" ::: "memory");
+        const int cchunk = lane & 15;  // 16-byte chunk of the row
+        const int ccol = wn * 128 + cchunk * 8;
+        const int cvalid = a.N - n0 - ccol;
+#pragma unroll 8
+        for (int rr = 0; rr < 32; ++rr) {
+            const int r = rr * 4 + (lane >> 4);
+            const u32x4_t v = *(const FL_LDS u32x4_t *)(wbuf + r * EPI_ROW + cchunk * 16);
+            const int row = wm * 128 + r;
+            const bool row_ok = m0 + row < a.M;
+            const uint32_t off = (uint32_t)(row * a.N + ccol) * 2;
+            if (cvalid >= 8) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v), rO, row_ok ? off : kOob, 0, 0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+                    store_elem<2>(h, rO, (row_ok && e < cvalid) ? off + e * 2 : kOob);
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -407,7 +503,7 @@ struct Dma16 {
             wait_vm<0>();
             __syncthreads();
         }
-        base::epilogue(a, m0, n0, wm, wn, lane, acc);
+        epilogue_lds(a, m0, n0, wave, wm, wn, lane, acc, (FL_LDS char *)smem);
         if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
     }
 };
@@ -539,7 +635,7 @@ struct Stg16 : Dma16<DT, ACT, 64> {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        D::base::epilogue(a, m0, n0, wm, wn, lane, acc);
+        D::epilogue_lds(a, m0, n0, wave, wm, wn, lane, acc, lds);
         if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
     }
 
@@ -563,7 +659,7 @@ struct Stg16 : Dma16<DT, ACT, 64> {
 template <int DT, int ACT>
 __global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArgs a) {
     using T = Stg16<DT, ACT>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * T::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[(2 * T::BUF_BYTES > T::D::EPI_BYTES) ? 2 * T::BUF_BYTES : T::D::EPI_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     if (!a.persistent) {
         const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
@@ -582,7 +678,7 @@ __global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArg
 template <int DT, int ACT, int BK>
 __global__ void __launch_bounds__(kThreads, 1) fused_linear_dma16_kernel(GemmArgs a) {
     using T = Dma16<DT, ACT, BK>;
-    __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     if (!a.persistent) {
         const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
