@@ -69,24 +69,31 @@ __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t voffset, uint3
 }
 #pragma clang diagnostic pop
 
-template <int DT, int ACT, int BK_>
+template <int DT, int ACT, int BK_, int BN_ = 256>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
-    static constexpr int BM = 256, BN = 256, BK = BK_;
+    static constexpr int BM = 256, BN = BN_, BK = BK_;
     static_assert(BK == 32 || BK == 64, "stage depth");
-    static constexpr int NBUF = 128 / BK;            // 128 KB of LDS in the ring
-    static constexpr int KK = BK / 16;               // 16-MFMA blocks per stage
+    static_assert(BN == 256 || BN == 128, "tile width");
+    static constexpr int WN = BN / 2;                // wave tile: 128 x WN (waves 2 x 2)
+    static constexpr int NI = WN / 32;               // 32-wide MFMA blocks per wave along N
+    static constexpr int KK = BK / 16;               // MFMA blocks (k16) per stage
     static constexpr int CA = BK / 8;                // 16-byte chunks per A row
+    static constexpr int CB = BN / 8;                // 16-byte chunks per B row
     static constexpr int A_BYTES = BM * BK * 2;      // rows of BK*2 bytes
-    static constexpr int B_BYTES = BK * BN * 2;      // rows of 512 bytes (32 chunks)
+    static constexpr int B_BYTES = BK * BN * 2;      // rows of BN*2 bytes
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
+    static constexpr int NBUF = (BN == 256 ? 131072 : 147456) / BUF_BYTES;  // stages in the LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
+    static constexpr int B_ROWS_PER_COPY = 64 / CB;  // B rows per 1 KB copy
     static constexpr int NA = CA;                    // A copies per wave per stage
-    static constexpr int NB = BK / 8;                // B copies per wave per stage (2 rows each)
+    static constexpr int NB = BK / B_ROWS_PER_COPY / 4;  // B copies per wave per stage
     static constexpr int DMA_PER_WAVE = NA + NB;
+    static constexpr int SLOTS = 4 * NI;             // MFMAs per block
+    static constexpr int READS = 4 + 2 * NI;         // operand reads per block
     static_assert(NA * 4 * A_ROWS_PER_COPY == BM, "A copies cover the tile");
-    static_assert(NB * 4 * 2 == BK, "B copies cover the stage");
-    static_assert(DMA_PER_WAVE <= 16, "copies fit the MFMA slots of one block");
+    static_assert(NB * 4 * B_ROWS_PER_COPY == BK, "B copies cover the stage");
+    static_assert(NBUF >= 2, "double buffering at least");
 
     // A swizzle: chunk c of row r sits at c ^ fa(r).  16-byte operand reads
     // of 8 consecutive rows (8 lanes per cycle) and of 16 consecutive rows
@@ -97,9 +104,10 @@ struct Dma16 {
         else
             return ((r >> 1) ^ ((r & 1) << 2)) & 7;
     }
-    // B swizzle: chunk c (0..31) of k-row r sits at c ^ fb(r), fb in {0,6,12,10}
-    // by r % 4; conflict-free for the transposed 8-byte reads (4 rows x 2 or
-    // 4 chunks per 16 or 32 lanes).
+    // B swizzle: chunk c of k-row r sits at c ^ fb(r), fb in {0,6,12,10} by
+    // r % 4 (rows are 256 or 512 bytes, a multiple of the bank width);
+    // conflict-free for the transposed 8-byte reads (4 rows x 2 or 4 chunks
+    // per 16 or 32 lanes).
     __device__ __forceinline__ static int fb(int r) { return (0xAC60 >> (4 * (r & 3))) & 0xF; }
 
     // Per-lane copy offsets and operand-read addresses, fixed for a tile.
@@ -109,17 +117,18 @@ struct Dma16 {
     // past N) uses kOob so the hardware range check writes zeros; rows past
     // M are beyond num_records of A's descriptor.  Copy i of a wave covers
     // A rows A_ROWS_PER_COPY*(wave*NA + i) + lane/CA and B k-rows
-    // 2*(wave*NB + i) + lane/32; the swizzle of those rows repeats with period
-    // 2 in i, so two offsets per operand plus a stride describe all copies.
+    // B_ROWS_PER_COPY*(wave*NB + i) + lane/CB; the swizzle of those rows
+    // repeats with period 2 in i (or 1), so two offsets per operand plus a
+    // stride describe all copies.
     struct Lane {
         i32x4_t rA, rB;
         uint32_t a_off[2];  // byte offset (k0 = 0) of copies i = 0, 1; +i/2 * a_step
         int a_k[2];         // K index within the stage of those chunks
         uint32_t b_off[2];  // same for B (kOob when the columns are past N); +i/2 * b_step
-        int b_k0;           // K row within the stage of copy 0 (copy i: + 2i)
+        int b_k0;           // K row within the stage of copy 0 (copy i: + B_ROWS_PER_COPY*i)
         uint32_t a_step, b_step;
         int a_frag[KK];     // LDS byte address of A operand reads per kk (mi adds 32 rows)
-        int b_frag[4];      // LDS byte address of B operand reads per ni (kk adds 16 rows, h 4 rows)
+        int b_frag[NI];     // LDS byte address of B operand reads per ni (kk adds 16 rows, h 4 rows)
     };
 
     __device__ __forceinline__ static void setup(const GemmArgs &a, int m0, int n0, int wave, int lane, int wm,
@@ -133,13 +142,13 @@ struct Dma16 {
             const int ca = (lane % CA) ^ fa(ra);
             L.a_off[i] = (uint32_t)(ra * a.K + ca * 8) * 2;
             L.a_k[i] = ca * 8;
-            const int rb = 2 * (wave * NB + i) + (lane >> 5);
-            const int cb = (lane & 31) ^ fb(rb);
+            const int rb = B_ROWS_PER_COPY * (wave * NB + i) + lane / CB;
+            const int cb = (lane % CB) ^ fb(rb);
             L.b_off[i] = (n0 + cb * 8 < a.N) ? (uint32_t)(rb * a.N + cb * 8) * 2 : kOob;
         }
-        L.b_k0 = 2 * wave * NB + (lane >> 5);
+        L.b_k0 = B_ROWS_PER_COPY * wave * NB + lane / CB;
         L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * 2;
-        L.b_step = (uint32_t)(4 * a.N) * 2;
+        L.b_step = (uint32_t)(2 * B_ROWS_PER_COPY * a.N) * 2;
         const int lrow = lane & 31, lg = lane >> 5;
         const int r = wm * 128 + lrow;
 #pragma unroll
@@ -147,9 +156,9 @@ struct Dma16 {
         const int g16 = lane >> 4, i16 = lane & 15;
         const int rk = (g16 >> 1) * 8 + (i16 >> 2);  // k-row for kk = 0, h = 0
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int n = wn * 128 + ni * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-            L.b_frag[ni] = A_BYTES + rk * 512 + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
+        for (int ni = 0; ni < NI; ++ni) {
+            const int n = wn * WN + ni * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+            L.b_frag[ni] = A_BYTES + rk * (BN * 2) + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
         }
     }
 
@@ -182,7 +191,7 @@ struct Dma16 {
         } else {
             constexpr int i = I - NA;
             const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
-            const bool ok = (L.b_k0 + 2 * i < s.kleft) && (L.b_off[i & 1] != kOob);
+            const bool ok = (L.b_k0 + B_ROWS_PER_COPY * i < s.kleft) && (L.b_off[i & 1] != kOob);
             lds_copy16(L.rB, ok ? off : kOob, s.sob, s.bdst + i * 1024);
         }
     }
@@ -235,8 +244,8 @@ struct Dma16 {
         if (a.N & 7) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                const int rb = L.b_k0 + 2 * i;  // K row within the stage
-                const int cb = (lane & 31) ^ fb(rb);
+                const int rb = L.b_k0 + B_ROWS_PER_COPY * i;  // K row within the stage
+                const int cb = (lane % CB) ^ fb(rb);
                 const int col = n0 + cb * 8;
                 if (rb == kleft - 1 && col <= a.N - 1 && a.N - 1 < col + 8) {
                     const int e = a.N - 1 - col;
@@ -250,37 +259,38 @@ struct Dma16 {
     }
 
     struct Frags {
-        u32x4_t a[4];     // A operand per mi
-        s16x4_t b[4][2];  // B operand per ni, two halves of 4 k values
+        u32x4_t a[4];      // A operand per mi
+        s16x4_t b[NI][2];  // B operand per ni, two halves of 4 k values
     };
 
-    // Operand read number P of the 12 that make up one kk block, in the order
-    // the MFMAs of a block consume them: a0, b0 (2 halves), b1, b2, b3, a1..a3.
+    // Operand read number P of the READS that make up one kk block, in the
+    // order the MFMAs of a block consume them: a0, b0 (2 halves) .. b(NI-1),
+    // a1..a3.
     template <int P>
     __device__ __forceinline__ static void read_piece(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
         if constexpr (P == 0) {
             f.a[0] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk]);
-        } else if constexpr (P <= 8) {
+        } else if constexpr (P <= 2 * NI) {
             constexpr int ni = (P - 1) / 2, h = (P - 1) % 2;
-            f.b[ni][h] =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 8192 + h * 2048));
+            f.b[ni][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 16 * (BN * 2) + h * 4 * (BN * 2)));
         } else {
-            constexpr int mi = P - 8;
+            constexpr int mi = P - 2 * NI;
             f.a[mi] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk] + mi * 32 * BK * 2);
         }
     }
 
     template <int P = 0>
     __device__ __forceinline__ static void read_all(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
-        if constexpr (P < 12) {
+        if constexpr (P < READS) {
             read_piece<P>(L, buf, kk, f);
             read_all<P + 1>(L, buf, kk, f);
         }
     }
 
     template <int I>
-    __device__ __forceinline__ static void mma_one(const Frags &f, f32x16_t (&acc)[4][4]) {
-        constexpr int mi = I / 4, ni = I % 4;
+    __device__ __forceinline__ static void mma_one(const Frags &f, f32x16_t (&acc)[4][NI]) {
+        constexpr int mi = I / NI, ni = I % NI;
         const s16x8_t bv = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
         if constexpr (DT == FL_F16)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bv),
@@ -292,18 +302,29 @@ struct Dma16 {
                                                                   0, 0, 0);
     }
 
-    // One block: the 16 MFMAs on `use`, with the 12 operand reads of block
-    // kk_next of buffer `src` (into `fill`) slotted after MFMAs 4..15 and,
-    // when COPY, the copies of a look-ahead stage after MFMAs
-    // 0..DMA_PER_WAVE-1.  Without copies the reads follow MFMAs 0..11.
+    // Copies [C0, C1) of a look-ahead stage.
+    template <int C0, int C1>
+    __device__ __forceinline__ static void copy_range(const Lane &L, const Stage &s) {
+        if constexpr (C0 < C1) {
+            copy_one<C0>(L, s);
+            copy_range<C0 + 1, C1>(L, s);
+        }
+    }
+
+    // One block: the SLOTS MFMAs on `use`, with the READS operand reads of
+    // block kk_next of buffer `src` (into `fill`) in the last READS slots
+    // and, when COPY, the DMA_PER_WAVE copies of a look-ahead stage spread
+    // over all slots.  Without copies the reads follow the first MFMAs.
     template <int I, bool COPY>
     __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next, const Stage &s,
-                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][4]) {
-        if constexpr (I < 16) {
+                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][NI]) {
+        if constexpr (I < SLOTS) {
             mma_one<I>(use, acc);
-            if constexpr (COPY && I < DMA_PER_WAVE) copy_one<I>(L, s);
-            constexpr int R = COPY ? I - 4 : I;
-            if constexpr (R >= 0 && R < 12) read_piece<R>(L, src, kk_next, fill);
+            if constexpr (COPY)
+                copy_range<(I * DMA_PER_WAVE + SLOTS - 1) / SLOTS, ((I + 1) * DMA_PER_WAVE + SLOTS - 1) / SLOTS>(L,
+                                                                                                                 s);
+            constexpr int R = COPY ? I - (SLOTS - READS) : I;
+            if constexpr (R >= 0 && R < READS) read_piece<R>(L, src, kk_next, fill);
             __builtin_amdgcn_sched_barrier(0);
             block<I + 1, COPY>(L, src, kk_next, s, use, fill, acc);
         }
@@ -329,7 +350,7 @@ struct Dma16 {
     template <int B, int J = 0>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                  uint32_t lds_addr, int m0, int n0, int kt, int wave, Frags (&f)[2],
-                                                 f32x16_t (&acc)[4][4]) {
+                                                 f32x16_t (&acc)[4][NI]) {
         if constexpr (J < KK - 1) {
             const Stage none{};
             block<0, false>(L, lds + B * BUF_BYTES, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
@@ -348,7 +369,7 @@ struct Dma16 {
     template <int B>
     __device__ __forceinline__ static void stage_group(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                        uint32_t lds_addr, int m0, int n0, int kt, int wave,
-                                                       Frags (&f)[2], f32x16_t (&acc)[4][4]) {
+                                                       Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
         if constexpr (B < NBUF) {
             stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
             stage_group<B + 1>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
@@ -359,7 +380,7 @@ struct Dma16 {
     template <int B>
     __device__ __forceinline__ static void stage_tail(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                       uint32_t lds_addr, int m0, int n0, int kt, int nk, int wave,
-                                                      Frags (&f)[2], f32x16_t (&acc)[4][4]) {
+                                                      Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
         if constexpr (B < NBUF - 1) {
             if (kt + B < nk) {
                 stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
@@ -376,12 +397,13 @@ struct Dma16 {
     // write instruction touches fall in different banks).  Phase 2: each
     // lane reads 16 bytes of a row back and stores them, so a store
     // instruction writes 4 whole rows of 256 bytes (full 128-byte lines).
-    static constexpr int EPI_ROW = 256 + 16;
+    static constexpr int EPI_ROW = WN * 2 + 16;
     static constexpr int EPI_WAVE = 128 * EPI_ROW;
     static constexpr int EPI_BYTES = 4 * EPI_WAVE;
+    static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
 
     __device__ __forceinline__ static void epilogue_lds(const GemmArgs &a, int m0, int n0, int wave, int wm, int wn,
-                                                        int lane, const f32x16_t (&acc)[4][4], FL_LDS char *lds) {
+                                                        int lane, const f32x16_t (&acc)[4][NI], FL_LDS char *lds) {
         using io = Io<DT>;
         using quad_t = u32x2_t;
         const size_t o_org = (size_t)m0 * a.N + n0;
@@ -394,15 +416,15 @@ struct Dma16 {
                       a.bias ? (size_t)(a.N - n0) * 2 : 0);
         FL_LDS char *wbuf = lds + wave * EPI_WAVE;
         const int lrow = lane & 31, lg = lane >> 5;
-        int col[16], valid[16];
+        int col[NG], valid[NG];
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            col[g] = wn * 128 + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
+        for (int g = 0; g < NG; ++g) {
+            col[g] = wn * WN + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
             valid[g] = a.N - n0 - col[g];
         }
-        quad_t bq[16];
+        quad_t bq[NG];
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
+        for (int g = 0; g < NG; ++g) {
             bq[g] = quad_t{};
             if (a.bias) bq[g] = base::load4(rBias, valid[g] > 0 ? (uint32_t)col[g] * 2 : kOob, valid[g]);
         }
@@ -410,21 +432,21 @@ struct Dma16 {
             const int row = wm * 128 + mi * 32 + lrow;
             return (m0 + row < a.M && valid[g] > 0) ? (uint32_t)(row * a.N + col[g]) * 2 : kOob;
         };
-        quad_t yq[2][16];
+        quad_t yq[2][NG];
         if constexpr (ACT == FL_ACT_GLU) {
 #pragma unroll
-            for (int g = 0; g < 16; ++g) yq[0][g] = base::load4(rY, yoff(0, g), valid[g]);
+            for (int g = 0; g < NG; ++g) yq[0][g] = base::load4(rY, yoff(0, g), valid[g]);
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             if constexpr (ACT == FL_ACT_GLU) {
                 if (mi + 1 < 4) {
 #pragma unroll
-                    for (int g = 0; g < 16; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
+                    for (int g = 0; g < NG; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
                 }
             }
 #pragma unroll
-            for (int g = 0; g < 16; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 const int ni = g >> 2, q = g & 3;
                 uint32_t o[4];
 #pragma unroll
@@ -442,12 +464,14 @@ struct Dma16 {
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
         asm volatile("" ::: "memory");
-        const int cchunk = lane & 15;  // 16-byte chunk of the row
-        const int ccol = wn * 128 + cchunk * 8;
+        constexpr int CPR = WN / 8;    // 16-byte chunks per row of the wave tile
+        constexpr int RPP = 64 / CPR;  // rows per store instruction
+        const int cchunk = lane % CPR;
+        const int ccol = wn * WN + cchunk * 8;
         const int cvalid = a.N - n0 - ccol;
 #pragma unroll 8
-        for (int rr = 0; rr < 32; ++rr) {
-            const int r = rr * 4 + (lane >> 4);
+        for (int rr = 0; rr < 128 / RPP; ++rr) {
+            const int r = rr * RPP + lane / CPR;
             const u32x4_t v = *(const FL_LDS u32x4_t *)(wbuf + r * EPI_ROW + cchunk * 16);
             const int row = wm * 128 + r;
             const bool row_ok = m0 + row < a.M;
@@ -474,11 +498,11 @@ struct Dma16 {
         const FL_LDS char *lds = (const FL_LDS char *)smem;
         const uint32_t lds_addr = (uint32_t)(uintptr_t)(FL_LDS void *)smem;
 
-        f32x16_t acc[4][4];
+        f32x16_t acc[4][NI];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
@@ -519,11 +543,12 @@ struct Dma16 {
 // during block 2 of stage kt+1, before the barrier that publishes them.
 template <int DT, int ACT>
 struct Stg16 : Dma16<DT, ACT, 64> {
-    using D = Dma16<DT, ACT, 64>;
+    using D = Dma16<DT, ACT, 64, 256>;
     using typename D::Frags;
     using typename D::Lane;
     using typename D::Stage;
     static constexpr int NA = D::NA, NB = D::NB, NC = D::DMA_PER_WAVE, KK = D::KK, BUF_BYTES = D::BUF_BYTES;
+    static constexpr int NI = D::NI;
     static constexpr int A_BYTES = D::A_BYTES;
 
     struct Regs {
@@ -560,7 +585,7 @@ struct Stg16 : Dma16<DT, ACT, 64> {
     __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next,
                                                  const __amdgpu_buffer_rsrc_t &rA, const __amdgpu_buffer_rsrc_t &rB,
                                                  const Stage &s, FL_LDS char *wbuf, int wave, int lane, Regs &r,
-                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][4]) {
+                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][NI]) {
         if constexpr (I < 16) {
             D::template mma_one<I>(use, acc);
             if constexpr (MODE == 1) load_one<I>(L, rA, rB, s, r);
@@ -577,7 +602,7 @@ struct Stg16 : Dma16<DT, ACT, 64> {
     template <int B>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
                                                  const __amdgpu_buffer_rsrc_t &rB, FL_LDS char *lds, int kt,
-                                                 int wave, int lane, Regs &r, Frags (&f)[2], f32x16_t (&acc)[4][4]) {
+                                                 int wave, int lane, Regs &r, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
         FL_LDS char *cur = lds + B * BUF_BYTES;
         FL_LDS char *nxt = lds + (B ^ 1) * BUF_BYTES;
         const Stage none{};
@@ -675,9 +700,9 @@ __global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArg
     }
 }
 
-template <int DT, int ACT, int BK>
+template <int DT, int ACT, int BK, int BN>
 __global__ void __launch_bounds__(kThreads, 1) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK>;
+    using T = Dma16<DT, ACT, BK, BN>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     if (!a.persistent) {

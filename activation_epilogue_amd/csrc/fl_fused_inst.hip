@@ -17,10 +17,20 @@ void launch(const GemmArgs &a, int grid, hipStream_t s) {
 
 }  // namespace
 
-template <int DT, int ACT, int BK>
+template <int DT, int ACT, int BK, int BN>
 void launch_dma(const GemmArgs &a, int grid, hipStream_t s) {
     if constexpr (DT != FL_F32)
-        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+template <int DT, int BK, int BN>
+fused_launcher pick_dma(int act) {
+    switch (act) {
+    case FL_ACT_NONE: return launch_dma<DT, FL_ACT_NONE, BK, BN>;
+    case FL_ACT_RELU: return launch_dma<DT, FL_ACT_RELU, BK, BN>;
+    case FL_ACT_GELU_TANH: return launch_dma<DT, FL_ACT_GELU_TANH, BK, BN>;
+    default: return launch_dma<DT, FL_ACT_GLU, BK, BN>;
+    }
 }
 
 template <int DT, int ACT>
@@ -32,25 +42,19 @@ void launch_stg(const GemmArgs &a, int grid, hipStream_t s) {
 template <>
 fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant) {
     constexpr int DT = FL_INST_DTYPE;
-    // fp16/bf16 with 16-byte aligned operands use the direct-to-LDS kernel
-    // (64-deep K stages, or 32-deep with variant 2) unless the register-staged
-    // one is requested (variant 1).
-    if (DT != FL_F32 && vec && variant == 3) {
-        switch (act) {
-        case FL_ACT_NONE: return launch_stg<DT, FL_ACT_NONE>;
-        case FL_ACT_RELU: return launch_stg<DT, FL_ACT_RELU>;
-        case FL_ACT_GELU_TANH: return launch_stg<DT, FL_ACT_GELU_TANH>;
-        default: return launch_stg<DT, FL_ACT_GLU>;
-        }
-    }
-    if (DT != FL_F32 && vec && variant != 1) {
-        const bool bk32 = variant == 2;
-        switch (act) {
-        case FL_ACT_NONE: return bk32 ? launch_dma<DT, FL_ACT_NONE, 32> : launch_dma<DT, FL_ACT_NONE, 64>;
-        case FL_ACT_RELU: return bk32 ? launch_dma<DT, FL_ACT_RELU, 32> : launch_dma<DT, FL_ACT_RELU, 64>;
-        case FL_ACT_GELU_TANH:
-            return bk32 ? launch_dma<DT, FL_ACT_GELU_TANH, 32> : launch_dma<DT, FL_ACT_GELU_TANH, 64>;
-        default: return bk32 ? launch_dma<DT, FL_ACT_GLU, 32> : launch_dma<DT, FL_ACT_GLU, 64>;
+    if constexpr (DT != FL_F32) {
+        switch (variant) {
+        case kDirect64x256: return pick_dma<DT, 64, 256>(act);
+        case kDirect32x256: return pick_dma<DT, 32, 256>(act);
+        case kDirect64x128: return pick_dma<DT, 64, 128>(act);
+        case kStaged64x256:
+            switch (act) {
+            case FL_ACT_NONE: return launch_stg<DT, FL_ACT_NONE>;
+            case FL_ACT_RELU: return launch_stg<DT, FL_ACT_RELU>;
+            case FL_ACT_GELU_TANH: return launch_stg<DT, FL_ACT_GELU_TANH>;
+            default: return launch_stg<DT, FL_ACT_GLU>;
+            }
+        default: break;
         }
     }
     switch (act) {

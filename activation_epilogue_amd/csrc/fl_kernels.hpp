@@ -80,12 +80,12 @@ template <> struct Io<FL_BF16> {
 
 // ------------------------------------------------------------- epilogue ops
 
-// The activation applied to x = acc + bias (y is the gate operand).
+// The activation applied to x = acc + bias (y is the gate operand), in fp32.
 // GELU(tanh): with tanh(u) = 2 sigmoid(2u) - 1 the tanh form becomes
 // x * sigmoid(2u) = x / (1 + 2^(-2u log2 e)), u = sqrt(2/pi) (x + 0.044715 x^3);
 // one v_exp_f32 and one v_rcp_f32.  x -> -inf gives x * 0, x -> +inf gives x.
 template <int ACT>
-__device__ __forceinline__ float activate(float x, float y) {
+__device__ __forceinline__ float activate_math(float x, float y) {
     if constexpr (ACT == FL_ACT_RELU) {
         return __builtin_fmaxf(x, 0.0f);  // branchless clamp, float literal
     } else if constexpr (ACT == FL_ACT_GELU_TANH) {
@@ -98,6 +98,18 @@ __device__ __forceinline__ float activate(float x, float y) {
     } else {
         return x;
     }
+}
+
+// The epilogue value, held as an fp32 register before any cast.  Without the
+// empty asm the compiler may fold a following cast to a 16-bit type into the
+// last fma (v_fma_mix with a 16-bit result rounds once where fp32 math and a
+// cast round twice), differently from one kernel to the next; with it every
+// kernel rounds to fp32 first and then casts once.
+template <int ACT>
+__device__ __forceinline__ float activate(float x, float y) {
+    float r = activate_math<ACT>(x, y);
+    asm("" : "+v"(r));
+    return r;
 }
 
 // ------------------------------------------------------------- tile order
@@ -577,10 +589,17 @@ __global__ void __launch_bounds__(kThreads) activation_kernel(const void *Xv, co
 
 typedef void (*fused_launcher)(const GemmArgs &, int grid, hipStream_t);
 
-// Returns the launcher of the fused kernel for (DT, act): the direct-to-LDS
-// fp16/bf16 kernel when `vec` and variant != 1 (variant 2: 32-deep K stages),
-// else the register-staged kernel with the vector or element load path.  Defined in the per-dtype
-// instantiation unit.
+// Kernel variants (selected on the host, see fused_linear.hip).
+enum Variant {
+    kRegStaged = 1,     // FusedTile: register-staged loads, 256x256, any dtype; `vec` picks the load path
+    kDirect64x256 = 0,  // Dma16 BK 64, 256x256 (fp16/bf16)
+    kDirect32x256 = 2,  // Dma16 BK 32, 256x256
+    kStaged64x256 = 3,  // Stg16: the Dma16 pipeline staged through VGPRs (aligned rows)
+    kDirect64x128 = 4,  // Dma16 BK 64, 256x128
+};
+
+// Returns the launcher of the fused kernel for (DT, act, variant); defined in
+// the per-dtype instantiation unit.
 template <int DT>
 fused_launcher pick_fused_for(int act, bool vec, int variant);
 

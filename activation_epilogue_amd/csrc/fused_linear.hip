@@ -70,15 +70,41 @@ fl::fused_launcher pick_fused(int dtype, int act, bool vec, int variant) {
 
 struct TileShape {
     int bm, bn;
+    int variant;  // fl::Variant
 };
 
-fl_status tile_shape(const fl_options *opt, TileShape &t) {
+// Kernel and tile for a problem.  tile_cfg: 0 automatic, 1 256x256, 2 256x128
+// (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
+// (fp16/bf16), 5 the direct pipeline staged through VGPRs (fp16/bf16, needs
+// aligned rows; checked at launch).  fp32 always runs the register-staged
+// kernel.  Automatic fp16/bf16 choice: the width (256 or 128) with the
+// smaller waves * relative tile time, a 256x128 tile taking 0.55 of a
+// 256x256 one; ties go to 256.
+fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg >= 0 && cfg <= 5 && cfg != 2) {
-        t = {256, 256};
+    if (cfg < 0 || cfg > 5) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (dtype == FL_F32) {
+        if (cfg == 2) return fail(FL_ERR_UNSUPPORTED, "tile_cfg 2 (256x128) is fp16/bf16 only");
+        t = {256, 256, fl::kRegStaged};
         return FL_OK;
     }
-    return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    switch (cfg) {
+    case 1: t = {256, 256, fl::kDirect64x256}; return FL_OK;
+    case 2: t = {256, 128, fl::kDirect64x128}; return FL_OK;
+    case 3: t = {256, 256, fl::kRegStaged}; return FL_OK;
+    case 4: t = {256, 256, fl::kDirect32x256}; return FL_OK;
+    case 5: t = {256, 256, fl::kStaged64x256}; return FL_OK;
+    default: break;
+    }
+    const int64_t cus = cu_count();
+    const int64_t tm = (M + 255) / 256;
+    const int64_t waves256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
+    const int64_t waves128 = (tm * ((N + 127) / 128) + cus - 1) / cus;
+    if (waves128 * 55 < waves256 * 100)
+        t = {256, 128, fl::kDirect64x128};
+    else
+        t = {256, 256, fl::kDirect64x256};
+    return FL_OK;
 }
 
 int grid_elementwise(int64_t work_items) {
@@ -118,7 +144,7 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
         if (opt->no_xcd_remap != 0 && opt->no_xcd_remap != 1)
             return fail(FL_ERR_INVALID_ARG, "no_xcd_remap must be 0 or 1");
         TileShape t;
-        s = tile_shape(opt, t);
+        s = tile_shape(dtype, M, N, opt, t);
         if (s != FL_OK) return s;
     }
     const size_t es = elem_size(dtype);
@@ -147,14 +173,14 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
                       int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
-    fl_status s = tile_shape(opt, t);
+    fl_status s = tile_shape(dtype, M, N, opt, t);
     if (s != FL_OK) return s;
     const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
     const int es = (int)elem_size(dtype);
     const int vec = 16 / es;
-    // fp16/bf16 take the direct-to-LDS kernel at any alignment (variant 0, 2);
-    // the register-staged kernel needs 16-byte aligned rows for its vector path.
+    // The direct-to-LDS kernels take any alignment; the register-staged
+    // kernels need 16-byte aligned rows for their vector path.
     const bool aligned_rows = (K % vec == 0) && (N % vec == 0) && aligned(A, 16) && aligned(B, 16) &&
                               aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16));
     fl::GemmArgs a;
@@ -178,13 +204,10 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
     }
-    // variant: 0 = default kernel for the dtype/path, 1 = register-staged,
-    // 2 = direct-to-LDS with 32-deep K stages, 3 = same pipeline staged through VGPRs
-    const int variant = !opt ? 0 : opt->tile_cfg == 3 ? 1 : opt->tile_cfg == 4 ? 2 : opt->tile_cfg == 5 ? 3 : 0;
-    const bool direct = dtype != FL_F32 && (variant == 0 || variant == 2);
-    const bool use_vec = direct || aligned_rows;
-    if (variant == 3 && !aligned_rows) return fail(FL_ERR_UNSUPPORTED, "tile_cfg 5 needs 16-byte aligned rows");
-    pick_fused(dtype, act, use_vec, variant)(a, grid, static_cast<hipStream_t>(stream));
+    if (t.variant == fl::kStaged64x256 && !aligned_rows)
+        return fail(FL_ERR_UNSUPPORTED, "tile_cfg 5 needs 16-byte aligned rows");
+    const bool use_vec = t.variant != fl::kRegStaged || aligned_rows;
+    pick_fused(dtype, act, use_vec, t.variant)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
 }
 
@@ -316,7 +339,7 @@ fl_status fl_tile_grid(int64_t M, int64_t N, int64_t K, fl_dtype dtype, const fl
     fl_status s = check_dims(M, N, K);
     if (s != FL_OK) return s;
     TileShape t;
-    s = tile_shape(opt, t);
+    s = tile_shape(dtype, M, N, opt, t);
     if (s != FL_OK) return s;
     if (!block_m || !block_n || !tiles_m || !tiles_n) return fail(FL_ERR_INVALID_ARG, "NULL output pointer");
     *block_m = t.bm;

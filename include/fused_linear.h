@@ -88,12 +88,20 @@ typedef struct {
                            1 gives row-major tile order. */
     int32_t persistent; /* 0 = one workgroup per output tile; 1 = a grid sized
                            to the GPU whose workgroups loop over tiles. */
-    int32_t tile_cfg;   /* 0 = automatic (= 1); 1 = 256x256 tiles, for
-                           16-byte aligned fp16/bf16 direct-to-LDS copies
-                           with 64-deep K stages; 3 = 256x256 with
-                           register-staged loads (the fp32 and unaligned
-                           path) for every dtype; 4 = as 1 with 32-deep K
-                           stages.  Any other value is FL_ERR_UNSUPPORTED. */
+    int32_t tile_cfg;   /* Kernel and tile.  0 = automatic: fp32 runs the
+                           register-staged 256x256 kernel; fp16/bf16 run the
+                           direct-to-LDS kernel with 256x256 tiles, or 256x128
+                           when that takes fewer waves x relative tile time
+                           on this GPU's compute units.  1 = 256x256 direct
+                           (fp16/bf16; fp32 as 0); 2 = 256x128 direct
+                           (fp16/bf16 only); 3 = register-staged 256x256 for
+                           any dtype; 4 = 256x256 direct with 32-deep K
+                           stages; 5 = the direct pipeline with its copies
+                           staged through registers (fp16/bf16, K and N
+                           multiples of 8, 16-byte aligned pointers).  Every
+                           variant gives bit-identical results.  Any other
+                           value, or a variant the problem does not allow,
+                           is FL_ERR_UNSUPPORTED. */
     int32_t no_xcd_remap; /* 0 = place neighbouring tiles on one XCD; 1 = off */
     uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
                            counters (see fl_tile_grid); each output tile adds
@@ -119,8 +127,8 @@ fl_status fl_fused_linear(const void *A, const void *B, const void *bias,
 /* As fl_fused_linear, with explicit options (opt may be NULL = defaults).
  * Results are bitwise identical for every group_m, persistent and
  * no_xcd_remap setting: they change which workgroup computes a tile, never
- * the arithmetic of the tile.  tile_cfg changes the tile shape and may change
- * the fp32 rounding order inside the MFMA sums (within tolerance). */
+ * the arithmetic of the tile; every tile_cfg sums each output in the same
+ * order too, so results are bit-identical across all options. */
 fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias,
                              const void *Y, void *out, int64_t M, int64_t N,
                              int64_t K, fl_act act, fl_dtype dtype,
@@ -144,8 +152,10 @@ fl_status fl_bias_add(void *X, const void *bias, int64_t M, int64_t N,
 fl_status fl_activation(const void *X, const void *Y, void *out, int64_t M,
                         int64_t N, fl_act act, fl_dtype dtype, void *stream);
 
-/* Tile grid fl_fused_linear_ex would use for this problem (no GPU call).
- * Writes the tile shape and the number of tiles along M and N. */
+/* Tile grid fl_fused_linear_ex would use for this problem.  Writes the tile
+ * shape and the number of tiles along M and N.  The automatic choice reads
+ * the current device's compute-unit count once (256 when no device is
+ * available); no other HIP call is made. */
 fl_status fl_tile_grid(int64_t M, int64_t N, int64_t K, fl_dtype dtype,
                        const fl_options *opt, int32_t *block_m,
                        int32_t *block_n, int32_t *tiles_m, int32_t *tiles_n);

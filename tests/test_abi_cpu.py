@@ -101,10 +101,20 @@ def test_unfused_entry_points_reject_bad_arguments(lib):
 
 
 def test_tile_grid(lib):
+    # automatic choice: 256-wide tiles unless 128-wide ones need fewer
+    # "waves x relative tile time" on 256 compute units
     assert fl.tile_grid(4096, 4096, 4096, F16) == (256, 256, 16, 16)
     assert fl.tile_grid(4097, 3071, 1537, BF16) == (256, 256, 17, 12)
-    assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 256, 4, 85)
+    assert fl.tile_grid(8192, 14336, 4096, BF16) == (256, 256, 32, 56)
+    assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 128, 4, 169)
+    assert fl.tile_grid(127, 129, 96, F16) == (256, 128, 1, 2)
     assert fl.tile_grid(127, 129, 96, F32) == (256, 256, 1, 1)
+    assert fl.tile_grid(1024, 21568, 4096, F16, tile_cfg=1) == (256, 256, 4, 85)
+    assert fl.tile_grid(4096, 4096, 4096, BF16, tile_cfg=2) == (256, 128, 16, 32)
+    with pytest.raises(fl.FusedLinearError):
+        fl.tile_grid(64, 64, 64, F32, tile_cfg=2)
+    with pytest.raises(fl.FusedLinearError):
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=6)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):

@@ -257,3 +257,33 @@ def test_y_may_alias_out():
     torch.cuda.synchronize()
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act="glu", dtype="f16")
     _assert_close(to_host(Y, "f16"), ref, "f16", "Y == out")
+
+
+# ------------------------------------------------------------ kernel variants
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "glu"])
+@pytest.mark.parametrize("shape", [(127, 129, 96), (300, 520, 1000), (513, 264, 72), (1024, 2048, 1024)])
+def test_kernel_variants_bit_identical_and_within_tolerance(dtype, act, shape):
+    """Every fp16/bf16 kernel variant (256x256 or 256x128 tiles, 64- or
+    32-deep K stages, direct or register-staged copies) sums each output in
+    the same k order, so results are bit-identical; each also passes the
+    oracle check."""
+    M, N, K = shape
+    d = synth.draw(M, N, K, dtype, act, seed=21)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    outs = {}
+    cfgs = [0, 1, 2, 3, 4] + ([5] if (K % 8 == 0 and N % 8 == 0) else [])
+    for cfg in cfgs:
+        say("variant", cfg, dtype, act, shape)
+        outs[cfg] = _run_fused(d, act, dtype, tile_cfg=cfg)
+        _assert_close(outs[cfg], ref, dtype, f"tile_cfg {cfg}")
+    base = outs[1].view(np.uint8)
+    for cfg, o in outs.items():
+        assert np.array_equal(o.view(np.uint8), base), f"tile_cfg {cfg} differs from tile_cfg 1"
+
+
+def test_tile_cfg_5_rejects_unaligned_rows():
+    d = synth.draw(64, 63, 64, "f16", "relu", seed=1)
+    with pytest.raises(fl.FusedLinearError):
+        _run_fused(d, "relu", "f16", tile_cfg=5)
