@@ -67,6 +67,22 @@ __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t voffset, uint3
                  "s"(soffset), "s"(lds_addr)
                  : "memory", "m0");
 }
+// One 16-bit load and its wait in a single asm block.  A load into a VGPR
+// that the compiler sees, issued on a branch inside the K loop, makes its
+// wait-count pass assume the register may still be pending on every later
+// pass through the loop, and it then drains all outstanding copies
+// (vmcnt(0)) before the next LDS read into that register: the look-ahead
+// copies would land in lock step with the MFMAs.  Hidden here, the only
+// vector-memory operations the compiler tracks in the loop are none, and
+// every wait on the copies is an explicit one.
+__device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset) {
+    uint32_t v;
+    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(v)
+                 : "v"(voffset), "s"(rsrc)
+                 : "memory");
+    return v & 0xffffu;
+}
 #pragma clang diagnostic pop
 
 template <int DT, int ACT, int BK_, int BN_ = 256>
@@ -217,8 +233,8 @@ struct Dma16 {
     __device__ __forceinline__ static void fix_k_tail(const GemmArgs &a, const Lane &L, int m0, int n0, int kt,
                                                       int wave, int lane, FL_LDS char *buf) {
         const int k0 = kt * BK, kleft = a.K - k0;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, (size_t)a.M * a.K * 2);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, (size_t)a.K * a.N * 2);
+        const i32x4_t rA = sgpr_rsrc(a.A, (size_t)a.M * a.K * 2);
+        const i32x4_t rB = sgpr_rsrc(a.B, (size_t)a.K * a.N * 2);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int kb = L.a_k[i & 1];
@@ -234,8 +250,7 @@ struct Dma16 {
                 const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
                 if (row == a.M - 1) {
                     const uint32_t e = (uint32_t)(valid - 1);
-                    const uint32_t x =
-                        (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rA, (uint32_t)((size_t)a.M * a.K - 1) * 2, 0, 0);
+                    const uint32_t x = load_u16_now(rA, (uint32_t)((size_t)a.M * a.K - 1) * 2);
                     v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
                 }
                 *(FL_LDS u32x4_t *)p = v;
@@ -251,8 +266,7 @@ struct Dma16 {
                     const int e = a.N - 1 - col;
                     FL_LDS uint16_t *q =
                         (FL_LDS uint16_t *)(buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16 + 2 * e);
-                    *q = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rB, (uint32_t)((size_t)a.K * a.N - 1) * 2, 0,
-                                                                         0);
+                    *q = (uint16_t)load_u16_now(rB, (uint32_t)((size_t)a.K * a.N - 1) * 2);
                 }
             }
         }
@@ -340,52 +354,33 @@ struct Dma16 {
         asm volatile("" ::: "memory");
     }
 
-    // Blocks J..KK-1 of stage kt, held in buffer B.  On entry the operands of
-    // block J are in f[J & 1].  Before the last block: wait until this
-    // wave's copies of stage kt+1 have landed (those of stages kt+2 ..
-    // kt+NBUF-1 stay in flight) and barrier, after which stage kt+1 is
-    // visible to every wave and buffer B has been read by all of them, so
-    // the last block refills it with stage kt+NBUF while reading stage
-    // kt+1's first operands.
-    template <int B, int J = 0>
+    // Blocks J..KK-1 of stage kt, held in LDS buffer `buf` (uniform, kept
+    // at run time so that one copy of the stage code serves every buffer and
+    // every stage count: no unrolled group, no separate tail).  On entry the
+    // operands of block J are in f[J & 1].  Before the last block: wait
+    // until this wave's copies of stage kt+1 have landed (those of stages
+    // kt+2 .. kt+NBUF-1 stay in flight) and barrier, after which stage kt+1
+    // is visible to every wave and buffer `buf` has been read by all of
+    // them, so the last block refills it with stage kt+NBUF while reading
+    // stage kt+1's first operands.
+    template <int J = 0>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                 uint32_t lds_addr, int m0, int n0, int kt, int wave, Frags (&f)[2],
-                                                 f32x16_t (&acc)[4][NI]) {
+                                                 uint32_t lds_addr, int m0, int n0, int kt, int nk, int buf,
+                                                 int wave, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
+        const FL_LDS char *cur = lds + buf * BUF_BYTES;
         if constexpr (J < KK - 1) {
             const Stage none{};
-            block<0, false>(L, lds + B * BUF_BYTES, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
-            stage<B, J + 1>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
+            block<0, false>(L, cur, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
+            stage<J + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, f, acc);
         } else {
+            const int nbuf = buf + 1 == NBUF ? 0 : buf + 1;
+            const FL_LDS char *nxt = lds + nbuf * BUF_BYTES;
             wait_vm<(NBUF - 2) * DMA_PER_WAVE>();
-            if (((a.K | a.N) & 7) && kt + 2 == (a.K + BK - 1) / BK)
-                fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63,
-                           (FL_LDS char *)lds + ((B + 1) % NBUF) * BUF_BYTES);
+            if (((a.K | a.N) & 7) && kt + 2 == nk)
+                fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
             __syncthreads();
-            const Stage s = stage_of(a, kt + NBUF, wave, lds_addr + B * BUF_BYTES);
-            block<0, true>(L, lds + ((B + 1) % NBUF) * BUF_BYTES, 0, s, f[J & 1], f[(J + 1) & 1], acc);
-        }
-    }
-
-    template <int B>
-    __device__ __forceinline__ static void stage_group(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                       uint32_t lds_addr, int m0, int n0, int kt, int wave,
-                                                       Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
-        if constexpr (B < NBUF) {
-            stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
-            stage_group<B + 1>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
-        }
-    }
-
-    // Remaining stages kt.. nk-1 (fewer than NBUF), buffers 0.. in order.
-    template <int B>
-    __device__ __forceinline__ static void stage_tail(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
-                                                      uint32_t lds_addr, int m0, int n0, int kt, int nk, int wave,
-                                                      Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
-        if constexpr (B < NBUF - 1) {
-            if (kt + B < nk) {
-                stage<B>(a, L, lds, lds_addr, m0, n0, kt + B, wave, f, acc);
-                stage_tail<B + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, wave, f, acc);
-            }
+            const Stage s = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
+            block<0, true>(L, nxt, 0, s, f[J & 1], f[(J + 1) & 1], acc);
         }
     }
 
@@ -517,11 +512,13 @@ struct Dma16 {
             __syncthreads();
             Frags f[2];
             read_all(L, lds, 0, f[0]);
-            int kt = 0;
-            // Whole groups of NBUF stages, no branch inside, so the buffer of
-            // every stage is a compile-time constant.
-            for (; kt + NBUF <= nk; kt += NBUF) stage_group<0>(a, L, lds, lds_addr, m0, n0, kt, wave, f, acc);
-            stage_tail<0>(a, L, lds, lds_addr, m0, n0, kt, nk, wave, f, acc);
+            static_assert(KK % 2 == 0, "operand double buffer f[] must line up across stages");
+            int buf = 0;
+#pragma unroll 1
+            for (int kt = 0; kt < nk; ++kt) {
+                stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, f, acc);
+                buf = buf + 1 == NBUF ? 0 : buf + 1;
+            }
             // The look-ahead copies (past the end of K) must land before this
             // workgroup's LDS is reused.
             wait_vm<0>();
@@ -704,18 +701,14 @@ template <int DT, int ACT, int BK, int BN>
 __global__ void __launch_bounds__(kThreads, 1) fused_linear_dma16_kernel(GemmArgs a) {
     using T = Dma16<DT, ACT, BK, BN>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
+    // One strided loop for both launch modes (one program per tile runs one
+    // iteration), so the tile body is inlined once.
     const int ntiles = a.tiles_m * a.tiles_n;
-    if (!a.persistent) {
-        const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int G = gridDim.x;
+    const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
+    for (int pid = slot; pid < ntiles; pid += G) {
         T::run_tile(a, pid, smem);
-    } else {
-        const int G = gridDim.x;
-        const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
-        for (int base = 0; base < ntiles; base += G) {
-            const int pid = base + slot;
-            if (pid < ntiles) T::run_tile(a, pid, smem);
-            __syncthreads();
-        }
+        __syncthreads();
     }
 }
 
