@@ -461,23 +461,39 @@ struct Dma16 {
         asm volatile("" ::: "memory");
         constexpr int CPR = WN / 8;    // 16-byte chunks per row of the wave tile
         constexpr int RPP = 64 / CPR;  // rows per store instruction
+        constexpr int BATCH = 8;       // LDS reads issued ahead of their stores
+        constexpr int PASSES = 128 / RPP;
+        static_assert(PASSES % BATCH == 0, "whole batches");
         const int cchunk = lane % CPR;
         const int ccol = wn * WN + cchunk * 8;
         const int cvalid = a.N - n0 - ccol;
-#pragma unroll 8
-        for (int rr = 0; rr < 128 / RPP; ++rr) {
-            const int r = rr * RPP + lane / CPR;
-            const u32x4_t v = *(const FL_LDS u32x4_t *)(wbuf + r * EPI_ROW + cchunk * 16);
-            const int row = wm * 128 + r;
-            const bool row_ok = m0 + row < a.M;
-            const uint32_t off = (uint32_t)(row * a.N + ccol) * 2;
-            if (cvalid >= 8) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v), rO, row_ok ? off : kOob, 0, 0);
-            } else {
+        const FL_LDS char *rbase = wbuf + (lane / CPR) * EPI_ROW + cchunk * 16;
+        auto out_off = [&](int rr) -> uint32_t {
+            const int row = wm * 128 + rr * RPP + lane / CPR;
+            return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * 2 : kOob;
+        };
+        if (cvalid >= 8) {
+            // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
+#pragma unroll 1
+            for (int rb = 0; rb < PASSES; rb += BATCH) {
+                u32x4_t v[BATCH];
+#pragma unroll
+                for (int j = 0; j < BATCH; ++j) v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
+#pragma unroll
+                for (int j = 0; j < BATCH; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j), 0,
+                                                           0);
+            }
+        } else {
+            // The chunk that holds column N-1 (and chunks past it): elements.
+#pragma unroll 1
+            for (int rr = 0; rr < PASSES; ++rr) {
+                const u32x4_t v = *(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW);
+                const uint32_t off = out_off(rr);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
-                    store_elem<2>(h, rO, (row_ok && e < cvalid) ? off + e * 2 : kOob);
+                    store_elem<2>(h, rO, (off != kOob && e < cvalid) ? off + e * 2 : kOob);
                 }
             }
         }
@@ -524,7 +540,12 @@ struct Dma16 {
             wait_vm<0>();
             __syncthreads();
         }
-        epilogue_lds(a, m0, n0, wave, wm, wn, lane, acc, (FL_LDS char *)smem);
+        // The epilogue's per-lane addresses derive from a copy of the lane
+        // index made here, so the compiler cannot compute them before the K
+        // loop and keep them (spilled) across it.
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        epilogue_lds(a, m0, n0, wave, wm, wn, lane_e, acc, (FL_LDS char *)smem);
         if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
     }
 };
