@@ -45,6 +45,10 @@ WORKLOADS = {w.name: w for w in [
     Workload("relu_bf16_4097x3071x1537", 4097, 3071, 1537, "bf16", "relu"),
     Workload("glu_f16_1024x21568x4096", 1024, 21568, 4096, "f16", "glu"),
     Workload("gelu_bf16_8192x14336x4096", 8192, 14336, 4096, "bf16", "gelu_tanh", bias_var=0.1),
+    # the gate at the TLX page's own shape and K sweep (its MI350X table)
+    Workload("glu_f16_1024x21568x256", 1024, 21568, 256, "f16", "glu"),
+    Workload("glu_f16_1024x21568x512", 1024, 21568, 512, "f16", "glu"),
+    Workload("glu_f16_1024x21568x1024", 1024, 21568, 1024, "f16", "glu"),
 ]}
 
 

@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
+    p.add_argument("--tile-cfg", type=int, default=0, help="fl_options.tile_cfg (0 = automatic)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -148,6 +149,12 @@ def main():
         opts["group_m"] = args.group_m
     if args.persistent:
         opts["persistent"] = 1
+    if args.tile_cfg:
+        opts["tile_cfg"] = args.tile_cfg
+    code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **opts)
+    kernel = ("fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else
+              "fused_linear_stg16_kernel" if args.tile_cfg == 5 else "fused_linear_dma16_kernel")
 
     def step():
         fl.fused_linear(A, B, bias, Y, act=w.act, out=out, **opts)
@@ -192,12 +199,12 @@ def main():
         "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s)" % (
             w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else ""),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "io_dtype": w.dtype,
-                   "accumulate": "f32", "tile": "256x256", "group_m": args.group_m or 4,
-                   "persistent": bool(args.persistent)},
+                   "accumulate": "f32", "tile": f"{bm}x{bn}", "tiles": tiles_m * tiles_n,
+                   "tile_cfg": args.tile_cfg, "group_m": args.group_m or 4, "persistent": bool(args.persistent)},
         "frac_of_peak": round(tflops / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "fused_linear_kernel", "avg_launch_ms": round(ms_event, 4),
+                     "kernel": kernel, "avg_launch_ms": round(ms_event, 4),
                      "algorithmic_bytes": alg_bytes},
     }
 
