@@ -85,13 +85,22 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 }
 #pragma clang diagnostic pop
 
-template <int DT, int ACT, int BK_, int BN_ = 256>
+// WAVES_N waves along N and 2 along M: 4 waves (one per SIMD, 128 x BN/2
+// each) or 8 waves (two per SIMD, 128 x BN/4 each; the two waves sharing a
+// SIMD own the same columns and cover each other's waits).  SPREAD: the
+// copies of a look-ahead stage are issued over that many blocks (the block
+// after the barrier that frees their buffer and the next SPREAD-1 blocks)
+// instead of all in one, so the address unit's queue does not fill up and
+// hold back the MFMAs behind them.
+template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr int BM = 256, BN = BN_, BK = BK_;
     static_assert(BK == 32 || BK == 64, "stage depth");
     static_assert(BN == 256 || BN == 128, "tile width");
-    static constexpr int WN = BN / 2;                // wave tile: 128 x WN (waves 2 x 2)
+    static_assert(WAVES_N == 2 || WAVES_N == 4, "wave grid");
+    static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
     static constexpr int NI = WN / 32;               // 32-wide MFMA blocks per wave along N
     static constexpr int KK = BK / 16;               // MFMA blocks (k16) per stage
     static constexpr int CA = BK / 8;                // 16-byte chunks per A row
@@ -102,13 +111,20 @@ struct Dma16 {
     static constexpr int NBUF = (BN == 256 ? 131072 : 147456) / BUF_BYTES;  // stages in the LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
     static constexpr int B_ROWS_PER_COPY = 64 / CB;  // B rows per 1 KB copy
-    static constexpr int NA = CA;                    // A copies per wave per stage
-    static constexpr int NB = BK / B_ROWS_PER_COPY / 4;  // B copies per wave per stage
+    static constexpr int NA = BM / (A_ROWS_PER_COPY * WAVES);  // A copies per wave per stage
+    static constexpr int NB = BK / (B_ROWS_PER_COPY * WAVES);  // B copies per wave per stage
     static constexpr int DMA_PER_WAVE = NA + NB;
     static constexpr int SLOTS = 4 * NI;             // MFMAs per block
     static constexpr int READS = 4 + 2 * NI;         // operand reads per block
-    static_assert(NA * 4 * A_ROWS_PER_COPY == BM, "A copies cover the tile");
-    static_assert(NB * 4 * B_ROWS_PER_COPY == BK, "B copies cover the stage");
+    static_assert(NA * WAVES * A_ROWS_PER_COPY == BM, "A copies cover the tile");
+    static_assert(NB * WAVES * B_ROWS_PER_COPY == BK, "B copies cover the stage");
+    // The swizzle of a copy's rows repeats with period 2 in the copy index
+    // (Lane below keeps two offsets and a stride), so each wave's first copy
+    // must have an even index: an even number of copies per wave.
+    static_assert(NA % 2 == 0 && NB % 2 == 0, "copies per wave");
+    static_assert(SPREAD >= 1 && SPREAD <= KK, "copies spread over the blocks of one stage at most");
+    // Copies [part_lo(p), part_lo(p+1)) of a stage form part p.
+    static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPREAD; }
     static_assert(NBUF >= 2, "double buffering at least");
 
     // A swizzle: chunk c of row r sits at c ^ fa(r).  16-byte operand reads
@@ -327,20 +343,19 @@ struct Dma16 {
 
     // One block: the SLOTS MFMAs on `use`, with the READS operand reads of
     // block kk_next of buffer `src` (into `fill`) in the last READS slots
-    // and, when COPY, the DMA_PER_WAVE copies of a look-ahead stage spread
-    // over all slots.  Without copies the reads follow the first MFMAs.
-    template <int I, bool COPY>
+    // and copies [C0, C1) of the look-ahead stage `s` spread over all slots.
+    // Without copies the reads follow the first MFMAs.
+    template <int I, int C0, int C1>
     __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next, const Stage &s,
                                                  const Frags &use, Frags &fill, f32x16_t (&acc)[4][NI]) {
         if constexpr (I < SLOTS) {
+            constexpr int NC = C1 - C0;
             mma_one<I>(use, acc);
-            if constexpr (COPY)
-                copy_range<(I * DMA_PER_WAVE + SLOTS - 1) / SLOTS, ((I + 1) * DMA_PER_WAVE + SLOTS - 1) / SLOTS>(L,
-                                                                                                                 s);
-            constexpr int R = COPY ? I - (SLOTS - READS) : I;
+            copy_range<C0 + (I * NC + SLOTS - 1) / SLOTS, C0 + ((I + 1) * NC + SLOTS - 1) / SLOTS>(L, s);
+            constexpr int R = NC > 0 ? I - (SLOTS - READS) : I;
             if constexpr (R >= 0 && R < READS) read_piece<R>(L, src, kk_next, fill);
             __builtin_amdgcn_sched_barrier(0);
-            block<I + 1, COPY>(L, src, kk_next, s, use, fill, acc);
+            block<I + 1, C0, C1>(L, src, kk_next, s, use, fill, acc);
         }
     }
 
@@ -357,21 +372,25 @@ struct Dma16 {
     // Blocks J..KK-1 of stage kt, held in LDS buffer `buf` (uniform, kept
     // at run time so that one copy of the stage code serves every buffer and
     // every stage count: no unrolled group, no separate tail).  On entry the
-    // operands of block J are in f[J & 1].  Before the last block: wait
-    // until this wave's copies of stage kt+1 have landed (those of stages
-    // kt+2 .. kt+NBUF-1 stay in flight) and barrier, after which stage kt+1
-    // is visible to every wave and buffer `buf` has been read by all of
-    // them, so the last block refills it with stage kt+NBUF while reading
-    // stage kt+1's first operands.
+    // operands of block J are in f[J & 1] and `pend` describes the
+    // look-ahead stage whose part 0 of the copies was issued in the block
+    // before this stage; blocks 0..SPREAD-2 issue its parts 1..SPREAD-1.
+    // Before the last block: wait until this wave's copies of stage kt+1
+    // have landed (those of stages kt+2 .. kt+NBUF-1, all issued by then,
+    // stay in flight) and barrier, after which stage kt+1 is visible to
+    // every wave and buffer `buf` has been read by all of them, so the last
+    // block starts refilling it with stage kt+NBUF while reading stage
+    // kt+1's first operands.
     template <int J = 0>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                  uint32_t lds_addr, int m0, int n0, int kt, int nk, int buf,
-                                                 int wave, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
+                                                 int wave, Stage &pend, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
         const FL_LDS char *cur = lds + buf * BUF_BYTES;
         if constexpr (J < KK - 1) {
-            const Stage none{};
-            block<0, false>(L, cur, J + 1, none, f[J & 1], f[(J + 1) & 1], acc);
-            stage<J + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, f, acc);
+            constexpr int p = J + 1 < SPREAD ? J + 1 : SPREAD;  // part SPREAD is empty
+            block<0, part_lo(p), part_lo(p < SPREAD ? p + 1 : p)>(L, cur, J + 1, pend, f[J & 1], f[(J + 1) & 1],
+                                                                    acc);
+            stage<J + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
         } else {
             const int nbuf = buf + 1 == NBUF ? 0 : buf + 1;
             const FL_LDS char *nxt = lds + nbuf * BUF_BYTES;
@@ -379,8 +398,8 @@ struct Dma16 {
             if (((a.K | a.N) & 7) && kt + 2 == nk)
                 fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
             __syncthreads();
-            const Stage s = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
-            block<0, true>(L, nxt, 0, s, f[J & 1], f[(J + 1) & 1], acc);
+            pend = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
+            block<0, 0, part_lo(1)>(L, nxt, 0, pend, f[J & 1], f[(J + 1) & 1], acc);
         }
     }
 
@@ -394,7 +413,7 @@ struct Dma16 {
     // instruction writes 4 whole rows of 256 bytes (full 128-byte lines).
     static constexpr int EPI_ROW = WN * 2 + 16;
     static constexpr int EPI_WAVE = 128 * EPI_ROW;
-    static constexpr int EPI_BYTES = 4 * EPI_WAVE;
+    static constexpr int EPI_BYTES = WAVES * EPI_WAVE;
     static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
 
     __device__ __forceinline__ static void epilogue_lds(const GemmArgs &a, int m0, int n0, int wave, int wm, int wn,
@@ -456,6 +475,9 @@ struct Dma16 {
                 const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's 128x128
                 *(FL_LDS u32x2_t *)(wbuf + r * EPI_ROW + c * 2) = w;
             }
+            // One row block at a time: without this the scheduler reads
+            // every accumulator out of the AGPRs up front and spills.
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
         asm volatile("" ::: "memory");
@@ -502,7 +524,7 @@ struct Dma16 {
     __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave >> 1, wn = wave & 1;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         int tm, tn;
         grouped_tile(pid, a.tiles_m, a.tiles_n, a.group, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
@@ -521,9 +543,13 @@ struct Dma16 {
         if (nk > 0) {
             Lane L;
             setup(a, m0, n0, wave, lane, wm, wn, L);
+            // Stages 0..NBUF-2 whole, then part 0 of stage NBUF-1's copies
+            // (its other parts go out in stage 0's first blocks).
 #pragma unroll
-            for (int b = 0; b < NBUF; ++b) copy_all(L, stage_of(a, b, wave, lds_addr + b * BUF_BYTES));
-            wait_vm<(NBUF - 1) * DMA_PER_WAVE>();
+            for (int b = 0; b < NBUF - 1; ++b) copy_all(L, stage_of(a, b, wave, lds_addr + b * BUF_BYTES));
+            Stage pend = stage_of(a, NBUF - 1, wave, lds_addr + (NBUF - 1) * BUF_BYTES);
+            copy_range<0, part_lo(1)>(L, pend);
+            wait_vm<(NBUF - 2) * DMA_PER_WAVE + part_lo(1)>();
             if (((a.K | a.N) & 7) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
             __syncthreads();
             Frags f[2];
@@ -532,7 +558,7 @@ struct Dma16 {
             int buf = 0;
 #pragma unroll 1
             for (int kt = 0; kt < nk; ++kt) {
-                stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, f, acc);
+                stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
                 buf = buf + 1 == NBUF ? 0 : buf + 1;
             }
             // The look-ahead copies (past the end of K) must land before this
@@ -718,9 +744,9 @@ __global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArg
     }
 }
 
-template <int DT, int ACT, int BK, int BN>
-__global__ void __launch_bounds__(kThreads, 1) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN>;
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD>
+__global__ void __launch_bounds__(64 * 2 * WAVES_N, 1) fused_linear_dma16_kernel(GemmArgs a) {
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

@@ -76,13 +76,15 @@ struct TileShape {
 // Kernel and tile for a problem.  tile_cfg: 0 automatic, 1 256x256, 2 256x128
 // (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
 // (fp16/bf16), 5 the direct pipeline staged through VGPRs (fp16/bf16, needs
-// aligned rows; checked at launch).  fp32 always runs the register-staged
+// aligned rows; checked at launch), 6 256x256 direct with 8 waves
+// (fp16/bf16).  fp32 always runs the register-staged
 // kernel.  Automatic fp16/bf16 choice: the width (256 or 128) with the
 // smaller waves * relative tile time, a 256x128 tile taking 0.55 of a
-// 256x256 one; ties go to 256.
+// 256x256 one; ties go to 256, which runs the 8-wave kernel (1.5-14% faster
+// than the 4-wave one on every measured shape).
 fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 5) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
         if (cfg == 2) return fail(FL_ERR_UNSUPPORTED, "tile_cfg 2 (256x128) is fp16/bf16 only");
         t = {256, 256, fl::kRegStaged};
@@ -94,6 +96,7 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, Til
     case 3: t = {256, 256, fl::kRegStaged}; return FL_OK;
     case 4: t = {256, 256, fl::kDirect32x256}; return FL_OK;
     case 5: t = {256, 256, fl::kStaged64x256}; return FL_OK;
+    case 6: t = {256, 256, fl::kDirect64x256W8}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
@@ -103,7 +106,7 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, Til
     if (waves128 * 55 < waves256 * 100)
         t = {256, 128, fl::kDirect64x128};
     else
-        t = {256, 256, fl::kDirect64x256};
+        t = {256, 256, fl::kDirect64x256W8};
     return FL_OK;
 }
 

@@ -90,15 +90,18 @@ typedef struct {
                            to the GPU whose workgroups loop over tiles. */
     int32_t tile_cfg;   /* Kernel and tile.  0 = automatic: fp32 runs the
                            register-staged 256x256 kernel; fp16/bf16 run the
-                           direct-to-LDS kernel with 256x256 tiles, or 256x128
-                           when that takes fewer waves x relative tile time
-                           on this GPU's compute units.  1 = 256x256 direct
+                           direct-to-LDS kernel with 256x256 tiles (8 waves,
+                           as 6), or 256x128 (4 waves, as 2) when that takes
+                           fewer waves x relative tile time on this GPU's
+                           compute units.  1 = 256x256 direct, 4 waves
                            (fp16/bf16; fp32 as 0); 2 = 256x128 direct
                            (fp16/bf16 only); 3 = register-staged 256x256 for
                            any dtype; 4 = 256x256 direct with 32-deep K
                            stages; 5 = the direct pipeline with its copies
                            staged through registers (fp16/bf16, K and N
-                           multiples of 8, 16-byte aligned pointers).  Every
+                           multiples of 8, 16-byte aligned pointers);
+                           6 = 256x256 direct with 8 waves (two per SIMD,
+                           128x64 each; fp16/bf16; fp32 as 0).  Every
                            variant gives bit-identical results.  Any other
                            value, or a variant the problem does not allow,
                            is FL_ERR_UNSUPPORTED. */

@@ -113,8 +113,9 @@ def test_tile_grid(lib):
     assert fl.tile_grid(4096, 4096, 4096, BF16, tile_cfg=2) == (256, 128, 16, 32)
     with pytest.raises(fl.FusedLinearError):
         fl.tile_grid(64, 64, 64, F32, tile_cfg=2)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=6) == (256, 256, 16, 16)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=6)
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=7)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
