@@ -91,8 +91,11 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // copies of a look-ahead stage are issued over that many blocks (the block
 // after the barrier that frees their buffer and the next SPREAD-1 blocks)
 // instead of all in one, so the address unit's queue does not fill up and
-// hold back the MFMAs behind them.
-template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1>
+// hold back the MFMAs behind them.  OCC: workgroups resident per CU; with 2
+// the LDS ring and the epilogue staging fit in half of the LDS (72 KB) and
+// the registers in half of the register file, so one workgroup's epilogue
+// and start-up overlap the other's K loop.
+template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr int BM = 256, BN = BN_, BK = BK_;
@@ -108,7 +111,7 @@ struct Dma16 {
     static constexpr int A_BYTES = BM * BK * 2;      // rows of BK*2 bytes
     static constexpr int B_BYTES = BK * BN * 2;      // rows of BN*2 bytes
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-    static constexpr int NBUF = (BN == 256 ? 131072 : 147456) / BUF_BYTES;  // stages in the LDS ring
+    static constexpr int NBUF = (OCC == 2 ? 73728 : BN == 256 ? 131072 : 147456) / BUF_BYTES;  // LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
     static constexpr int B_ROWS_PER_COPY = 64 / CB;  // B rows per 1 KB copy
     static constexpr int NA = BM / (A_ROWS_PER_COPY * WAVES);  // A copies per wave per stage
@@ -126,6 +129,7 @@ struct Dma16 {
     // Copies [part_lo(p), part_lo(p+1)) of a stage form part p.
     static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPREAD; }
     static_assert(NBUF >= 2, "double buffering at least");
+    static_assert(OCC == 1 || (OCC == 2 && WAVES == 4), "two resident workgroups of 4 waves");
 
     // A swizzle: chunk c of row r sits at c ^ fa(r).  16-byte operand reads
     // of 8 consecutive rows (8 lanes per cycle) and of 16 consecutive rows
@@ -744,9 +748,9 @@ __global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArg
     }
 }
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD>
-__global__ void __launch_bounds__(64 * 2 * WAVES_N, 1) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD>;
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC>
+__global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

@@ -597,6 +597,7 @@ enum Variant {
     kStaged64x256 = 3,  // Stg16: the Dma16 pipeline staged through VGPRs (aligned rows)
     kDirect64x128 = 4,  // Dma16 BK 64, 256x128
     kDirect64x256W8 = 5,  // Dma16 BK 64, 256x256, 8 waves (two per SIMD)
+    kDirect32x128Occ2 = 6,  // Dma16 BK 32, 256x128, two workgroups per CU
 };
 
 // Returns the launcher of the fused kernel for (DT, act, variant); defined in

@@ -77,16 +77,22 @@ struct TileShape {
 // (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
 // (fp16/bf16), 5 the direct pipeline staged through VGPRs (fp16/bf16, needs
 // aligned rows; checked at launch), 6 256x256 direct with 8 waves
-// (fp16/bf16).  fp32 always runs the register-staged
-// kernel.  Automatic fp16/bf16 choice: the width (256 or 128) with the
-// smaller waves * relative tile time, a 256x128 tile taking 0.55 of a
-// 256x256 one; ties go to 256, which runs the 8-wave kernel (1.5-14% faster
-// than the 4-wave one on every measured shape).
-fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, TileShape &t) {
+// (fp16/bf16), 7 256x128 with 32-deep K stages, two workgroups per CU
+// (fp16/bf16).  fp32 always runs the register-staged kernel.
+// Automatic fp16/bf16 choice: the width (256 or 128) with the smaller
+// waves * relative tile time, a 256x128 tile taking 0.55 of a 256x256 one;
+// ties go to 256, which runs the 8-wave kernel (1.5-14% faster than the
+// 4-wave one on every measured shape).  Then, when the 256x128 grid fills
+// both workgroup slots of every CU, short reductions switch to the
+// two-per-CU kernel, whose epilogues and start-ups overlap the other
+// workgroup's K loop: K <= 3072 where 256x128 was chosen (measured +16% to
+// +29% at K 256..1024, +4% at 3072, -2% at 4096 on 1024x21568), K <= 512
+// where 256x256 was (+5% at 8192^2 x 512, -3% at 1024).
+fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 7) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
-        if (cfg == 2) return fail(FL_ERR_UNSUPPORTED, "tile_cfg 2 (256x128) is fp16/bf16 only");
+        if (cfg == 2 || cfg == 7) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
         t = {256, 256, fl::kRegStaged};
         return FL_OK;
     }
@@ -97,13 +103,18 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, const fl_options *opt, Til
     case 4: t = {256, 256, fl::kDirect32x256}; return FL_OK;
     case 5: t = {256, 256, fl::kStaged64x256}; return FL_OK;
     case 6: t = {256, 256, fl::kDirect64x256W8}; return FL_OK;
+    case 7: t = {256, 128, fl::kDirect32x128Occ2}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
     const int64_t tm = (M + 255) / 256;
     const int64_t waves256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
     const int64_t waves128 = (tm * ((N + 127) / 128) + cus - 1) / cus;
-    if (waves128 * 55 < waves256 * 100)
+    const bool narrow = waves128 * 55 < waves256 * 100;
+    const bool fills_two = tm * ((N + 127) / 128) >= 2 * cus;
+    if (fills_two && K <= (narrow ? 3072 : 512))
+        t = {256, 128, fl::kDirect32x128Occ2};
+    else if (narrow)
         t = {256, 128, fl::kDirect64x128};
     else
         t = {256, 256, fl::kDirect64x256W8};
@@ -147,7 +158,7 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
         if (opt->no_xcd_remap != 0 && opt->no_xcd_remap != 1)
             return fail(FL_ERR_INVALID_ARG, "no_xcd_remap must be 0 or 1");
         TileShape t;
-        s = tile_shape(dtype, M, N, opt, t);
+        s = tile_shape(dtype, M, N, K, opt, t);
         if (s != FL_OK) return s;
     }
     const size_t es = elem_size(dtype);
@@ -176,7 +187,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
                       int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
-    fl_status s = tile_shape(dtype, M, N, opt, t);
+    fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
     const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
@@ -342,7 +353,7 @@ fl_status fl_tile_grid(int64_t M, int64_t N, int64_t K, fl_dtype dtype, const fl
     fl_status s = check_dims(M, N, K);
     if (s != FL_OK) return s;
     TileShape t;
-    s = tile_shape(dtype, M, N, opt, t);
+    s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
     if (!block_m || !block_n || !tiles_m || !tiles_n) return fail(FL_ERR_INVALID_ARG, "NULL output pointer");
     *block_m = t.bm;

@@ -93,7 +93,10 @@ typedef struct {
                            direct-to-LDS kernel with 256x256 tiles (8 waves,
                            as 6), or 256x128 (4 waves, as 2) when that takes
                            fewer waves x relative tile time on this GPU's
-                           compute units.  1 = 256x256 direct, 4 waves
+                           compute units; short reductions (K <= 3072 for a
+                           256x128 choice, K <= 512 for 256x256) whose
+                           256x128 grid fills two workgroups per compute unit
+                           run as 7.  1 = 256x256 direct, 4 waves
                            (fp16/bf16; fp32 as 0); 2 = 256x128 direct
                            (fp16/bf16 only); 3 = register-staged 256x256 for
                            any dtype; 4 = 256x256 direct with 32-deep K
@@ -101,7 +104,9 @@ typedef struct {
                            staged through registers (fp16/bf16, K and N
                            multiples of 8, 16-byte aligned pointers);
                            6 = 256x256 direct with 8 waves (two per SIMD,
-                           128x64 each; fp16/bf16; fp32 as 0).  Every
+                           128x64 each; fp16/bf16; fp32 as 0); 7 = 256x128
+                           direct with 32-deep K stages and two workgroups
+                           per compute unit (fp16/bf16 only).  Every
                            variant gives bit-identical results.  Any other
                            value, or a variant the problem does not allow,
                            is FL_ERR_UNSUPPORTED. */

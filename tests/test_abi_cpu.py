@@ -114,8 +114,15 @@ def test_tile_grid(lib):
     with pytest.raises(fl.FusedLinearError):
         fl.tile_grid(64, 64, 64, F32, tile_cfg=2)
     assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=6) == (256, 256, 16, 16)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=7) == (256, 128, 16, 32)
+    # short reductions whose 256x128 grid fills two workgroups per CU
+    assert fl.tile_grid(1024, 21568, 256, F16) == (256, 128, 4, 169)
+    assert fl.tile_grid(8192, 8192, 512, F16) == (256, 128, 32, 64)
+    assert fl.tile_grid(8192, 8192, 1024, F16) == (256, 256, 32, 32)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=7)
+        fl.tile_grid(64, 64, 64, F32, tile_cfg=7)
+    with pytest.raises(fl.FusedLinearError):
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=8)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
