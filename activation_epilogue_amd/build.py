@@ -1,7 +1,8 @@
 """Build libfused_linear.so for gfx950 with hipcc, in-tree.
 
 Four translation units compiled in parallel: the host/ABI unit (with the
-elementwise kernels) and one unit of fused GEMM kernels per dtype.  Every
+elementwise kernels) and one unit of fused GEMM kernels per dtype; then the
+separate MFMA-rate probe library used by the benchmark.  Every
 device compile carries -Xclang -target-feature -Xclang -packed-fp32-ops so
 that no packed fp32 instructions are generated.
 """
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfused_linear.so")
+PROBE_LIB = os.path.join(PKG, "libfl_mfma_probe.so")  # measurement aid, not part of the product path
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
@@ -56,6 +58,11 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     tmp = LIB + f".tmp{os.getpid()}"
     subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], check=True)
     os.replace(tmp, LIB)
+    # the sustained-MFMA-rate probe used by bench.py --mfma-ceiling
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "mfma_probe.hip"), "-o", tmp], check=True,
+                   capture_output=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
     p.add_argument("--tile-cfg", type=int, default=0, help="fl_options.tile_cfg (0 = automatic)")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="instead of the workload: the sustained MFMA rate of this GPU (register-only MFMA loop)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -112,8 +114,40 @@ def cpu_baseline(w, d, target_s):
                       f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
 
 
+def mfma_ceiling(args):
+    """Sustained v_mfma_f32_32x32x16_f16 rate with register operands (no
+    memory traffic in the loop), for constant and for random operands: the
+    matrix unit's power, and so the clock the chip holds, depends on how
+    many operand bits toggle.  One JSON line."""
+    import ctypes
+    import torch
+    from activation_epilogue_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.fl_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fl_probe_mfma.restype = ctypes.c_int
+    grid, iters = 256, 4096
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = grid * 4 * 16 * iters * 32768
+    res = {"probe": "v_mfma_f32_32x32x16_f16, 256 workgroups x 4 waves, operands in registers",
+           "peak_datasheet_tflops": PEAK_TFLOPS["f16"]}
+    for random in (0, 1):
+        def step():
+            rc = lib.fl_probe_mfma(out.data_ptr(), grid, iters, random, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"fl_probe_mfma failed: {rc}")
+        ms, _ = time_loop(step, 30, 20, stream)
+        tf = flops / (ms * 1e-3) / 1e12
+        key = "random_operands" if random else "constant_operands"
+        res[key] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["f16"], 4),
+                    "us_per_launch": round(ms * 1e3, 1)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.mfma_ceiling:
+        return mfma_ceiling(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
               "path (the layer shards by output columns or rows with no communication; see DESIGN.md).",
