@@ -17,6 +17,8 @@ Sources (page title, section):
     map ("Tiles and grouped ownership").
   * "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block": the
     gate X + X*Y.
+  * "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a
+    same-shape residual added to the accumulator before the activation.
   * GELU(tanh): not printed on the pages; Hendrycks & Gimpel (2016).
 """
 from __future__ import annotations
@@ -61,11 +63,11 @@ def _load():
             build()
             lib = ctypes.CDLL(LIB)
             p, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-            for name in ("orc_fused_linear", "orc_unfused_chain"):
-                f = getattr(lib, name)
-                f.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
-                f.restype = c_int
-            lib.orc_element.argtypes = [c_int, c_int, p, p, p, p, i64, i64, i64, i64, i64, p]
+            lib.orc_fused_linear.argtypes = [c_int, c_int, p, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
+            lib.orc_fused_linear.restype = c_int
+            lib.orc_unfused_chain.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
+            lib.orc_unfused_chain.restype = c_int
+            lib.orc_element.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, i64, i64, p]
             lib.orc_element.restype = c_int
             lib.orc_decode.argtypes = [c_int, p, i64, p]
             lib.orc_encode.argtypes = [c_int, p, i64, p]
@@ -90,9 +92,9 @@ def _raw(a, dtype):
     return a
 
 
-def _call(fname, A, B, bias, Y, act, dtype, rows, threads, want_x):
+def _call(fname, A, B, bias, Y, act, dtype, rows, threads, want_x, R=None):
     lib = _load()
-    A, B, bias, Y = (_raw(x, dtype) for x in (A, B, bias, Y))
+    A, B, bias, Y, R = (_raw(x, dtype) for x in (A, B, bias, Y, R))
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
@@ -101,6 +103,8 @@ def _call(fname, A, B, bias, Y, act, dtype, rows, threads, want_x):
         raise ValueError("bias is (N,)")
     if act == "glu" and (Y is None or Y.shape != (M, N)):
         raise ValueError("the gate needs Y of shape (M,N)")
+    if R is not None and R.shape != (M, N):
+        raise ValueError("the residual R is (M,N)")
     if rows is None:
         nrows, rows_arr = M, None
     else:
@@ -108,19 +112,26 @@ def _call(fname, A, B, bias, Y, act, dtype, rows, threads, want_x):
         nrows = rows_arr.size
     out = np.empty((nrows, N), dtype=STORAGE[dtype])
     x = np.empty((nrows, N), dtype=np.float64) if want_x else None
-    st = getattr(lib, fname)(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(Y),
-                             _ptr(out), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(x))
+    head = (DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias))
+    tail = (_ptr(Y), _ptr(out), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(x))
+    if fname == "orc_fused_linear":
+        st = lib.orc_fused_linear(*head, _ptr(R), *tail)
+    else:
+        if R is not None:
+            raise ValueError("the unfused chain has no residual stage")
+        st = getattr(lib, fname)(*head, *tail)
     if st != 0:
         raise RuntimeError(f"{fname} failed with status {st}")
     return (out, x) if want_x else out
 
 
-def fused_linear(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None, want_x=False):
-    """round_once(act(A@B + bias)) in the storage type of ``dtype``.
+def fused_linear(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None, want_x=False, R=None):
+    """round_once(act(A@B + bias [+ R])) in the storage type of ``dtype``.
 
+    ``R`` is an optional (M,N) residual added before the activation.
     ``rows`` selects output rows (the result then has len(rows) rows).
     ``want_x`` also returns the unrounded FP64 epilogue value."""
-    return _call("orc_fused_linear", A, B, bias, Y, act, dtype, rows, threads, want_x)
+    return _call("orc_fused_linear", A, B, bias, Y, act, dtype, rows, threads, want_x, R)
 
 
 def unfused_chain(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None):
@@ -128,14 +139,14 @@ def unfused_chain(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, thread
     return _call("orc_unfused_chain", A, B, bias, Y, act, dtype, rows, threads, False)
 
 
-def element(A, B, bias, Y, act, dtype, i, j):
-    """Unrounded FP64 act(A[i,:]@B[:,j] + bias[j])."""
+def element(A, B, bias, Y, act, dtype, i, j, R=None):
+    """Unrounded FP64 act(A[i,:]@B[:,j] + bias[j] [+ R[i,j]])."""
     lib = _load()
-    A, B, bias, Y = (_raw(x, dtype) for x in (A, B, bias, Y))
+    A, B, bias, Y, R = (_raw(x, dtype) for x in (A, B, bias, Y, R))
     M, K = A.shape
     N = B.shape[1]
     v = ctypes.c_double()
-    st = lib.orc_element(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(Y),
+    st = lib.orc_element(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(R), _ptr(Y),
                          M, N, K, int(i), int(j), ctypes.addressof(v))
     if st != 0:
         raise RuntimeError("orc_element failed")

@@ -11,6 +11,7 @@
  * fusion, no reordering):
  *   X[i,j]   = sum_k A[i,k] * B[k,j]              (FP64, k ascending)
  *   X[i,j]  += bias[j]                            (once, by column)
+ *   X[i,j]  += R[i,j]                             (residual, when given)
  *   out[i,j] = act(X[i,j]) (or X + X*Y for the gate)
  *   out      = round_to_nearest_even(out, dtype)  (once, at the end)
  *
@@ -27,6 +28,9 @@
  *     with actual_group = min(GROUP, tiles_m - first_m).
  *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block":
  *     X = A@B + bias, out = X + X*Y.
+ *   - "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants":
+ *     a same-shape residual tile is added to the accumulator after the K
+ *     loop, before the activation.
  *   - GELU: the pages name it as a fusable activation but print no formula;
  *     this file uses the tanh form of Hendrycks & Gimpel (2016),
  *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with libm tanh.
@@ -176,19 +180,21 @@ static int check_args(int dtype, int act, const void *A, const void *B,
 }
 
 /*
- * out (nrows x N, dtype) = round(act(A[rows]@B + bias)).
- * rows == NULL computes every row (nrows must equal M).  bias may be NULL
- * (counts as zero).  Y is (M, N) and read only for the gate.  x_out, when not
+ * out (nrows x N, dtype) = round(act(A[rows]@B + bias + R)).
+ * rows == NULL computes every row (nrows must equal M).  bias and the
+ * residual R (M, N) may be NULL (count as zero).  Y is (M, N) and read only
+ * for the gate.  x_out, when not
  * NULL, receives the unrounded FP64 value after the epilogue (nrows x N).
  * unfused != 0 switches to the three-stage chain that rounds after every
  * stage: round(act(round(round(A@B) + bias))), which is what separate
  * GEMM, bias and activation kernels each storing in dtype compute.
  */
 static int run(int dtype, int act, const void *A, const void *B,
-               const void *bias, const void *Y, void *out, int64_t M,
-               int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
-               int nthreads, double *x_out, int unfused) {
+               const void *bias, const void *R, const void *Y, void *out,
+               int64_t M, int64_t N, int64_t K, const int64_t *rows,
+               int64_t nrows, int nthreads, double *x_out, int unfused) {
     if (check_args(dtype, act, A, B, Y, out, M, N, K)) return 1;
+    if (unfused && R) return 1; /* the chain has no residual stage */
     if (!rows) nrows = M;
     if (nrows < 0) return 1;
     if (rows)
@@ -225,7 +231,8 @@ static int run(int dtype, int act, const void *A, const void *B,
                     double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
                     double x = acc[j], v;
                     if (!unfused) {
-                        v = apply_act(act, x + bias64[j], y);
+                        double res = R ? dec_one(dtype, R, i * N + j) : 0.0;
+                        v = apply_act(act, x + bias64[j] + res, y);
                     } else {
                         double tmp[1];
                         uint16_t h[2];
@@ -252,29 +259,31 @@ static int run(int dtype, int act, const void *A, const void *B,
 }
 
 int orc_fused_linear(int dtype, int act, const void *A, const void *B,
-                     const void *bias, const void *Y, void *out, int64_t M,
-                     int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
-                     int nthreads, double *x_out) {
-    return run(dtype, act, A, B, bias, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0);
+                     const void *bias, const void *R, const void *Y, void *out,
+                     int64_t M, int64_t N, int64_t K, const int64_t *rows,
+                     int64_t nrows, int nthreads, double *x_out) {
+    return run(dtype, act, A, B, bias, R, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0);
 }
 
 int orc_unfused_chain(int dtype, int act, const void *A, const void *B,
                       const void *bias, const void *Y, void *out, int64_t M,
                       int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
                       int nthreads, double *x_out) {
-    return run(dtype, act, A, B, bias, Y, out, M, N, K, rows, nrows, nthreads, x_out, 1);
+    return run(dtype, act, A, B, bias, NULL, Y, out, M, N, K, rows, nrows, nthreads, x_out, 1);
 }
 
-/* Single output element (i, j), FP64, unrounded: act(sum_k A[i,k]B[k,j] + bias[j]). */
+/* Single output element (i, j), FP64, unrounded:
+ * act(sum_k A[i,k]B[k,j] + bias[j] + R[i,j]). */
 int orc_element(int dtype, int act, const void *A, const void *B,
-                const void *bias, const void *Y, int64_t M, int64_t N,
-                int64_t K, int64_t i, int64_t j, double *value) {
+                const void *bias, const void *R, const void *Y, int64_t M,
+                int64_t N, int64_t K, int64_t i, int64_t j, double *value) {
     if (check_args(dtype, act, A, B, Y, value, M, N, K)) return 1;
     if (i < 0 || i >= M || j < 0 || j >= N) return 1;
     double x = 0.0;
     for (int64_t k = 0; k < K; ++k)
         x += dec_one(dtype, A, i * K + k) * dec_one(dtype, B, k * N + j);
     x += bias ? dec_one(dtype, bias, j) : 0.0;
+    x += R ? dec_one(dtype, R, i * N + j) : 0.0;
     double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
     *value = apply_act(act, x, y);
     return 0;

@@ -116,3 +116,26 @@ def test_bias_in_reduction_passes_at_k1_fails_at_k3():
             assert _flagged(out, chain, 127, 129) == expect_flag
     finally:
         BK = saved
+
+
+@pytest.mark.parametrize("mistake", ["residual_after_relu", "residual_row_broadcast", "residual_transposed"])
+def test_residual_mutant_is_flagged(mistake):
+    """The residual variant ("Variants": add the same-shape tile before the
+    activation) with the mistakes a kernel could make; each must fail the
+    tolerance check on the ragged workload."""
+    w = synth.WORKLOADS["relu_f32_127x129x96"]
+    d = synth.draw(w.M, w.N, w.K, "f32", "relu", seed=0)
+    R = synth.to_storage(np.random.default_rng(5).standard_normal((w.M, w.N)), "f32")
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], act="relu", dtype="f32", R=R)
+    A, B, b, R64 = (x.astype(np.float64) for x in (d["A"], d["B"], d["bias"], R))
+    X = A @ B + b[None, :]
+    if mistake == "residual_after_relu":
+        out = np.maximum(X, 0.0) + R64
+    elif mistake == "residual_row_broadcast":
+        out = np.maximum(X + R64[:, :1], 0.0)
+    else:
+        Rt = R64.ravel()[:w.M * w.N].reshape(w.N, w.M).T  # (N,M) storage read as (M,N)
+        out = np.maximum(X + Rt, 0.0)
+    assert not oracle.compare(out.astype(np.float32), ref, "f32")["ok"], mistake
+    good = np.maximum(X + R64, 0.0)
+    assert oracle.compare(good.astype(np.float32), ref, "f32")["ok"]

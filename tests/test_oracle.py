@@ -297,3 +297,83 @@ def test_tile_map_rejects_bad_arguments():
     for args in ((6, 3, 2, 2), (-1, 3, 2, 2), (0, 0, 2, 1), (0, 3, 2, 0)):
         with pytest.raises(ValueError):
             oracle.tile_of_pid(*args)
+
+
+# -------------------------------------------------------------- residual add
+# "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a
+# same-shape residual tile is added to the accumulator after the K loop,
+# before the activation.
+
+def _draw_residual(M, N, dtype, seed, rmax=3):
+    """Integer residual in {-rmax..rmax}, stored in dtype (exact)."""
+    rng = np.random.default_rng(seed)
+    return synth.to_storage(rng.integers(-rmax, rmax + 1, (M, N)).astype(np.float64), dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+def test_residual_of_zeros_changes_nothing(dtype, act):
+    d = synth.draw(33, 47, 29, dtype, act, seed=4)
+    zero = synth.to_storage(np.zeros((33, 47)), dtype)
+    plain = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    with_r = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=zero)
+    assert np.array_equal(plain.view(np.uint8), with_r.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (17, 33, 0), (40, 65, 30)])
+def test_residual_integer_inputs_bit_exact(dtype, act, shape):
+    """Brute force in int64: act(A@B + bias + R), every value exact."""
+    M, N, K = shape
+    d = synth.draw_integer(M, N, K, dtype, act, seed=M + 3 * N + 7 * K, amax=1, bias_max=3)
+    Rs = _draw_residual(M, N, dtype, seed=K + 1)
+    A, B, bias, R = (oracle.decode(x, dtype).astype(np.int64) for x in (d["A"], d["B"], d["bias"], Rs))
+    X = A @ B + bias[None, :] + R
+    if act == "relu":
+        exp = np.maximum(X, 0)
+    elif act == "glu":
+        exp = X + X * oracle.decode(d["Y"], dtype).astype(np.int64)
+    else:
+        exp = X
+    assert np.abs(exp).max(initial=0) <= 256
+    out = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=Rs)
+    assert np.array_equal(oracle.decode(out, dtype), exp.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+def test_residual_that_cancels_gives_zero(dtype, act):
+    """R = -(A@B + bias), exact in integers: the residual enters before the
+    activation, so every output is act(0) = 0; a residual added after the
+    activation would leave act(X) - X, nonzero wherever X < 0 (ReLU) or X != 0."""
+    M, N, K = 24, 40, 16
+    d = synth.draw_integer(M, N, K, dtype, act, seed=9, amax=1, bias_max=3)
+    A, B, bias = (oracle.decode(d[k], dtype).astype(np.int64) for k in ("A", "B", "bias"))
+    X = A @ B + bias[None, :]
+    R = synth.to_storage(-X.astype(np.float64), dtype)
+    out = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=R)
+    assert np.array_equal(oracle.decode(out, dtype), np.zeros((M, N)))
+    if act == "relu":
+        after = np.maximum(X, 0) - X
+        assert (after != 0).any()
+
+
+def test_residual_element_and_rows_match_full():
+    d = synth.draw(30, 50, 40, "f16", "glu", seed=12)
+    R = synth.to_storage(np.random.default_rng(0).standard_normal((30, 50)), "f16")
+    full, xf = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act="glu", dtype="f16", want_x=True, R=R)
+    rows = np.array([29, 3, 3])
+    assert np.array_equal(oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act="glu", dtype="f16",
+                                              rows=rows, R=R), full[rows])
+    for (i, j) in [(0, 0), (29, 49), (11, 7)]:
+        v = oracle.element(d["A"], d["B"], d["bias"], d["Y"], "glu", "f16", i, j, R=R)
+        assert abs(v - xf[i, j]) <= 1e-12 * max(1.0, abs(v))
+
+
+def test_residual_fp64_value_matches_numpy():
+    d = synth.draw(64, 96, 80, "f32", "none", seed=13)
+    R = synth.to_storage(np.random.default_rng(1).standard_normal((64, 96)), "f32")
+    A, B, bias, R64 = (oracle.decode(x, "f32") for x in (d["A"], d["B"], d["bias"], R))
+    _, x = oracle.fused_linear(d["A"], d["B"], d["bias"], act="none", dtype="f32", want_x=True, R=R)
+    np.testing.assert_allclose(x, A @ B + bias[None, :] + R64, rtol=1e-12, atol=1e-13)
