@@ -8,7 +8,8 @@ runs in the library's HIP kernels; there is no fallback.  If the library has
 not been built, importing works but every call raises ``LibraryNotBuilt``.
 
 Entry points (same names as the C ABI, without the ``fl_`` prefix):
-  fused_linear(A, B, bias=None, Y=None, act="relu", out=None, **options)
+  fused_linear(A, B, bias=None, Y=None, act="relu", out=None, R=None, **options)
+                                          # R: residual -> fl_fused_linear_residual
   gemm(A, B, X=None)                      # unfused step 1: X = A@B
   bias_add(X, bias)                       # unfused step 2: X += bias (in place)
   activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
@@ -24,7 +25,8 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
-EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_gemm", "fl_bias_add", "fl_activation",
+EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_gemm", "fl_bias_add",
+           "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
 
@@ -60,13 +62,15 @@ def load_library():
     P_i32 = ctypes.POINTER(ctypes.c_int32)
     lib.fl_fused_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp]
     lib.fl_fused_linear_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, ctypes.POINTER(Options)]
+    lib.fl_fused_linear_residual.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
+                                             ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
     lib.fl_activation.argtypes = [vp, vp, vp, i64, i64, c_int, c_int, vp]
     lib.fl_tile_grid.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(Options), P_i32, P_i32, P_i32, P_i32]
     lib.fl_tile_of_program.argtypes = [i32, i32, i32, i32, i32, i32, P_i32, P_i32]
-    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_gemm", "fl_bias_add", "fl_activation",
-              "fl_tile_grid", "fl_tile_of_program"):
+    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_gemm", "fl_bias_add",
+              "fl_activation", "fl_tile_grid", "fl_tile_of_program"):
         getattr(lib, f).restype = c_int
     lib.fl_status_string.argtypes = [c_int]
     lib.fl_status_string.restype = ctypes.c_char_p
@@ -119,11 +123,12 @@ def _options(group_m=0, persistent=0, tile_cfg=0, no_xcd_remap=0, debug_tile_cou
     return Options(int(group_m), int(persistent), int(tile_cfg), int(no_xcd_remap), ptr)
 
 
-def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, stream=None, **options):
-    """out = act(A@B + bias) in one kernel.  A (M,K), B (K,N), bias (N,),
-    Y (M,N) for act="glu" (out = X + X*Y).  Returns out (allocated with torch
-    if not given).  Keyword options map to fl_options (group_m, persistent,
-    tile_cfg, no_xcd_remap, debug_tile_count)."""
+def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, R=None, stream=None, **options):
+    """out = act(A@B + bias [+ R]) in one kernel.  A (M,K), B (K,N), bias (N,),
+    Y (M,N) for act="glu" (out = X + X*Y), R (M,N) an optional residual added
+    before the activation (fl_fused_linear_residual).  Returns out (allocated
+    with torch if not given).  Keyword options map to fl_options (group_m,
+    persistent, tile_cfg, no_xcd_remap, debug_tile_count)."""
     import torch
     lib = load_library()
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
@@ -134,6 +139,13 @@ def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, stream=None, 
     code = _dtype_code(dt)
     if out is None:
         out = torch.empty((M, N), dtype=dt, device=A.device)
+    if R is not None:
+        opt = _options(**options)
+        _check(lib.fl_fused_linear_residual(
+            _dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(bias, "bias", dt, (N,)),
+            _dev_ptr(R, "R", dt, (M, N)), _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", dt, (M, N)),
+            M, N, K, ACTS[act], code, _stream(A, stream), ctypes.byref(opt)))
+        return out
     args = (_dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(bias, "bias", dt, (N,)),
             _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", dt, (M, N)), M, N, K, ACTS[act], code,
             _stream(A, stream))

@@ -94,8 +94,10 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // hold back the MFMAs behind them.  OCC: workgroups resident per CU; with 2
 // the LDS ring and the epilogue staging fit in half of the LDS (72 KB) and
 // the registers in half of the register file, so one workgroup's epilogue
-// and start-up overlap the other's K loop.
-template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1>
+// and start-up overlap the other's K loop.  RES: the epilogue adds the
+// residual a.R (compiled in only where it is used, so the plain epilogue
+// keeps its registers).
+template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr int BM = 256, BN = BN_, BK = BK_;
@@ -429,6 +431,9 @@ struct Dma16 {
         const __amdgpu_buffer_rsrc_t rO = make_rsrc(static_cast<char *>(a.out) + o_org * 2, o_bytes);
         const __amdgpu_buffer_rsrc_t rY =
             make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * 2 : nullptr, a.Y ? o_bytes : 0);
+        constexpr bool has_r = RES;
+        const __amdgpu_buffer_rsrc_t rR =
+            make_rsrc(has_r ? static_cast<const char *>(a.R) + o_org * 2 : nullptr, has_r ? o_bytes : 0);
         const __amdgpu_buffer_rsrc_t rBias =
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * 2 : nullptr,
                       a.bias ? (size_t)(a.N - n0) * 2 : 0);
@@ -450,10 +455,20 @@ struct Dma16 {
             const int row = wm * 128 + mi * 32 + lrow;
             return (m0 + row < a.M && valid[g] > 0) ? (uint32_t)(row * a.N + col[g]) * 2 : kOob;
         };
-        quad_t yq[2][NG];
+        // Y (gate) of row block mi+1 is loaded before row block mi is
+        // computed, and so is R (residual) except with the gate, where the
+        // registers for two look-ahead rings are not there and R is loaded
+        // for the current row block.  Every load precedes the stores of
+        // phase 2, so out may alias Y or R.
+        constexpr int RA = ACT == FL_ACT_GLU ? 0 : 1;  // residual row blocks loaded ahead
+        quad_t yq[2][NG], rq[RA + 1][NG];
         if constexpr (ACT == FL_ACT_GLU) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) yq[0][g] = base::load4(rY, yoff(0, g), valid[g]);
+        }
+        if constexpr (RA && has_r) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) rq[0][g] = base::load4(rR, yoff(0, g), valid[g]);
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -463,6 +478,11 @@ struct Dma16 {
                     for (int g = 0; g < NG; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
                 }
             }
+            if (has_r && mi + RA < 4) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    rq[(mi + RA) % (RA + 1)][g] = base::load4(rR, yoff(mi + RA, g), valid[g]);
+            }
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int ni = g >> 2, q = g & 3;
@@ -470,7 +490,8 @@ struct Dma16 {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
-                    const float x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
+                    float x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
+                    if constexpr (has_r) x += base::elem_f32(rq[mi % (RA + 1)][g], e);
                     o[e] = io::from_f32(activate<ACT>(x, y));
                 }
                 u32x2_t w;
@@ -580,177 +601,9 @@ struct Dma16 {
     }
 };
 
-// Register-staged variant of the same pipeline (NBUF = 2, BK = 64, K and N
-// multiples of 8): the
-// copies of a stage go global -> VGPR (buffer_load_dwordx4, 16 per wave)
-// -> LDS (ds_write_b128 at the position the direct copy would have used),
-// so the LDS layout, the operand reads and the MFMA order -- and therefore
-// the results, bit for bit -- are those of Dma16.  Loads of stage kt+2 are
-// issued in the last block of stage kt (right after the barrier that
-// follows the writes of stage kt+1); their writes go into the free buffer
-// during block 2 of stage kt+1, before the barrier that publishes them.
-template <int DT, int ACT>
-struct Stg16 : Dma16<DT, ACT, 64> {
-    using D = Dma16<DT, ACT, 64, 256>;
-    using typename D::Frags;
-    using typename D::Lane;
-    using typename D::Stage;
-    static constexpr int NA = D::NA, NB = D::NB, NC = D::DMA_PER_WAVE, KK = D::KK, BUF_BYTES = D::BUF_BYTES;
-    static constexpr int NI = D::NI;
-    static constexpr int A_BYTES = D::A_BYTES;
-
-    struct Regs {
-        u32x4_t v[NC];
-    };
-
-    template <int I>
-    __device__ __forceinline__ static void load_one(const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
-                                                    const __amdgpu_buffer_rsrc_t &rB, const Stage &s, Regs &r) {
-        if constexpr (I < NA) {
-            const uint32_t off = L.a_off[I & 1] + (uint32_t)(I >> 1) * L.a_step;
-            r.v[I] = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, L.a_k[I & 1] < s.kleft ? off : kOob, s.soa, 0));
-        } else {
-            constexpr int i = I - NA;
-            const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
-            const bool ok = (L.b_k0 + 2 * i < s.kleft) && (L.b_off[i & 1] != kOob);
-            r.v[I] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? off : kOob, s.sob, 0));
-        }
-    }
-
-    // LDS byte address of copy I of this wave's lane within a buffer.
-    template <int I>
-    __device__ __forceinline__ static int store_addr(int wave, int lane) {
-        if constexpr (I < NA)
-            return (wave * NA + I) * 1024 + lane * 16;
-        else
-            return A_BYTES + (wave * NB + (I - NA)) * 1024 + lane * 16;
-    }
-
-    // Block of 16 MFMAs on `use` with the reads of (src, kk_next) into fill,
-    // plus one load (MODE 1) or one LDS write (MODE 2) per MFMA slot.
-    template <int I, int MODE>
-    __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next,
-                                                 const __amdgpu_buffer_rsrc_t &rA, const __amdgpu_buffer_rsrc_t &rB,
-                                                 const Stage &s, FL_LDS char *wbuf, int wave, int lane, Regs &r,
-                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][NI]) {
-        if constexpr (I < 16) {
-            D::template mma_one<I>(use, acc);
-            if constexpr (MODE == 1) load_one<I>(L, rA, rB, s, r);
-            if constexpr (MODE == 2) *(FL_LDS u32x4_t *)(wbuf + store_addr<I>(wave, lane)) = r.v[I];
-            constexpr int R = (MODE == 1) ? I - 4 : I;
-            if constexpr (R >= 0 && R < 12) D::template read_piece<R>(L, src, kk_next, fill);
-            __builtin_amdgcn_sched_barrier(0);
-            block<I + 1, MODE>(L, src, kk_next, rA, rB, s, wbuf, wave, lane, r, use, fill, acc);
-        }
-    }
-
-    // Stage kt in buffer B (operands of block 0 in f[0]; loads of stage kt+1
-    // in flight in r).
-    template <int B>
-    __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
-                                                 const __amdgpu_buffer_rsrc_t &rB, FL_LDS char *lds, int kt,
-                                                 int wave, int lane, Regs &r, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
-        FL_LDS char *cur = lds + B * BUF_BYTES;
-        FL_LDS char *nxt = lds + (B ^ 1) * BUF_BYTES;
-        const Stage none{};
-        block<0, 0>(L, cur, 1, rA, rB, none, nullptr, wave, lane, r, f[0], f[1], acc);
-        block<0, 0>(L, cur, 2, rA, rB, none, nullptr, wave, lane, r, f[1], f[0], acc);
-        block<0, 2>(L, cur, 3, rA, rB, none, nxt, wave, lane, r, f[0], f[1], acc);
-        __syncthreads();  // stage kt+1 written by every wave; buffer B fully read
-        const Stage s = D::stage_of(a, kt + 2, wave, 0);
-        block<0, 1>(L, nxt, 0, rA, rB, s, nullptr, wave, lane, r, f[1], f[0], acc);
-    }
-
-    __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
-        const int tid = threadIdx.x, lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave >> 1, wn = wave & 1;
-        int tm, tn;
-        grouped_tile(pid, a.tiles_m, a.tiles_n, a.group, tm, tn);
-        const int m0 = tm * D::BM, n0 = tn * D::BN;
-        FL_LDS char *lds = (FL_LDS char *)smem;
-
-        f32x16_t acc[4][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
-
-        const int nk = (a.K + D::BK - 1) / D::BK;
-        if (nk > 0) {
-            Lane L;
-            D::setup(a, m0, n0, wave, lane, wm, wn, L);
-            const size_t a_org = (size_t)m0 * a.K;
-            const __amdgpu_buffer_rsrc_t rA =
-                make_rsrc(static_cast<const char *>(a.A) + a_org * 2, ((size_t)a.M * a.K - a_org) * 2);
-            const __amdgpu_buffer_rsrc_t rB =
-                make_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * 2, ((size_t)a.K * a.N - n0) * 2);
-            Regs r;
-            // stage 0 -> buffer 0, then stage 1 loads in flight
-            const Stage s0 = D::stage_of(a, 0, wave, 0);
-            load_all(L, rA, rB, s0, r);
-            store_all(lds, wave, lane, r);
-            const Stage s1 = D::stage_of(a, 1, wave, 0);
-            load_all(L, rA, rB, s1, r);
-            __syncthreads();
-            Frags f[2];
-            D::read_all(L, lds, 0, f[0]);
-            int kt = 0;
-            for (; kt + 2 <= nk; kt += 2) {
-                stage<0>(a, L, rA, rB, lds, kt, wave, lane, r, f, acc);
-                stage<1>(a, L, rA, rB, lds, kt + 1, wave, lane, r, f, acc);
-            }
-            if (kt < nk) stage<0>(a, L, rA, rB, lds, kt, wave, lane, r, f, acc);
-            // the look-ahead loads past the end of K are still in flight
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-        D::epilogue_lds(a, m0, n0, wave, wm, wn, lane, acc, lds);
-        if (a.tile_count && tid == 0) atomicAdd(&a.tile_count[tm * a.tiles_n + tn], 1u);
-    }
-
-    template <int I = 0>
-    __device__ __forceinline__ static void load_all(const Lane &L, const __amdgpu_buffer_rsrc_t &rA,
-                                                    const __amdgpu_buffer_rsrc_t &rB, const Stage &s, Regs &r) {
-        if constexpr (I < NC) {
-            load_one<I>(L, rA, rB, s, r);
-            load_all<I + 1>(L, rA, rB, s, r);
-        }
-    }
-    template <int I = 0>
-    __device__ __forceinline__ static void store_all(FL_LDS char *buf, int wave, int lane, const Regs &r) {
-        if constexpr (I < NC) {
-            *(FL_LDS u32x4_t *)(buf + store_addr<I>(wave, lane)) = r.v[I];
-            store_all<I + 1>(buf, wave, lane, r);
-        }
-    }
-};
-
-template <int DT, int ACT>
-__global__ void __launch_bounds__(kThreads, 1) fused_linear_stg16_kernel(GemmArgs a) {
-    using T = Stg16<DT, ACT>;
-    __shared__ __attribute__((aligned(1024))) char smem[(2 * T::BUF_BYTES > T::D::EPI_BYTES) ? 2 * T::BUF_BYTES : T::D::EPI_BYTES];
-    const int ntiles = a.tiles_m * a.tiles_n;
-    if (!a.persistent) {
-        const int pid = a.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-        T::run_tile(a, pid, smem);
-    } else {
-        const int G = gridDim.x;
-        const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
-        for (int base = 0; base < ntiles; base += G) {
-            const int pid = base + slot;
-            if (pid < ntiles) T::run_tile(a, pid, smem);
-            __syncthreads();
-        }
-    }
-}
-
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC>;
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

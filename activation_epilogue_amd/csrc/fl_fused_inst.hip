@@ -21,46 +21,39 @@ void launch(const GemmArgs &a, int grid, hipStream_t s) {
 // 4096^3 fp16, 8192x14336x4096 bf16 and 1024x21568x4096 fp16 shapes.
 constexpr int kCopySpread = 2;
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, bool RES>
 void launch_dma(const GemmArgs &a, int grid, hipStream_t s) {
     if constexpr (DT != FL_F32)
-        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC>), dim3(grid),
+        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES>), dim3(grid),
                            dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
 }
 
-template <int DT, int BK, int BN, int WAVES_N = 2, int OCC = 1>
-fused_launcher pick_dma(int act) {
+template <int DT, int BK, int BN, int WAVES_N, int OCC, bool RES>
+fused_launcher pick_dma_res(int act) {
     switch (act) {
-    case FL_ACT_NONE: return launch_dma<DT, FL_ACT_NONE, BK, BN, WAVES_N, OCC>;
-    case FL_ACT_RELU: return launch_dma<DT, FL_ACT_RELU, BK, BN, WAVES_N, OCC>;
-    case FL_ACT_GELU_TANH: return launch_dma<DT, FL_ACT_GELU_TANH, BK, BN, WAVES_N, OCC>;
-    default: return launch_dma<DT, FL_ACT_GLU, BK, BN, WAVES_N, OCC>;
+    case FL_ACT_NONE: return launch_dma<DT, FL_ACT_NONE, BK, BN, WAVES_N, OCC, RES>;
+    case FL_ACT_RELU: return launch_dma<DT, FL_ACT_RELU, BK, BN, WAVES_N, OCC, RES>;
+    case FL_ACT_GELU_TANH: return launch_dma<DT, FL_ACT_GELU_TANH, BK, BN, WAVES_N, OCC, RES>;
+    default: return launch_dma<DT, FL_ACT_GLU, BK, BN, WAVES_N, OCC, RES>;
     }
 }
 
-template <int DT, int ACT>
-void launch_stg(const GemmArgs &a, int grid, hipStream_t s) {
-    if constexpr (DT != FL_F32)
-        hipLaunchKernelGGL((fused_linear_stg16_kernel<DT, ACT>), dim3(grid), dim3(kThreads), 0, s, a);
+template <int DT, int BK, int BN, int WAVES_N = 2, int OCC = 1>
+fused_launcher pick_dma(int act, bool residual) {
+    return residual ? pick_dma_res<DT, BK, BN, WAVES_N, OCC, true>(act)
+                    : pick_dma_res<DT, BK, BN, WAVES_N, OCC, false>(act);
 }
 
 template <>
-fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant) {
+fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant, bool residual) {
     constexpr int DT = FL_INST_DTYPE;
     if constexpr (DT != FL_F32) {
         switch (variant) {
-        case kDirect64x256: return pick_dma<DT, 64, 256>(act);
-        case kDirect32x256: return pick_dma<DT, 32, 256>(act);
-        case kDirect64x128: return pick_dma<DT, 64, 128>(act);
-        case kDirect64x256W8: return pick_dma<DT, 64, 256, 4>(act);
-        case kDirect32x128Occ2: return pick_dma<DT, 32, 128, 2, 2>(act);
-        case kStaged64x256:
-            switch (act) {
-            case FL_ACT_NONE: return launch_stg<DT, FL_ACT_NONE>;
-            case FL_ACT_RELU: return launch_stg<DT, FL_ACT_RELU>;
-            case FL_ACT_GELU_TANH: return launch_stg<DT, FL_ACT_GELU_TANH>;
-            default: return launch_stg<DT, FL_ACT_GLU>;
-            }
+        case kDirect64x256: return pick_dma<DT, 64, 256>(act, residual);
+        case kDirect32x256: return pick_dma<DT, 32, 256>(act, residual);
+        case kDirect64x128: return pick_dma<DT, 64, 128>(act, residual);
+        case kDirect64x256W8: return pick_dma<DT, 64, 256, 4>(act, residual);
+        case kDirect32x128Occ2: return pick_dma<DT, 32, 128, 2, 2>(act, residual);
         default: break;
         }
     }

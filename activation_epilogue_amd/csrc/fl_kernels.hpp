@@ -178,6 +178,7 @@ struct GemmArgs {
     const void *B;
     const void *bias;  // may be null
     const void *Y;     // gate operand or null
+    const void *R;     // residual (M,N) added before the activation, or null
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;
@@ -396,6 +397,9 @@ struct FusedTile {
         const __amdgpu_buffer_rsrc_t rO = make_rsrc(static_cast<char *>(a.out) + o_org * ES, o_bytes);
         const __amdgpu_buffer_rsrc_t rY =
             make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * ES : nullptr, a.Y ? o_bytes : 0);
+        const bool has_r = a.R != nullptr;
+        const __amdgpu_buffer_rsrc_t rR =
+            make_rsrc(has_r ? static_cast<const char *>(a.R) + o_org * ES : nullptr, has_r ? o_bytes : 0);
         const __amdgpu_buffer_rsrc_t rBias =
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * ES : nullptr,
                       a.bias ? (size_t)(a.N - n0) * ES : 0);
@@ -433,11 +437,15 @@ struct FusedTile {
             for (int g = 0; g < 16; ++g) {
                 const int ni = g >> 2, q = g & 3;
                 const uint32_t off = offset(mi, g);
+                // residual of this group, read (like Y) before this row block's stores
+                quad_t rq = quad_t{};
+                if (has_r) rq = load4(rR, off, valid[g]);
                 bits o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = (ACT == FL_ACT_GLU) ? elem_f32(yq[mi & 1][g], e) : 0.0f;
-                    const float x = acc[mi][ni][q * 4 + e] + elem_f32(bq[g], e);
+                    float x = acc[mi][ni][q * 4 + e] + elem_f32(bq[g], e);
+                    if (has_r) x += elem_f32(rq, e);
                     o[e] = __builtin_bit_cast(bits, io::from_f32(activate<ACT>(x, y)));
                 }
                 if (VECTOR && valid[g] >= 4) {
@@ -594,15 +602,15 @@ enum Variant {
     kRegStaged = 1,     // FusedTile: register-staged loads, 256x256, any dtype; `vec` picks the load path
     kDirect64x256 = 0,  // Dma16 BK 64, 256x256 (fp16/bf16)
     kDirect32x256 = 2,  // Dma16 BK 32, 256x256
-    kStaged64x256 = 3,  // Stg16: the Dma16 pipeline staged through VGPRs (aligned rows)
     kDirect64x128 = 4,  // Dma16 BK 64, 256x128
     kDirect64x256W8 = 5,  // Dma16 BK 64, 256x256, 8 waves (two per SIMD)
     kDirect32x128Occ2 = 6,  // Dma16 BK 32, 256x128, two workgroups per CU
 };
 
-// Returns the launcher of the fused kernel for (DT, act, variant); defined in
-// the per-dtype instantiation unit.
+// Returns the launcher of the fused kernel for (DT, act, variant, residual);
+// defined in the per-dtype instantiation unit.  The register-staged kernels
+// test a.R at run time; the direct ones are compiled with or without it.
 template <int DT>
-fused_launcher pick_fused_for(int act, bool vec, int variant);
+fused_launcher pick_fused_for(int act, bool vec, int variant, bool residual);
 
 }  // namespace fl

@@ -62,10 +62,10 @@ int cu_count() {
 
 // The fused kernels of each dtype are compiled in their own translation unit
 // (fl_fused_inst.hip built once per dtype) so the build runs in parallel.
-fl::fused_launcher pick_fused(int dtype, int act, bool vec, int variant) {
-    if (dtype == FL_F32) return fl::pick_fused_for<FL_F32>(act, vec, variant);
-    if (dtype == FL_F16) return fl::pick_fused_for<FL_F16>(act, vec, variant);
-    return fl::pick_fused_for<FL_BF16>(act, vec, variant);
+fl::fused_launcher pick_fused(int dtype, int act, bool vec, int variant, bool residual) {
+    if (dtype == FL_F32) return fl::pick_fused_for<FL_F32>(act, vec, variant, residual);
+    if (dtype == FL_F16) return fl::pick_fused_for<FL_F16>(act, vec, variant, residual);
+    return fl::pick_fused_for<FL_BF16>(act, vec, variant, residual);
 }
 
 struct TileShape {
@@ -75,10 +75,9 @@ struct TileShape {
 
 // Kernel and tile for a problem.  tile_cfg: 0 automatic, 1 256x256, 2 256x128
 // (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
-// (fp16/bf16), 5 the direct pipeline staged through VGPRs (fp16/bf16, needs
-// aligned rows; checked at launch), 6 256x256 direct with 8 waves
-// (fp16/bf16), 7 256x128 with 32-deep K stages, two workgroups per CU
-// (fp16/bf16).  fp32 always runs the register-staged kernel.
+// (fp16/bf16), 5 256x256 direct with 8 waves (fp16/bf16), 6 256x128 with
+// 32-deep K stages, two workgroups per CU (fp16/bf16).  fp32 always runs the
+// register-staged kernel.
 // Automatic fp16/bf16 choice: the width (256 or 128) with the smaller
 // waves * relative tile time, a 256x128 tile taking 0.55 of a 256x256 one;
 // ties go to 256, which runs the 8-wave kernel (1.5-14% faster than the
@@ -90,9 +89,9 @@ struct TileShape {
 // where 256x256 was (+5% at 8192^2 x 512, -3% at 1024).
 fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 7) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
-        if (cfg == 2 || cfg == 7) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
+        if (cfg == 2 || cfg == 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
         t = {256, 256, fl::kRegStaged};
         return FL_OK;
     }
@@ -101,9 +100,8 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     case 2: t = {256, 128, fl::kDirect64x128}; return FL_OK;
     case 3: t = {256, 256, fl::kRegStaged}; return FL_OK;
     case 4: t = {256, 256, fl::kDirect32x256}; return FL_OK;
-    case 5: t = {256, 256, fl::kStaged64x256}; return FL_OK;
-    case 6: t = {256, 256, fl::kDirect64x256W8}; return FL_OK;
-    case 7: t = {256, 128, fl::kDirect32x128Occ2}; return FL_OK;
+    case 5: t = {256, 256, fl::kDirect64x256W8}; return FL_OK;
+    case 6: t = {256, 128, fl::kDirect32x128Occ2}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
@@ -145,8 +143,9 @@ fl_status check_dims(int64_t M, int64_t N, int64_t K) {
 }
 
 // Shared validation of the GEMM-shaped entry points.
-fl_status validate_gemm(const void *A, const void *B, const void *bias, const void *Y, const void *out, int64_t M,
-                        int64_t N, int64_t K, int act, int dtype, const fl_options *opt) {
+fl_status validate_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y,
+                        const void *out, int64_t M, int64_t N, int64_t K, int act, int dtype,
+                        const fl_options *opt) {
     if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", act);
     fl_status s = check_dims(M, N, K);
@@ -172,7 +171,7 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
     if (!out && o_bytes) return fail(FL_ERR_INVALID_ARG, "out is NULL");
     if (act == FL_ACT_GLU && !Y && o_bytes) return fail(FL_ERR_INVALID_ARG, "the gate needs Y");
     if (act != FL_ACT_GLU && Y) return fail(FL_ERR_INVALID_ARG, "Y is only used by the gate (FL_ACT_GLU)");
-    const void *ptrs[5] = {A, B, bias, Y, out};
+    const void *ptrs[6] = {A, B, bias, R, Y, out};
     for (const void *p : ptrs)
         if (p && !aligned(p, es)) return fail(FL_ERR_INVALID_ARG, "pointer %p is not aligned to the element size", p);
     if (overlaps(out, o_bytes, A, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
@@ -180,11 +179,13 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
     if (overlaps(out, o_bytes, bias, bias_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps bias");
     if (Y && Y != out && overlaps(out, o_bytes, Y, o_bytes))
         return fail(FL_ERR_INVALID_ARG, "Y partially overlaps out (only Y == out is allowed)");
+    if (R && R != out && overlaps(out, o_bytes, R, o_bytes))
+        return fail(FL_ERR_INVALID_ARG, "R partially overlaps out (only R == out is allowed)");
     return FL_OK;
 }
 
-fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M, int64_t N,
-                      int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
+fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
+                      int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
@@ -196,12 +197,14 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     // The direct-to-LDS kernels take any alignment; the register-staged
     // kernels need 16-byte aligned rows for their vector path.
     const bool aligned_rows = (K % vec == 0) && (N % vec == 0) && aligned(A, 16) && aligned(B, 16) &&
-                              aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16));
+                              aligned(out, 16) && (!bias || aligned(bias, 16)) && (!Y || aligned(Y, 16)) &&
+                              (!R || aligned(R, 16));
     fl::GemmArgs a;
     a.A = A;
     a.B = B;
     a.bias = bias;
     a.Y = Y;
+    a.R = R;
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
@@ -218,10 +221,8 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
     }
-    if (t.variant == fl::kStaged64x256 && !aligned_rows)
-        return fail(FL_ERR_UNSUPPORTED, "tile_cfg 5 needs 16-byte aligned rows");
     const bool use_vec = t.variant != fl::kRegStaged || aligned_rows;
-    pick_fused(dtype, act, use_vec, t.variant)(a, grid, static_cast<hipStream_t>(stream));
+    pick_fused(dtype, act, use_vec, t.variant, R != nullptr)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
 }
 
@@ -233,9 +234,19 @@ fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias, con
                              int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream,
                              const fl_options *opt) {
     clear_error();
-    fl_status s = validate_gemm(A, B, bias, Y, out, M, N, K, act, dtype, opt);
+    fl_status s = validate_gemm(A, B, bias, nullptr, Y, out, M, N, K, act, dtype, opt);
     if (s != FL_OK) return s;
-    return launch_gemm(A, B, bias, Y, out, M, N, K, act, dtype, stream, opt);
+    return launch_gemm(A, B, bias, nullptr, Y, out, M, N, K, act, dtype, stream, opt);
+}
+
+fl_status fl_fused_linear_residual(const void *A, const void *B, const void *bias, const void *R, const void *Y,
+                                   void *out, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
+                                   void *stream, const fl_options *opt) {
+    clear_error();
+    if (!R && M > 0 && N > 0) return fail(FL_ERR_INVALID_ARG, "R is NULL (use fl_fused_linear without a residual)");
+    fl_status s = validate_gemm(A, B, bias, R, Y, out, M, N, K, act, dtype, opt);
+    if (s != FL_OK) return s;
+    return launch_gemm(A, B, bias, R, Y, out, M, N, K, act, dtype, stream, opt);
 }
 
 fl_status fl_fused_linear(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M,
@@ -246,9 +257,9 @@ fl_status fl_fused_linear(const void *A, const void *B, const void *bias, const 
 fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,
                   void *stream) {
     clear_error();
-    fl_status s = validate_gemm(A, B, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, nullptr);
+    fl_status s = validate_gemm(A, B, nullptr, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, nullptr);
     if (s != FL_OK) return s;
-    return launch_gemm(A, B, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, stream, nullptr);
+    return launch_gemm(A, B, nullptr, nullptr, nullptr, X, M, N, K, FL_ACT_NONE, dtype, stream, nullptr);
 }
 
 fl_status fl_bias_add(void *X, const void *bias, int64_t M, int64_t N, fl_dtype dtype, void *stream) {

@@ -5,8 +5,9 @@ holds none of the method's arithmetic.  The same bytes feed the device path
 and the FP64 oracle.
 
 Recipe: ``numpy.random.default_rng(seed)`` (PCG64), draws in float64 in the
-order A, B, bias, Y; A and B ~ N(0, 1/K) (1/K is the variance, so the standard
-deviation is K**-0.5), bias ~ N(0, bias_var), Y ~ U(-1, 1) (gate only); each
+order A, B, bias, Y, R; A and B ~ N(0, 1/K) (1/K is the variance, so the standard
+deviation is K**-0.5), bias ~ N(0, bias_var), Y ~ U(-1, 1) (gate only), R ~
+N(0, 1) (residual workloads only); each
 array is then stored in the dtype with round-to-nearest-even (numpy's cast for
 fp32/fp16, torch's fp32->bf16 cast for bf16).  Storage: fp32 as float32, fp16
 as float16, bf16 as the uint16 bit pattern.
@@ -30,6 +31,7 @@ class Workload:
     act: str
     bias_var: float = 1.0
     seed: int = 0
+    residual: bool = False
 
     @property
     def flops(self) -> int:
@@ -49,6 +51,8 @@ WORKLOADS = {w.name: w for w in [
     Workload("glu_f16_1024x21568x256", 1024, 21568, 256, "f16", "glu"),
     Workload("glu_f16_1024x21568x512", 1024, 21568, 512, "f16", "glu"),
     Workload("glu_f16_1024x21568x1024", 1024, 21568, 1024, "f16", "glu"),
+    # FFN down-projection with the residual added in the epilogue (no activation)
+    Workload("residual_bf16_8192x4096x14336", 8192, 4096, 14336, "bf16", "none", residual=True),
 ]}
 
 
@@ -65,24 +69,27 @@ def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def draw(M, N, K, dtype, act, bias_var=1.0, seed=0, with_bias=True):
-    """Return dict(A, B, bias, Y) of raw storage arrays (Y None unless gate)."""
+def draw(M, N, K, dtype, act, bias_var=1.0, seed=0, with_bias=True, residual=False):
+    """Return dict(A, B, bias, Y, R) of raw storage arrays (Y None unless
+    gate, R None unless residual)."""
     rng = np.random.default_rng(seed)
     sd = 1.0 / np.sqrt(K) if K > 0 else 1.0
     A = rng.standard_normal((M, K)) * sd
     B = rng.standard_normal((K, N)) * sd
     bias = rng.standard_normal(N) * np.sqrt(bias_var) if with_bias else None
     Y = rng.uniform(-1.0, 1.0, (M, N)) if act == "glu" else None
+    R = rng.standard_normal((M, N)) if residual else None
     return {
         "A": to_storage(A, dtype),
         "B": to_storage(B, dtype),
         "bias": None if bias is None else to_storage(bias, dtype),
         "Y": None if Y is None else to_storage(Y, dtype),
+        "R": None if R is None else to_storage(R, dtype),
     }
 
 
 def draw_workload(w: Workload, with_bias=True):
-    return draw(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed, with_bias)
+    return draw(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed, with_bias, w.residual)
 
 
 def draw_integer(M, N, K, dtype, act, seed=0, amax=2, bias_max=4):
@@ -101,4 +108,5 @@ def draw_integer(M, N, K, dtype, act, seed=0, amax=2, bias_max=4):
         "B": to_storage(B, dtype),
         "bias": to_storage(bias, dtype),
         "Y": None if Y is None else to_storage(Y, dtype),
+        "R": None,
     }

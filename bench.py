@@ -103,7 +103,7 @@ def cpu_baseline(w, d, target_s):
     while True:
         rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+        oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, R=d["R"])
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or nrows >= w.M:
             break
@@ -175,7 +175,7 @@ def main():
             t = t.view(torch.int16).view(torch.bfloat16)
         return t.to("cuda")
 
-    A, B, bias, Y = dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["Y"])
+    A, B, bias, Y, R = dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["Y"]), dev(d["R"])
     out = torch.empty((w.M, w.N), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
     opts = {}
@@ -191,7 +191,7 @@ def main():
               "fused_linear_stg16_kernel" if args.tile_cfg == 5 else "fused_linear_dma16_kernel")
 
     def step():
-        fl.fused_linear(A, B, bias, Y, act=w.act, out=out, **opts)
+        fl.fused_linear(A, B, bias, Y, act=w.act, out=out, R=R, **opts)
 
     # The shader clock ramps up over the first ~100 ms of load; time the
     # sustained state.  These untimed steps precede the W warm-up steps.
@@ -215,7 +215,8 @@ def main():
     achieved = flops / (ms_event * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     es = ES[w.dtype]
-    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * (2 if w.act == "glu" else 1)) * es
+    mn_arrays = 1 + (w.act == "glu") + w.residual  # out, Y, R
+    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * mn_arrays) * es
 
     result = {
         "metric": METRIC,
@@ -230,9 +231,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s)" % (
-            w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else ""),
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "io_dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s%s)" % (
+            w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else "", ", R ~ N(0,1)" if w.residual else ""),
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "residual": w.residual,
+                   "io_dtype": w.dtype,
                    "accumulate": "f32", "tile": f"{bm}x{bn}", "tiles": tiles_m * tiles_n,
                    "tile_cfg": args.tile_cfg, "group_m": args.group_m or 4, "persistent": bool(args.persistent)},
         "frac_of_peak": round(tflops / peak, 4),
@@ -242,7 +244,9 @@ def main():
                      "algorithmic_bytes": alg_bytes},
     }
 
-    if not args.no_unfused:
+    if w.residual:
+        result["unfused"] = None  # no elementwise residual pass in the unfused chain
+    elif not args.no_unfused:
         X = torch.empty_like(out)
 
         def chain():

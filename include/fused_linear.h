@@ -96,17 +96,15 @@ typedef struct {
                            compute units; short reductions (K <= 3072 for a
                            256x128 choice, K <= 512 for 256x256) whose
                            256x128 grid fills two workgroups per compute unit
-                           run as 7.  1 = 256x256 direct, 4 waves
+                           run as 6.  1 = 256x256 direct, 4 waves
                            (fp16/bf16; fp32 as 0); 2 = 256x128 direct
                            (fp16/bf16 only); 3 = register-staged 256x256 for
                            any dtype; 4 = 256x256 direct with 32-deep K
-                           stages; 5 = the direct pipeline with its copies
-                           staged through registers (fp16/bf16, K and N
-                           multiples of 8, 16-byte aligned pointers);
-                           6 = 256x256 direct with 8 waves (two per SIMD,
-                           128x64 each; fp16/bf16; fp32 as 0); 7 = 256x128
-                           direct with 32-deep K stages and two workgroups
-                           per compute unit (fp16/bf16 only).  Every
+                           stages; 5 = 256x256 direct with 8 waves (two per
+                           SIMD, 128x64 each; fp16/bf16; fp32 as 0);
+                           6 = 256x128 direct with 32-deep K stages and two
+                           workgroups per compute unit (fp16/bf16 only).
+                           Every
                            variant gives bit-identical results.  Any other
                            value, or a variant the problem does not allow,
                            is FL_ERR_UNSUPPORTED. */
@@ -141,6 +139,27 @@ fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias,
                              const void *Y, void *out, int64_t M, int64_t N,
                              int64_t K, fl_act act, fl_dtype dtype,
                              void *stream, const fl_options *opt);
+
+/*
+ * out = act(A@B + bias + R): the fused linear layer with a same-shape
+ * residual R added to the accumulator after the K reduction, before the
+ * activation ("Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)",
+ * "Variants": the residual tile is loaded after the K loop under the same
+ * mask as the store).  In fp32: (acc + bias) + R, then act, then one
+ * rounding to dtype.
+ *   R     (M,N) device pointer in dtype, row stride N; must not be NULL
+ *         (unless M*N == 0).  R may be exactly out (each element is read
+ *         before it is written) but must not partially overlap it.
+ *   Every other argument, option and error as fl_fused_linear_ex; act may
+ *   be any activation, including the gate (then Y is required too:
+ *   out = X + X*Y with X = A@B + bias + R).
+ */
+fl_status fl_fused_linear_residual(const void *A, const void *B,
+                                   const void *bias, const void *R,
+                                   const void *Y, void *out, int64_t M,
+                                   int64_t N, int64_t K, fl_act act,
+                                   fl_dtype dtype, void *stream,
+                                   const fl_options *opt);
 
 /* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
  * traffic": GEMM writes X, a bias pass reads and writes it, an activation

@@ -113,16 +113,16 @@ def test_tile_grid(lib):
     assert fl.tile_grid(4096, 4096, 4096, BF16, tile_cfg=2) == (256, 128, 16, 32)
     with pytest.raises(fl.FusedLinearError):
         fl.tile_grid(64, 64, 64, F32, tile_cfg=2)
-    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=6) == (256, 256, 16, 16)
-    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=7) == (256, 128, 16, 32)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=5) == (256, 256, 16, 16)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=6) == (256, 128, 16, 32)
     # short reductions whose 256x128 grid fills two workgroups per CU
     assert fl.tile_grid(1024, 21568, 256, F16) == (256, 128, 4, 169)
     assert fl.tile_grid(8192, 8192, 512, F16) == (256, 128, 32, 64)
     assert fl.tile_grid(8192, 8192, 1024, F16) == (256, 256, 32, 32)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F32, tile_cfg=7)
+        fl.tile_grid(64, 64, 64, F32, tile_cfg=6)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=8)
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=7)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
@@ -146,3 +146,28 @@ def test_host_tile_map_with_xcd_step_is_a_bijection(lib, tm, tn, g):
     for x in range(min(8, n)):
         qs = [pos[tiles[p]] for p in range(x, n, 8)]
         assert qs == list(range(qs[0], qs[0] + len(qs)))
+
+
+R_P = 0x60000000
+
+
+def _res(lib, R=R_P, Y=None, out=OUT_P, act=RELU, M=64, N=64, K=64, dt=F16):
+    return lib.fl_fused_linear_residual(A_P, B_P, BIAS_P, R, Y, out, M, N, K, act, dt, None, None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(R=None), INVALID, "R is NULL"),
+    (dict(R=R_P + 1), INVALID, "not aligned"),
+    (dict(R=OUT_P + 2), INVALID, "R partially overlaps out"),
+    (dict(out=R_P, R=R_P + 64), INVALID, "R partially overlaps out"),
+    (dict(act=GLU), INVALID, "the gate needs Y"),
+    (dict(Y=Y_P), INVALID, "Y is only used by the gate"),
+])
+def test_residual_rejects_bad_arguments(lib, kwargs, status, msg):
+    assert _res(lib, **kwargs) == status
+    assert msg in lib.fl_last_error().decode()
+
+
+def test_residual_degenerate_shapes_return_ok(lib):
+    assert _res(lib, R=None, M=0) == OK
+    assert _res(lib, R=None, N=0) == OK
