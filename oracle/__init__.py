@@ -67,6 +67,11 @@ def _load():
             lib.orc_fused_linear.restype = c_int
             lib.orc_unfused_chain.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
             lib.orc_unfused_chain.restype = c_int
+            lib.orc_fused_linear_quant.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, c_int,
+                                                   ctypes.c_float, p, i64, c_int, p]
+            lib.orc_fused_linear_quant.restype = c_int
+            lib.orc_quantize.argtypes = [c_int, p, i64, p]
+            lib.orc_dequantize.argtypes = [c_int, p, i64, p]
             lib.orc_element.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, i64, i64, p]
             lib.orc_element.restype = c_int
             lib.orc_decode.argtypes = [c_int, p, i64, p]
@@ -132,6 +137,73 @@ def fused_linear(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads
     ``rows`` selects output rows (the result then has len(rows) rows).
     ``want_x`` also returns the unrounded FP64 epilogue value."""
     return _call("orc_fused_linear", A, B, bias, Y, act, dtype, rows, threads, want_x, R)
+
+
+QFORMATS = {"fp8_e4m3": 0, "int8": 1}
+
+
+def fused_linear_quant(A, B, bias, Y=None, act="relu", dtype="f16", qfmt="fp8_e4m3", scale=1.0, rows=None,
+                       threads=None, want_u=False):
+    """Quantized output: uint8 codes of Q(fp32(fp32(act(A@B + bias)) * scale)),
+    Q = saturating RNE to OCP FP8 E4M3 or RNE + clamp to int8 (int8 codes as
+    their two's-complement bytes).  ``want_u`` also returns the binary32
+    value Q decides on, as float64."""
+    lib = _load()
+    A, B, bias, Y = (_raw(x, dtype) for x in (A, B, bias, Y))
+    M, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != K:
+        raise ValueError("A is (M,K) and B is (K,N)")
+    if act == "glu" and (Y is None or Y.shape != (M, N)):
+        raise ValueError("the gate needs Y of shape (M,N)")
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = M if rows_arr is None else rows_arr.size
+    out = np.empty((nrows, N), dtype=np.uint8)
+    u = np.empty((nrows, N), dtype=np.float64) if want_u else None
+    st = lib.orc_fused_linear_quant(DTYPES[dtype], ACTS[act], _ptr(A), _ptr(B), _ptr(bias), _ptr(Y), _ptr(out),
+                                    M, N, K, QFORMATS[qfmt], float(scale), _ptr(rows_arr), nrows,
+                                    int(threads or 0), _ptr(u))
+    if st != 0:
+        raise RuntimeError(f"orc_fused_linear_quant failed with status {st}")
+    return (out, u) if want_u else out
+
+
+def quantize(u, qfmt):
+    """uint8 codes of saturating RNE FP8 E4M3 (or RNE + clamp int8) of float64 values."""
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    out = np.empty(u.shape, dtype=np.uint8)
+    _load().orc_quantize(QFORMATS[qfmt], _ptr(u), u.size, _ptr(out))
+    return out
+
+
+def dequantize(codes, qfmt):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().orc_dequantize(QFORMATS[qfmt], _ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def compare_quant(dev_codes, ref_codes, ref_u, qfmt, rel=1e-4, abs_=1e-6):
+    """Quantized parity: codes equal, except where the oracle's binary32
+    value u lies within rel*|u| + abs_ of the point where Q changes its
+    decision (then the neighbouring code is accepted too: the device's fp32
+    sum differs from the FP64 one by rounding).  Returns a dict with ok,
+    mismatches, accepted_near_boundary and the worst index."""
+    dev = np.asarray(dev_codes, dtype=np.uint8)
+    ref = np.asarray(ref_codes, dtype=np.uint8)
+    if dev.shape != ref.shape:
+        raise ValueError("shape mismatch")
+    diff = dev != ref
+    band = rel * np.abs(ref_u) + abs_
+    lo = quantize(ref_u - band, qfmt)
+    hi = quantize(ref_u + band, qfmt)
+    ok_alt = diff & ((dev == lo) | (dev == hi))
+    bad = diff & ~ok_alt
+    worst = None
+    if bad.any():
+        worst = tuple(int(v) for v in np.argwhere(bad)[0])
+    return {"ok": not bad.any(), "mismatches": int(bad.sum()), "accepted_near_boundary": int(ok_alt.sum()),
+            "worst": worst}
 
 
 def unfused_chain(A, B, bias, Y=None, act="relu", dtype="f32", rows=None, threads=None):

@@ -30,7 +30,9 @@
  *     X = A@B + bias, out = X + X*Y.
  *   - "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants":
  *     a same-shape residual tile is added to the accumulator after the K
- *     loop, before the activation.
+ *     loop, before the activation; and the quantized output: a scale and a
+ *     clamp applied to the epilogue value, then a cast to int8 or fp8
+ *     before the one store (see orc_fused_linear_quant).
  *   - GELU: the pages name it as a fusable activation but print no formula;
  *     this file uses the tanh form of Hendrycks & Gimpel (2016),
  *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with libm tanh.
@@ -139,6 +141,66 @@ int orc_encode(int dtype, const double *src, int64_t n, void *dst) {
     return 0;
 }
 
+/* ------------------------------------------------------ quantized output */
+
+enum { ORC_Q_FP8_E4M3 = 0, ORC_Q_INT8 = 1 };
+
+/* OCP FP8 E4M3 ("e4m3fn": exponent bias 7, 3 mantissa bits, subnormals,
+ * largest finite 448, no infinities, S.1111.111 = NaN).  Saturating: |u| >=
+ * 448 gives +-448; otherwise round to nearest, ties to even, on the format's
+ * grid (subnormal quantum 2^-9). */
+static uint8_t enc_e4m3(double u) {
+    if (isnan(u)) return 0x7f;
+    if (u >= 448.0) return 0x7e;
+    if (u <= -448.0) return 0xfe;
+    double r = round_fmt(u, 4, -6, 8); /* |r| <= 448 here: 464 is the first tie above */
+    return (uint8_t)enc_small(r, 4, 3);
+}
+
+static double dec_e4m3(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(m + 8), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* int8: round to nearest, ties to even, then clamp to [-128, 127]. */
+static uint8_t enc_i8(double u) {
+    double r = rint(u);
+    if (r > 127.0) r = 127.0;
+    if (r < -128.0) r = -128.0;
+    return (uint8_t)(int8_t)r;
+}
+
+static uint8_t quantize(int qfmt, double u) { return qfmt == ORC_Q_INT8 ? enc_i8(u) : enc_e4m3(u); }
+
+static double dequantize(int qfmt, uint8_t c) { return qfmt == ORC_Q_INT8 ? (double)(int8_t)c : dec_e4m3(c); }
+
+int orc_quantize(int qfmt, const double *src, int64_t n, uint8_t *dst) {
+    if (qfmt < 0 || qfmt > 1 || n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = quantize(qfmt, src[i]);
+    return 0;
+}
+
+int orc_dequantize(int qfmt, const uint8_t *src, int64_t n, double *dst) {
+    if (qfmt < 0 || qfmt > 1 || n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i) dst[i] = dequantize(qfmt, src[i]);
+    return 0;
+}
+
+/* The value a quantized store decides on, in the kernel's precision: the
+ * epilogue value v rounded to binary32, times the scale rounded to binary32
+ * (the product of two binary32 numbers is exact in FP64, so the second
+ * rounding is that of a binary32 multiply). */
+static double quant_input(double v, float scale) {
+    float t = (float)v;
+    return (double)(float)((double)t * (double)scale);
+}
+
 /* ------------------------------------------------------------ activation */
 
 double orc_gelu_tanh(double x) {
@@ -192,7 +254,8 @@ static int check_args(int dtype, int act, const void *A, const void *B,
 static int run(int dtype, int act, const void *A, const void *B,
                const void *bias, const void *R, const void *Y, void *out,
                int64_t M, int64_t N, int64_t K, const int64_t *rows,
-               int64_t nrows, int nthreads, double *x_out, int unfused) {
+               int64_t nrows, int nthreads, double *x_out, int unfused,
+               int qfmt, float scale) {
     if (check_args(dtype, act, A, B, Y, out, M, N, K)) return 1;
     if (unfused && R) return 1; /* the chain has no residual stage */
     if (!rows) nrows = M;
@@ -245,6 +308,12 @@ static int run(int dtype, int act, const void *A, const void *B,
                         /* stage 3: the activation pass */
                         v = apply_act(act, tmp[0], y);
                     }
+                    if (qfmt >= 0) {
+                        double u = quant_input(v, scale);
+                        if (x_out) x_out[r * N + j] = u;
+                        ((uint8_t *)out)[r * N + j] = quantize(qfmt, u);
+                        continue;
+                    }
                     if (x_out) x_out[r * N + j] = v;
                     enc_one(dtype, v, out, r * N + j);
                 }
@@ -262,14 +331,30 @@ int orc_fused_linear(int dtype, int act, const void *A, const void *B,
                      const void *bias, const void *R, const void *Y, void *out,
                      int64_t M, int64_t N, int64_t K, const int64_t *rows,
                      int64_t nrows, int nthreads, double *x_out) {
-    return run(dtype, act, A, B, bias, R, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0);
+    return run(dtype, act, A, B, bias, R, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0, -1, 1.0f);
+}
+
+/*
+ * Quantized output: out (nrows x N bytes) = Q(fp32(fp32(act(A@B + bias)) *
+ * scale)), Q = saturating RNE to FP8 E4M3 (qfmt 0) or RNE + clamp to int8
+ * (qfmt 1).  The activation and everything before it are as in
+ * orc_fused_linear (FP64, no residual); x_out, when not NULL, receives the
+ * binary32 value Q decides on.
+ */
+int orc_fused_linear_quant(int dtype, int act, const void *A, const void *B,
+                           const void *bias, const void *Y, void *out,
+                           int64_t M, int64_t N, int64_t K, int qfmt,
+                           float scale, const int64_t *rows, int64_t nrows,
+                           int nthreads, double *x_out) {
+    if (qfmt < 0 || qfmt > 1 || !isfinite(scale)) return 1;
+    return run(dtype, act, A, B, bias, NULL, Y, out, M, N, K, rows, nrows, nthreads, x_out, 0, qfmt, scale);
 }
 
 int orc_unfused_chain(int dtype, int act, const void *A, const void *B,
                       const void *bias, const void *Y, void *out, int64_t M,
                       int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
                       int nthreads, double *x_out) {
-    return run(dtype, act, A, B, bias, NULL, Y, out, M, N, K, rows, nrows, nthreads, x_out, 1);
+    return run(dtype, act, A, B, bias, NULL, Y, out, M, N, K, rows, nrows, nthreads, x_out, 1, -1, 1.0f);
 }
 
 /* Single output element (i, j), FP64, unrounded:

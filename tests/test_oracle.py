@@ -377,3 +377,101 @@ def test_residual_fp64_value_matches_numpy():
     A, B, bias, R64 = (oracle.decode(x, "f32") for x in (d["A"], d["B"], d["bias"], R))
     _, x = oracle.fused_linear(d["A"], d["B"], d["bias"], act="none", dtype="f32", want_x=True, R=R)
     np.testing.assert_allclose(x, A @ B + bias[None, :] + R64, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------- quantized output
+# "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a scale
+# and a clamp applied to the epilogue value, cast to int8 / fp8 before the
+# store.  FP8 is OCP E4M3 (largest finite 448, no infinities).
+
+def test_e4m3_decode_every_code_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.dequantize(codes, "fp8_e4m3")
+    exp = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    assert np.array_equal(got[~np.isnan(got)], exp[~np.isnan(exp)])
+    assert got[0x7e] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+
+
+def test_e4m3_encode_matches_torch_within_range():
+    rng = np.random.default_rng(4)
+    mag = 2.0 ** rng.uniform(-12, np.log2(440.0), 200000)
+    x = np.concatenate([mag * rng.choice([-1.0, 1.0], mag.size),
+                        # exact ties on the grid: 1 + 1/16 -> 1, 1 + 3/16 -> 1.25, subnormal ties
+                        [1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 0.0, 440.0, 447.9]])
+    got = oracle.quantize(x, "fp8_e4m3")
+    exp = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch casts from float32: compare on the float32 values, and on the
+    # float64 ones where they are float32 already (the ties above are)
+    x32 = x.astype(np.float32).astype(np.float64)
+    assert np.array_equal(oracle.quantize(x32, "fp8_e4m3"), exp)
+    same = x32 == x
+    assert same[-9:].all()
+    assert np.array_equal(got[same], exp[same])
+
+
+def test_e4m3_saturates_instead_of_nan():
+    x = np.array([448.0, 449.0, 464.0, 1e30, -448.0, -1e30, 447.0])
+    assert oracle.quantize(x, "fp8_e4m3").tolist() == [0x7e, 0x7e, 0x7e, 0x7e, 0xfe, 0xfe, 0x7e]
+
+
+def test_int8_matches_numpy_rint_and_clip():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(100000) * 100.0, np.arange(-130, 131) + 0.5, [-128.5, 127.5, 1e9, -1e9]])
+    got = oracle.quantize(x, "int8").view(np.int8)
+    exp = np.clip(np.rint(x), -128, 127).astype(np.int8)
+    assert np.array_equal(got, exp)
+    assert oracle.quantize(np.array([2.5, 3.5, -2.5, -3.5]), "int8").view(np.int8).tolist() == [2, 4, -2, -4]
+    assert np.array_equal(oracle.dequantize(np.arange(256, dtype=np.uint8), "int8"),
+                          np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("qfmt", ["fp8_e4m3", "int8"])
+def test_quant_integer_inputs_brute_force(dtype, act, qfmt):
+    """Exact integers with a power-of-two scale: every intermediate is exact,
+    so the codes follow from int64 arithmetic and the format's own cast."""
+    M, N, K = 37, 53, 24
+    d = synth.draw_integer(M, N, K, dtype, act, seed=31, amax=1, bias_max=3)
+    A, B, bias = (oracle.decode(d[k], dtype).astype(np.int64) for k in ("A", "B", "bias"))
+    X = A @ B + bias[None, :]
+    if act == "relu":
+        X = np.maximum(X, 0)
+    elif act == "glu":
+        X = X + X * oracle.decode(d["Y"], dtype).astype(np.int64)
+    scale = 0.25 if qfmt == "fp8_e4m3" else 4.0
+    u = X.astype(np.float64) * scale
+    if qfmt == "fp8_e4m3":
+        exp = torch.from_numpy(u.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        exp = np.clip(np.rint(u), -128, 127).astype(np.int8).view(np.uint8)
+    got, gu = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, qfmt=qfmt,
+                                        scale=scale, want_u=True)
+    assert np.array_equal(gu, u)
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
+def test_quant_value_is_the_binary32_epilogue_times_scale(act):
+    d = synth.draw(20, 30, 40, "bf16", act, seed=8)
+    scale = 7.3
+    _, x = oracle.fused_linear(d["A"], d["B"], d["bias"], act=act, dtype="bf16", want_x=True)
+    _, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], act=act, dtype="bf16", qfmt="fp8_e4m3",
+                                     scale=scale, want_u=True)
+    exp = (x.astype(np.float32) * np.float32(scale)).astype(np.float64)
+    assert np.array_equal(u, exp)
+
+
+def test_compare_quant_flags_off_by_one_codes_away_from_boundaries():
+    d = synth.draw(64, 96, 64, "f16", "relu", seed=9)
+    codes, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], act="relu", dtype="f16", qfmt="fp8_e4m3",
+                                         scale=20.0, want_u=True)
+    assert oracle.compare_quant(codes, codes, u, "fp8_e4m3")["ok"]
+    bumped = codes.copy()
+    i, j = np.argwhere((codes > 0x08) & (codes < 0x70))[5]
+    bumped[i, j] += 1
+    assert not oracle.compare_quant(bumped, codes, u, "fp8_e4m3")["ok"]
+    # scale applied twice, or the activation after the scale for a negative scale: flagged
+    twice = oracle.quantize(u * 20.0, "fp8_e4m3")
+    assert not oracle.compare_quant(twice, codes, u, "fp8_e4m3")["ok"]
