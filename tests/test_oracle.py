@@ -398,7 +398,7 @@ def test_e4m3_encode_matches_torch_within_range():
     mag = 2.0 ** rng.uniform(-12, np.log2(440.0), 200000)
     x = np.concatenate([mag * rng.choice([-1.0, 1.0], mag.size),
                         # exact ties on the grid: 1 + 1/16 -> 1, 1 + 3/16 -> 1.25, subnormal ties
-                        [1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 0.0, 440.0, 447.9]])
+                        [1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 0.0, 440.0, 447.5]])
     got = oracle.quantize(x, "fp8_e4m3")
     exp = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     # torch casts from float32: compare on the float32 values, and on the
