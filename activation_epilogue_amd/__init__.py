@@ -10,6 +10,8 @@ not been built, importing works but every call raises ``LibraryNotBuilt``.
 Entry points (same names as the C ABI, without the ``fl_`` prefix):
   fused_linear(A, B, bias=None, Y=None, act="relu", out=None, R=None, **options)
                                           # R: residual -> fl_fused_linear_residual
+  fused_linear_quant(A, B, bias=None, Y=None, act="relu", scale=1.0, qfmt="fp8_e4m3", out=None, **options)
+                                          # uint8 codes of Q(scale * act(A@B + bias))
   gemm(A, B, X=None)                      # unfused step 1: X = A@B
   bias_add(X, bias)                       # unfused step 2: X += bias (in place)
   activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
@@ -25,8 +27,8 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
-EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_gemm", "fl_bias_add",
-           "fl_activation",
+EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant", "fl_gemm",
+           "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
 
@@ -64,13 +66,15 @@ def load_library():
     lib.fl_fused_linear_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp, ctypes.POINTER(Options)]
     lib.fl_fused_linear_residual.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
                                              ctypes.POINTER(Options)]
+    lib.fl_fused_linear_quant.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, c_int, c_int, c_int, vp,
+                                          ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
     lib.fl_activation.argtypes = [vp, vp, vp, i64, i64, c_int, c_int, vp]
     lib.fl_tile_grid.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(Options), P_i32, P_i32, P_i32, P_i32]
     lib.fl_tile_of_program.argtypes = [i32, i32, i32, i32, i32, i32, P_i32, P_i32]
-    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_gemm", "fl_bias_add",
-              "fl_activation", "fl_tile_grid", "fl_tile_of_program"):
+    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant", "fl_gemm",
+              "fl_bias_add", "fl_activation", "fl_tile_grid", "fl_tile_of_program"):
         getattr(lib, f).restype = c_int
     lib.fl_status_string.argtypes = [c_int]
     lib.fl_status_string.restype = ctypes.c_char_p
@@ -154,6 +158,32 @@ def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, R=None, strea
         _check(lib.fl_fused_linear_ex(*args, ctypes.byref(opt)))
     else:
         _check(lib.fl_fused_linear(*args))
+    return out
+
+
+QFORMATS = {"fp8_e4m3": 0, "int8": 1}
+
+
+def fused_linear_quant(A, B, bias=None, Y=None, act="relu", scale=1.0, qfmt="fp8_e4m3", out=None, *, stream=None,
+                       **options):
+    """One-byte codes of Q(scale * act(A@B + bias)) in one kernel
+    (fl_fused_linear_quant): Q is saturating round-to-nearest-even to OCP FP8
+    E4M3 (qfmt="fp8_e4m3") or to int8 (qfmt="int8").  A, B, bias, Y are
+    fp16 or bf16; returns out, a (M,N) uint8 tensor (the codes' bytes)."""
+    import torch
+    lib = load_library()
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError("A must be (M,K) and B (K,N)")
+    M, K = A.shape
+    N = B.shape[1]
+    dt = A.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.uint8, device=A.device)
+    opt = _options(**options)
+    _check(lib.fl_fused_linear_quant(
+        _dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(bias, "bias", dt, (N,)),
+        _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", torch.uint8, (M, N)), float(scale), M, N, K, ACTS[act],
+        _dtype_code(dt), QFORMATS[qfmt], _stream(A, stream), ctypes.byref(opt)))
     return out
 
 

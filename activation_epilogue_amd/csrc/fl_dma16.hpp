@@ -96,8 +96,10 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // the registers in half of the register file, so one workgroup's epilogue
 // and start-up overlap the other's K loop.  RES: the epilogue adds the
 // residual a.R (compiled in only where it is used, so the plain epilogue
-// keeps its registers).
-template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false>
+// keeps its registers).  QF: -1 stores the I/O dtype; FL_Q_FP8_E4M3 or
+// FL_Q_INT8 store one-byte codes of the epilogue value times a.scale.
+template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false,
+          int QF = -1>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr int BM = 256, BN = BN_, BK = BK_;
@@ -417,7 +419,8 @@ struct Dma16 {
     // write instruction touches fall in different banks).  Phase 2: each
     // lane reads 16 bytes of a row back and stores them, so a store
     // instruction writes 4 whole rows of 256 bytes (full 128-byte lines).
-    static constexpr int EPI_ROW = WN * 2 + 16;
+    static constexpr int OES = QF < 0 ? 2 : 1;  // bytes per output element
+    static constexpr int EPI_ROW = WN * OES + 16;
     static constexpr int EPI_WAVE = 128 * EPI_ROW;
     static constexpr int EPI_BYTES = WAVES * EPI_WAVE;
     static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
@@ -427,8 +430,9 @@ struct Dma16 {
         using io = Io<DT>;
         using quad_t = u32x2_t;
         const size_t o_org = (size_t)m0 * a.N + n0;
-        const size_t o_bytes = ((size_t)a.M * a.N - o_org) * 2;
-        const __amdgpu_buffer_rsrc_t rO = make_rsrc(static_cast<char *>(a.out) + o_org * 2, o_bytes);
+        const size_t o_bytes = ((size_t)a.M * a.N - o_org) * 2;  // Y and R, in the I/O dtype
+        const __amdgpu_buffer_rsrc_t rO =
+            make_rsrc(static_cast<char *>(a.out) + o_org * OES, ((size_t)a.M * a.N - o_org) * OES);
         const __amdgpu_buffer_rsrc_t rY =
             make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * 2 : nullptr, a.Y ? o_bytes : 0);
         constexpr bool has_r = RES;
@@ -486,19 +490,23 @@ struct Dma16 {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int ni = g >> 2, q = g & 3;
-                uint32_t o[4];
+                float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
                     float x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
                     if constexpr (has_r) x += base::elem_f32(rq[mi % (RA + 1)][g], e);
-                    o[e] = io::from_f32(activate<ACT>(x, y));
+                    v[e] = activate<ACT>(x, y);
                 }
-                u32x2_t w;
-                w[0] = o[0] | (o[1] << 16);
-                w[1] = o[2] | (o[3] << 16);
-                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's 128x128
-                *(FL_LDS u32x2_t *)(wbuf + r * EPI_ROW + c * 2) = w;
+                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's tile
+                if constexpr (QF < 0) {
+                    u32x2_t w;
+                    w[0] = io::from_f32(v[0]) | ((uint32_t)io::from_f32(v[1]) << 16);
+                    w[1] = io::from_f32(v[2]) | ((uint32_t)io::from_f32(v[3]) << 16);
+                    *(FL_LDS u32x2_t *)(wbuf + r * EPI_ROW + c * 2) = w;
+                } else {
+                    *(FL_LDS uint32_t *)(wbuf + r * EPI_ROW + c) = quantize4<QF>(v, a.scale);
+                }
             }
             // One row block at a time: without this the scheduler reads
             // every accumulator out of the AGPRs up front and spills.
@@ -506,20 +514,21 @@ struct Dma16 {
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
         asm volatile("" ::: "memory");
-        constexpr int CPR = WN / 8;    // 16-byte chunks per row of the wave tile
-        constexpr int RPP = 64 / CPR;  // rows per store instruction
-        constexpr int BATCH = 8;       // LDS reads issued ahead of their stores
+        constexpr int EPC = 16 / OES;       // output elements per 16-byte chunk
+        constexpr int CPR = WN / EPC;       // 16-byte chunks per row of the wave tile
+        constexpr int RPP = 64 / CPR;       // rows per store instruction
+        constexpr int BATCH = 8;            // LDS reads issued ahead of their stores
         constexpr int PASSES = 128 / RPP;
         static_assert(PASSES % BATCH == 0, "whole batches");
         const int cchunk = lane % CPR;
-        const int ccol = wn * WN + cchunk * 8;
+        const int ccol = wn * WN + cchunk * EPC;
         const int cvalid = a.N - n0 - ccol;
         const FL_LDS char *rbase = wbuf + (lane / CPR) * EPI_ROW + cchunk * 16;
         auto out_off = [&](int rr) -> uint32_t {
             const int row = wm * 128 + rr * RPP + lane / CPR;
-            return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * 2 : kOob;
+            return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * OES : kOob;
         };
-        if (cvalid >= 8) {
+        if (cvalid >= EPC) {
             // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
 #pragma unroll 1
             for (int rb = 0; rb < PASSES; rb += BATCH) {
@@ -538,9 +547,14 @@ struct Dma16 {
                 const u32x4_t v = *(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW);
                 const uint32_t off = out_off(rr);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
-                    store_elem<2>(h, rO, (off != kOob && e < cvalid) ? off + e * 2 : kOob);
+                for (int e = 0; e < EPC; ++e) {
+                    if constexpr (OES == 2) {
+                        const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+                        store_elem<2>(h, rO, (off != kOob && e < cvalid) ? off + e * 2 : kOob);
+                    } else {
+                        const uint8_t b = (uint8_t)(v[e >> 2] >> (8 * (e & 3)));
+                        __builtin_amdgcn_raw_buffer_store_b8(b, rO, (off != kOob && e < cvalid) ? off + e : kOob, 0, 0);
+                    }
                 }
             }
         }
@@ -601,9 +615,13 @@ struct Dma16 {
     }
 };
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES>
+// Look-ahead copies issued over two blocks: measured best of 1..4 on the
+// 4096^3 fp16, 8192x14336x4096 bf16 and 1024x21568x4096 fp16 shapes.
+constexpr int kCopySpread = 2;
+
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES>;
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

@@ -17,14 +17,10 @@ void launch(const GemmArgs &a, int grid, hipStream_t s) {
 
 }  // namespace
 
-// Look-ahead copies issued over two blocks: measured best of 1..4 on the
-// 4096^3 fp16, 8192x14336x4096 bf16 and 1024x21568x4096 fp16 shapes.
-constexpr int kCopySpread = 2;
-
 template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, bool RES>
 void launch_dma(const GemmArgs &a, int grid, hipStream_t s) {
     if constexpr (DT != FL_F32)
-        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES>), dim3(grid),
+        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES, -1>), dim3(grid),
                            dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
 }
 

@@ -112,6 +112,34 @@ __device__ __forceinline__ float activate(float x, float y) {
     return r;
 }
 
+// The quantized store ("Triton: Fused Matmul + Bias + ReLU (Epilogue
+// Fusion)", "Variants": scale, clamp, cast to int8/fp8 before the store):
+// four epilogue values times the scale, in fp32, packed as four one-byte
+// codes (first value in the low byte).  FP8: clamp to the largest finite
+// E4M3 value 448, then the hardware conversion (round to nearest even, OCP
+// E4M3); int8: round to nearest even, clamp to [-128, 127].
+template <int QF>
+__device__ __forceinline__ uint32_t quantize4(const float (&v)[4], float scale) {
+    float u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = v[e] * scale;
+    if constexpr (QF == FL_Q_FP8_E4M3) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = __builtin_fminf(__builtin_fmaxf(u[e], -448.0f), 448.0f);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(u[2], u[3], w, true);
+        return (uint32_t)w;
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float r = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(u[e]), -128.0f), 127.0f);
+            w |= ((uint32_t)(int)r & 0xffu) << (8 * e);
+        }
+        return w;
+    }
+}
+
 // ------------------------------------------------------------- tile order
 
 // Grouped program -> (m_tile, n_tile): bands of `group` M-tiles are swept
@@ -179,6 +207,7 @@ struct GemmArgs {
     const void *bias;  // may be null
     const void *Y;     // gate operand or null
     const void *R;     // residual (M,N) added before the activation, or null
+    float scale;       // quantized output: codes of (epilogue value) * scale
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;
@@ -612,5 +641,11 @@ enum Variant {
 // test a.R at run time; the direct ones are compiled with or without it.
 template <int DT>
 fused_launcher pick_fused_for(int act, bool vec, int variant, bool residual);
+
+// Launcher of the quantized-output kernel for (DT, act, variant, qfmt), or
+// nullptr when that variant has none; defined in the per-dtype quantized
+// instantiation unit (fp16/bf16 only).
+template <int DT>
+fused_launcher pick_quant_for(int act, int variant, int qfmt);
 
 }  // namespace fl

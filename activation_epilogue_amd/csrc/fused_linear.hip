@@ -145,7 +145,7 @@ fl_status check_dims(int64_t M, int64_t N, int64_t K) {
 // Shared validation of the GEMM-shaped entry points.
 fl_status validate_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y,
                         const void *out, int64_t M, int64_t N, int64_t K, int act, int dtype,
-                        const fl_options *opt) {
+                        const fl_options *opt, bool out_optional = false) {
     if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", act);
     fl_status s = check_dims(M, N, K);
@@ -168,7 +168,7 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
     const size_t bias_bytes = bias ? (size_t)N * es : 0;
     if (!A && a_bytes) return fail(FL_ERR_INVALID_ARG, "A is NULL");
     if (!B && b_bytes) return fail(FL_ERR_INVALID_ARG, "B is NULL");
-    if (!out && o_bytes) return fail(FL_ERR_INVALID_ARG, "out is NULL");
+    if (!out && o_bytes && !out_optional) return fail(FL_ERR_INVALID_ARG, "out is NULL");
     if (act == FL_ACT_GLU && !Y && o_bytes) return fail(FL_ERR_INVALID_ARG, "the gate needs Y");
     if (act != FL_ACT_GLU && Y) return fail(FL_ERR_INVALID_ARG, "Y is only used by the gate (FL_ACT_GLU)");
     const void *ptrs[6] = {A, B, bias, R, Y, out};
@@ -185,7 +185,8 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
 }
 
 fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
-                      int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt) {
+                      int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt,
+                      int qfmt = -1, float scale = 1.0f) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
@@ -205,6 +206,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     a.bias = bias;
     a.Y = Y;
     a.R = R;
+    a.scale = scale;
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
@@ -220,6 +222,13 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (a.persistent) {
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
+    }
+    if (qfmt >= 0) {
+        const fl::fused_launcher q = dtype == FL_F16 ? fl::pick_quant_for<FL_F16>(act, t.variant, qfmt)
+                                                     : fl::pick_quant_for<FL_BF16>(act, t.variant, qfmt);
+        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5 and 6 only");
+        q(a, grid, static_cast<hipStream_t>(stream));
+        return check_launch("fused_linear_quant");
     }
     const bool use_vec = t.variant != fl::kRegStaged || aligned_rows;
     pick_fused(dtype, act, use_vec, t.variant, R != nullptr)(a, grid, static_cast<hipStream_t>(stream));
@@ -252,6 +261,28 @@ fl_status fl_fused_linear_residual(const void *A, const void *B, const void *bia
 fl_status fl_fused_linear(const void *A, const void *B, const void *bias, const void *Y, void *out, int64_t M,
                           int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream) {
     return fl_fused_linear_ex(A, B, bias, Y, out, M, N, K, act, dtype, stream, nullptr);
+}
+
+fl_status fl_fused_linear_quant(const void *A, const void *B, const void *bias, const void *Y, void *out_q,
+                                float scale, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
+                                fl_qformat qfmt, void *stream, const fl_options *opt) {
+    clear_error();
+    if (qfmt != FL_Q_FP8_E4M3 && qfmt != FL_Q_INT8) return fail(FL_ERR_INVALID_ARG, "unknown qformat %d", (int)qfmt);
+    if (!(scale == scale) || scale - scale != 0.0f) return fail(FL_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "quantized output takes fp16 or bf16 inputs");
+    // Validate the inputs as for a 16-bit output, with out checked apart:
+    // out_q holds M*N one-byte codes and may not overlap any input.
+    fl_status s = validate_gemm(A, B, bias, nullptr, Y, nullptr, M, N, K, act, dtype, opt, /*out_optional=*/true);
+    if (s != FL_OK) return s;
+    const size_t q_bytes = (size_t)M * N;
+    if (!out_q && q_bytes) return fail(FL_ERR_INVALID_ARG, "out is NULL");
+    const size_t es = elem_size(dtype);
+    if (overlaps(out_q, q_bytes, A, (size_t)M * K * es)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
+    if (overlaps(out_q, q_bytes, B, (size_t)K * N * es)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
+    if (overlaps(out_q, q_bytes, bias, bias ? (size_t)N * es : 0))
+        return fail(FL_ERR_INVALID_ARG, "out overlaps bias");
+    if (overlaps(out_q, q_bytes, Y, Y ? (size_t)M * N * es : 0)) return fail(FL_ERR_INVALID_ARG, "out overlaps Y");
+    return launch_gemm(A, B, bias, nullptr, Y, out_q, M, N, K, act, dtype, stream, opt, (int)qfmt, scale);
 }
 
 fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

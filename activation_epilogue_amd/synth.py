@@ -32,6 +32,8 @@ class Workload:
     bias_var: float = 1.0
     seed: int = 0
     residual: bool = False
+    qfmt: str = ""       # quantized output ("fp8_e4m3" or "int8"), else the I/O dtype
+    scale: float = 1.0   # quantized output scale
 
     @property
     def flops(self) -> int:
@@ -53,6 +55,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("glu_f16_1024x21568x1024", 1024, 21568, 1024, "f16", "glu"),
     # FFN down-projection with the residual added in the epilogue (no activation)
     Workload("residual_bf16_8192x4096x14336", 8192, 4096, 14336, "bf16", "none", residual=True),
+    # FFN up-projection whose GELU output is stored as FP8 E4M3 codes for the next layer
+    Workload("gelu_fp8out_bf16_8192x14336x4096", 8192, 14336, 4096, "bf16", "gelu_tanh", bias_var=0.1,
+             qfmt="fp8_e4m3", scale=64.0),
 ]}
 
 

@@ -103,7 +103,11 @@ def cpu_baseline(w, d, target_s):
     while True:
         rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, R=d["R"])
+        if w.qfmt:
+            oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, qfmt=w.qfmt,
+                                      scale=w.scale, rows=rows)
+        else:
+            oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, R=d["R"])
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or nrows >= w.M:
             break
@@ -176,7 +180,7 @@ def main():
         return t.to("cuda")
 
     A, B, bias, Y, R = dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["Y"]), dev(d["R"])
-    out = torch.empty((w.M, w.N), dtype=tdt, device="cuda")
+    out = torch.empty((w.M, w.N), dtype=torch.uint8 if w.qfmt else tdt, device="cuda")
     stream = torch.cuda.current_stream()
     opts = {}
     if args.group_m:
@@ -191,7 +195,10 @@ def main():
               "fused_linear_stg16_kernel" if args.tile_cfg == 5 else "fused_linear_dma16_kernel")
 
     def step():
-        fl.fused_linear(A, B, bias, Y, act=w.act, out=out, R=R, **opts)
+        if w.qfmt:
+            fl.fused_linear_quant(A, B, bias, Y, act=w.act, scale=w.scale, qfmt=w.qfmt, out=out, **opts)
+        else:
+            fl.fused_linear(A, B, bias, Y, act=w.act, out=out, R=R, **opts)
 
     # The shader clock ramps up over the first ~100 ms of load; time the
     # sustained state.  These untimed steps precede the W warm-up steps.
@@ -215,8 +222,8 @@ def main():
     achieved = flops / (ms_event * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     es = ES[w.dtype]
-    mn_arrays = 1 + (w.act == "glu") + w.residual  # out, Y, R
-    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * mn_arrays) * es
+    mn_arrays = (0 if w.qfmt else 1) + (w.act == "glu") + w.residual  # out, Y, R in the I/O dtype
+    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * mn_arrays) * es + (w.M * w.N if w.qfmt else 0)
 
     result = {
         "metric": METRIC,
@@ -234,6 +241,7 @@ def main():
         "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s%s)" % (
             w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else "", ", R ~ N(0,1)" if w.residual else ""),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "residual": w.residual,
+                   "out": w.qfmt or w.dtype, "scale": w.scale if w.qfmt else None,
                    "io_dtype": w.dtype,
                    "accumulate": "f32", "tile": f"{bm}x{bn}", "tiles": tiles_m * tiles_n,
                    "tile_cfg": args.tile_cfg, "group_m": args.group_m or 4, "persistent": bool(args.persistent)},
@@ -244,8 +252,8 @@ def main():
                      "algorithmic_bytes": alg_bytes},
     }
 
-    if w.residual:
-        result["unfused"] = None  # no elementwise residual pass in the unfused chain
+    if w.residual or w.qfmt:
+        result["unfused"] = None  # the unfused chain has no residual or quantizing pass
     elif not args.no_unfused:
         X = torch.empty_like(out)
 

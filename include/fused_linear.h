@@ -74,6 +74,12 @@ typedef enum {
     FL_ACT_GLU = 3        /* out = X + X*Y  (the gate; needs Y)       */
 } fl_act;
 
+/* One-byte output codes of fl_fused_linear_quant. */
+typedef enum {
+    FL_Q_FP8_E4M3 = 0, /* OCP FP8 E4M3 (largest finite 448, no infinities) */
+    FL_Q_INT8 = 1      /* two's-complement int8 */
+} fl_qformat;
+
 typedef enum {
     FL_OK = 0,
     FL_ERR_INVALID_ARG = 1,
@@ -160,6 +166,31 @@ fl_status fl_fused_linear_residual(const void *A, const void *B,
                                    int64_t N, int64_t K, fl_act act,
                                    fl_dtype dtype, void *stream,
                                    const fl_options *opt);
+
+/*
+ * out_q = Q(scale * act(A@B + bias)): the fused linear layer with a
+ * quantized store ("Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)",
+ * "Variants": a scale and a clamp applied to the accumulator's epilogue
+ * value and a cast to int8/fp8 before the store).  The epilogue value is the
+ * fp32 one fl_fused_linear would round to dtype; it is multiplied by scale
+ * in fp32 and
+ *   FL_Q_FP8_E4M3: clamped to [-448, 448] and rounded to nearest even on the
+ *                  OCP E4M3 grid (subnormals kept);
+ *   FL_Q_INT8:     rounded to nearest even and clamped to [-128, 127].
+ *   out_q  (M,N) device pointer to M*N bytes (row stride N); must not overlap
+ *          A, B, bias or Y.
+ *   scale  finite fp32 (a per-tensor output scale).
+ *   dtype  FL_F16 or FL_BF16 (FL_F32 inputs are FL_ERR_UNSUPPORTED).
+ *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5 or 6 (the kernels
+ *          the automatic choice uses); other values are FL_ERR_UNSUPPORTED.
+ * Errors as fl_fused_linear_ex; an unknown qfmt or a non-finite scale is
+ * FL_ERR_INVALID_ARG.
+ */
+fl_status fl_fused_linear_quant(const void *A, const void *B,
+                                const void *bias, const void *Y, void *out_q,
+                                float scale, int64_t M, int64_t N, int64_t K,
+                                fl_act act, fl_dtype dtype, fl_qformat qfmt,
+                                void *stream, const fl_options *opt);
 
 /* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
  * traffic": GEMM writes X, a bias pass reads and writes it, an activation

@@ -171,3 +171,29 @@ def test_residual_rejects_bad_arguments(lib, kwargs, status, msg):
 def test_residual_degenerate_shapes_return_ok(lib):
     assert _res(lib, R=None, M=0) == OK
     assert _res(lib, R=None, N=0) == OK
+
+
+def _quant(lib, out=OUT_P, scale=1.0, q=0, dt=F16, act=RELU, Y=None, opt=None, M=64, N=64, K=64):
+    return lib.fl_fused_linear_quant(A_P, B_P, BIAS_P, Y, out, scale, M, N, K, act, dt, q, None,
+                                     ctypes.byref(opt) if opt is not None else None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(q=5), INVALID, "unknown qformat"),
+    (dict(scale=float("nan")), INVALID, "scale must be finite"),
+    (dict(scale=float("inf")), INVALID, "scale must be finite"),
+    (dict(dt=F32), UNSUPPORTED, "fp16 or bf16"),
+    (dict(out=None), INVALID, "out is NULL"),
+    (dict(out=A_P + 100), INVALID, "out overlaps A"),
+    (dict(act=GLU, Y=Y_P, out=Y_P + 8191), INVALID, "out overlaps Y"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5 and 6"),
+    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5 and 6"),
+])
+def test_quant_rejects_bad_arguments(lib, kwargs, status, msg):
+    assert _quant(lib, **kwargs) == status
+    assert msg in lib.fl_last_error().decode()
+
+
+def test_quant_degenerate_shapes_return_ok(lib):
+    assert _quant(lib, out=None, M=0) == OK
+    assert _quant(lib, out=None, N=0) == OK

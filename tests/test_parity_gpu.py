@@ -350,3 +350,82 @@ def test_residual_may_alias_out(dtype):
     torch.cuda.synchronize()
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], act="relu", dtype=dtype, R=d["R"])
     _assert_close(to_host(R, dtype), ref, dtype, "R == out")
+
+
+# -------------------------------------------------------- quantized output
+# out_q = Q(scale * act(A@B + bias)) through fl_fused_linear_quant ("Triton:
+# Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants"): codes equal to
+# the oracle's, except where the oracle's binary32 value sits within the
+# fp32-summation error of a rounding boundary (then the neighbour is valid).
+
+def _run_quant(d, act, dtype, qfmt, scale, **opts):
+    M, K = d["A"].shape
+    N = d["B"].shape[1]
+    A, B, bias, Y = (to_dev(d[k], dtype) for k in ("A", "B", "bias", "Y"))
+    buf = torch.full((M * N + GUARD_Q,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = buf[:M * N].view(M, N)
+    fl.fused_linear_quant(A, B, bias, Y, act=act, scale=scale, qfmt=qfmt, out=out, **opts)
+    torch.cuda.synchronize()
+    assert bool((buf[M * N:] == 0xA5).all().item()), "write past the end of out"
+    return out.cpu().numpy()
+
+
+GUARD_Q = 1024
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("qfmt", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 17, 7), (67, 65, 70), (257, 264, 40), (513, 770, 33)])
+def test_quant_integer_inputs_bit_exact(dtype, act, qfmt, shape):
+    """Exact integers and a power-of-two scale: every intermediate is exact,
+    codes must match bit for bit (this also fixes the fp8 format: OCP E4M3)."""
+    M, N, K = shape
+    d = synth.draw_integer(M, N, K, dtype, act, seed=M + 3 * N + 5 * K, amax=1, bias_max=3)
+    scale = 0.25 if qfmt == "fp8_e4m3" else 8.0
+    say("quant integer", dtype, act, qfmt, shape)
+    got = _run_quant(d, act, dtype, qfmt, scale)
+    ref = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, qfmt=qfmt, scale=scale)
+    assert np.array_equal(got, ref), (np.argwhere(got != ref)[:5], got[got != ref][:5], ref[got != ref][:5])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("qfmt,scale", [("fp8_e4m3", 150.0), ("fp8_e4m3", 0.02), ("int8", 40.0)])
+def test_quant_random_inputs(dtype, act, qfmt, scale):
+    """Scale 150 sends part of the values past 448 (saturation), 0.02 into
+    the fp8 subnormal range, 40 past the int8 range."""
+    M, N, K = 300, 260, 1000
+    d = synth.draw(M, N, K, dtype, act, seed=17)
+    say("quant random", dtype, act, qfmt, scale)
+    got = _run_quant(d, act, dtype, qfmt, scale)
+    ref, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, qfmt=qfmt,
+                                       scale=scale, want_u=True)
+    res = oracle.compare_quant(got, ref, u, qfmt)
+    assert res["ok"], res
+    assert res["accepted_near_boundary"] <= 0.01 * M * N, res
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("qfmt", ["fp8_e4m3", "int8"])
+def test_quant_kernel_variants_identical(dtype, qfmt):
+    M, N, K = 513, 770, 600
+    d = synth.draw(M, N, K, dtype, "relu", seed=19)
+    outs = {}
+    for cfg in (0, 2, 5, 6):
+        say("quant variant", cfg, dtype, qfmt)
+        outs[cfg] = _run_quant(d, "relu", dtype, qfmt, 50.0, tile_cfg=cfg)
+    for cfg, o in outs.items():
+        assert np.array_equal(o, outs[2]), cfg
+
+
+def test_quant_full_size_sampled_rows():
+    w = synth.WORKLOADS["gelu_fp8out_bf16_8192x14336x4096"]
+    d = synth.draw_workload(w)
+    say("full size", w.name)
+    got = _run_quant(d, w.act, w.dtype, w.qfmt, w.scale)
+    rows = sample_rows(w.M)
+    ref, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, qfmt=w.qfmt,
+                                       scale=w.scale, rows=rows, want_u=True)
+    res = oracle.compare_quant(got[rows], ref, u, w.qfmt)
+    assert res["ok"], res
