@@ -411,6 +411,12 @@ struct Dma16 {
         }
     }
 
+    // The output is written once and not read again by this kernel: stores
+    // carry the non-temporal (streaming) policy bit, so the lines leave the
+    // L2 as they are written instead of at the end-of-kernel write-back
+    // (measured +1% at 4096^3, +2-3% on the 8192x14336 and gate shapes).
+    static constexpr int kStreamStore = 2;  // cache-policy operand: nt
+
     // --- epilogue through LDS ---
     // Phase 1 (registers): bias, activation and the one conversion, exactly
     // as FusedTile::epilogue computes them (same arithmetic, same order);
@@ -538,7 +544,7 @@ struct Dma16 {
 #pragma unroll
                 for (int j = 0; j < BATCH; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j), 0,
-                                                           0);
+                                                           kStreamStore);
             }
         } else {
             // The chunk that holds column N-1 (and chunks past it): elements.

@@ -491,6 +491,9 @@ struct FusedTile {
                     for (int e = 0; e < 4; ++e) store_elem<ES>(o[e], rO, e < valid[g] ? off + e * ES : kOob);
                 }
             }
+            // One row block at a time: without this the scheduler reads
+            // every accumulator out of the AGPRs up front and spills.
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
