@@ -411,10 +411,12 @@ struct Dma16 {
         }
     }
 
-    // The output is written once and not read again by this kernel: stores
-    // carry the non-temporal (streaming) policy bit, so the lines leave the
-    // L2 as they are written instead of at the end-of-kernel write-back
-    // (measured +1% at 4096^3, +2-3% on the 8192x14336 and gate shapes).
+    // The output is written once and not read again by this kernel: when
+    // its rows start on 128-byte lines (a.stream_out), the stores carry the
+    // non-temporal (streaming) policy bit, so the lines leave the L2 as they
+    // are written instead of at the end-of-kernel write-back (measured +1% at
+    // 4096^3, +2-3% on the 8192x14336 and gate shapes); on rows that are not
+    // line-aligned the partial lines it then writes cost 10% (4097x3071).
     static constexpr int kStreamStore = 2;  // cache-policy operand: nt
 
     // --- epilogue through LDS ---
@@ -541,10 +543,17 @@ struct Dma16 {
                 u32x4_t v[BATCH];
 #pragma unroll
                 for (int j = 0; j < BATCH; ++j) v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
+                if (a.stream_out) {
 #pragma unroll
-                for (int j = 0; j < BATCH; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j), 0,
-                                                           kStreamStore);
+                    for (int j = 0; j < BATCH; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j),
+                                                               0, kStreamStore);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < BATCH; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j),
+                                                               0, 0);
+                }
             }
         } else {
             // The chunk that holds column N-1 (and chunks past it): elements.

@@ -208,6 +208,7 @@ struct GemmArgs {
     const void *Y;     // gate operand or null
     const void *R;     // residual (M,N) added before the activation, or null
     float scale;       // quantized output: codes of (epilogue value) * scale
+    int stream_out;    // nonzero: every output row starts on a 128-byte line (streaming stores)
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;

@@ -207,6 +207,8 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     a.Y = Y;
     a.R = R;
     a.scale = scale;
+    const int64_t out_row_bytes = N * (qfmt >= 0 ? 1 : es);
+    a.stream_out = (out_row_bytes % 128 == 0) && aligned(out, 128);
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
