@@ -70,6 +70,9 @@ def _load():
             lib.orc_fused_linear_quant.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, c_int,
                                                    ctypes.c_float, p, i64, c_int, p]
             lib.orc_fused_linear_quant.restype = c_int
+            lib.orc_fused_linear_fp8.argtypes = [c_int, c_int, p, p, ctypes.c_double, p, p, p, i64, i64, i64, p,
+                                                 i64, c_int, p]
+            lib.orc_fused_linear_fp8.restype = c_int
             lib.orc_quantize.argtypes = [c_int, p, i64, p]
             lib.orc_dequantize.argtypes = [c_int, p, i64, p]
             lib.orc_element.argtypes = [c_int, c_int, p, p, p, p, p, i64, i64, i64, i64, i64, p]
@@ -166,6 +169,32 @@ def fused_linear_quant(A, B, bias, Y=None, act="relu", dtype="f16", qfmt="fp8_e4
     if st != 0:
         raise RuntimeError(f"orc_fused_linear_quant failed with status {st}")
     return (out, u) if want_u else out
+
+
+def fused_linear_fp8(A8, B8, ab_scale, bias, Y=None, act="relu", out_dtype="f16", rows=None, threads=None,
+                     want_x=False):
+    """round_once(act(ab_scale * (A8@B8) + bias)) in ``out_dtype`` storage: A8
+    (M,K) and B8 (K,N) are uint8 arrays of OCP FP8 E4M3 codes; bias (N,) and
+    Y (M,N) are ``out_dtype`` storage arrays."""
+    lib = _load()
+    A8 = np.ascontiguousarray(A8, dtype=np.uint8)
+    B8 = np.ascontiguousarray(B8, dtype=np.uint8)
+    bias, Y = (_raw(x, out_dtype) for x in (bias, Y))
+    M, K = A8.shape
+    K2, N = B8.shape
+    if K2 != K:
+        raise ValueError("A8 is (M,K) and B8 is (K,N)")
+    if act == "glu" and (Y is None or Y.shape != (M, N)):
+        raise ValueError("the gate needs Y of shape (M,N)")
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = M if rows_arr is None else rows_arr.size
+    out = np.empty((nrows, N), dtype=STORAGE[out_dtype])
+    x = np.empty((nrows, N), dtype=np.float64) if want_x else None
+    st = lib.orc_fused_linear_fp8(DTYPES[out_dtype], ACTS[act], _ptr(A8), _ptr(B8), float(ab_scale), _ptr(bias),
+                                  _ptr(Y), _ptr(out), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(x))
+    if st != 0:
+        raise RuntimeError(f"orc_fused_linear_fp8 failed with status {st}")
+    return (out, x) if want_x else out
 
 
 def quantize(u, qfmt):

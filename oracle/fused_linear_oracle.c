@@ -33,6 +33,10 @@
  *     loop, before the activation; and the quantized output: a scale and a
  *     clamp applied to the epilogue value, then a cast to int8 or fp8
  *     before the one store (see orc_fused_linear_quant).
+ *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next" (FP8
+ *     precision): the projection itself in FP8, i.e. A and B as OCP E4M3
+ *     codes with a per-tensor scale, fp32 accumulation, and the same
+ *     epilogue in the 16-bit output dtype (see orc_fused_linear_fp8).
  *   - GELU: the pages name it as a fusable activation but print no formula;
  *     this file uses the tanh form of Hendrycks & Gimpel (2016),
  *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with libm tanh.
@@ -372,6 +376,68 @@ int orc_element(int dtype, int act, const void *A, const void *B,
     double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
     *value = apply_act(act, x, y);
     return 0;
+}
+
+/* ---------------------------------------------------------- FP8 inputs */
+
+/*
+ * out (nrows x N, out_dtype) = round(act(ab_scale * (A8[rows] @ B8) + bias)):
+ * A8 (M,K) and B8 (K,N) are OCP FP8 E4M3 codes (decoded exactly), ab_scale
+ * is the product of the two per-tensor scales, bias and Y are in out_dtype
+ * (fp16 or bf16).  FP64 throughout, rounded once.  x_out, when not NULL,
+ * receives the unrounded epilogue value.
+ */
+int orc_fused_linear_fp8(int out_dtype, int act, const uint8_t *A8,
+                         const uint8_t *B8, double ab_scale, const void *bias,
+                         const void *Y, void *out, int64_t M, int64_t N,
+                         int64_t K, const int64_t *rows, int64_t nrows,
+                         int nthreads, double *x_out) {
+    if (out_dtype < 0 || out_dtype > 2 || act < 0 || act > 3) return 1;
+    if (M < 0 || N < 0 || K < 0 || !isfinite(ab_scale)) return 1;
+    if ((!A8 && M * K > 0) || (!B8 && K * N > 0) || (!out && M * N > 0)) return 1;
+    if (act == ORC_GLU && !Y && M * N > 0) return 1;
+    if (!rows) nrows = M;
+    if (nrows < 0) return 1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M) return 1;
+    if (nrows == 0 || N == 0) return 0;
+    double *B64 = (double *)malloc(sizeof(double) * (size_t)(K * N + 1));
+    if (!B64) return 2;
+    for (int64_t i = 0; i < K * N; ++i) B64[i] = dec_e4m3(B8[i]);
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+        double *arow = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+        if (!acc || !arow) {
+#pragma omp atomic write
+            status = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t i = rows ? rows[r] : r;
+                for (int64_t k = 0; k < K; ++k) arow[k] = dec_e4m3(A8[i * K + k]);
+                row_product(arow, B64, acc, N, K);
+                for (int64_t j = 0; j < N; ++j) {
+                    double x = acc[j] * ab_scale + (bias ? dec_one(out_dtype, bias, j) : 0.0);
+                    double y = (act == ORC_GLU) ? dec_one(out_dtype, Y, i * N + j) : 0.0;
+                    double v = apply_act(act, x, y);
+                    if (x_out) x_out[r * N + j] = v;
+                    enc_one(out_dtype, v, out, r * N + j);
+                }
+            }
+        }
+        free(acc);
+        free(arow);
+    }
+    free(B64);
+    return status;
 }
 
 /* --------------------------------------------------------------- tile map */

@@ -475,3 +475,42 @@ def test_compare_quant_flags_off_by_one_codes_away_from_boundaries():
     # scale applied twice, or the activation after the scale for a negative scale: flagged
     twice = oracle.quantize(u * 20.0, "fp8_e4m3")
     assert not oracle.compare_quant(twice, codes, u, "fp8_e4m3")["ok"]
+
+
+# ---------------------------------------------------------------- FP8 inputs
+# "Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next": the
+# projection in FP8 (A and B as OCP E4M3 codes, per-tensor scale, fp32
+# accumulation, 16-bit epilogue and output).
+
+def _e4m3_codes(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+def test_fp8_inputs_integer_brute_force(out_dtype, act):
+    """Small integers are exact E4M3 codes: int64 brute force, a power-of-two
+    scale, every intermediate exact, the output rounded once."""
+    rng = np.random.default_rng(41)
+    M, N, K = 29, 45, 52
+    A = rng.integers(-2, 3, (M, K))
+    B = rng.integers(-2, 3, (K, N))
+    bias = rng.integers(-4, 5, N)
+    Y = rng.integers(-1, 2, (M, N))
+    X = (A @ B) * 0.5 + bias[None, :]
+    exp = np.maximum(X, 0) if act == "relu" else X + X * Y if act == "glu" else X
+    got = oracle.fused_linear_fp8(_e4m3_codes(A), _e4m3_codes(B), 0.5, synth.to_storage(bias, out_dtype),
+                                  synth.to_storage(Y, out_dtype) if act == "glu" else None, act=act,
+                                  out_dtype=out_dtype)
+    assert np.array_equal(oracle.decode(got, out_dtype), exp.astype(np.float64))
+
+
+def test_fp8_inputs_match_decoded_matmul():
+    rng = np.random.default_rng(42)
+    A8 = _e4m3_codes(rng.standard_normal((40, 64)))
+    B8 = _e4m3_codes(rng.standard_normal((64, 50)))
+    bias = synth.to_storage(rng.standard_normal(50), "bf16")
+    _, x = oracle.fused_linear_fp8(A8, B8, 0.125, bias, act="none", out_dtype="bf16", want_x=True)
+    A = torch.from_numpy(A8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    B = torch.from_numpy(B8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_allclose(x, A @ B * 0.125 + oracle.decode(bias, "bf16")[None, :], rtol=1e-12, atol=1e-12)
