@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the ``fl_`` prefix):
                                           # R: residual -> fl_fused_linear_residual
   fused_linear_quant(A, B, bias=None, Y=None, act="relu", scale=1.0, qfmt="fp8_e4m3", out=None, **options)
                                           # uint8 codes of Q(scale * act(A@B + bias))
+  fused_linear_fp8(A8, B8, ab_scale, bias=None, Y=None, act="relu", out_dtype=torch.float16, out=None, **options)
+                                          # FP8 E4M3 operands, 16-bit epilogue and output
   gemm(A, B, X=None)                      # unfused step 1: X = A@B
   bias_add(X, bias)                       # unfused step 2: X += bias (in place)
   activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
@@ -27,8 +29,8 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
-EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant", "fl_gemm",
-           "fl_bias_add", "fl_activation",
+EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
+           "fl_fused_linear_fp8", "fl_gemm", "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
 
@@ -68,13 +70,15 @@ def load_library():
                                              ctypes.POINTER(Options)]
     lib.fl_fused_linear_quant.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, c_int, c_int, c_int, vp,
                                           ctypes.POINTER(Options)]
+    lib.fl_fused_linear_fp8.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
+                                        ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
     lib.fl_activation.argtypes = [vp, vp, vp, i64, i64, c_int, c_int, vp]
     lib.fl_tile_grid.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(Options), P_i32, P_i32, P_i32, P_i32]
     lib.fl_tile_of_program.argtypes = [i32, i32, i32, i32, i32, i32, P_i32, P_i32]
-    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant", "fl_gemm",
-              "fl_bias_add", "fl_activation", "fl_tile_grid", "fl_tile_of_program"):
+    for f in ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
+              "fl_fused_linear_fp8", "fl_gemm", "fl_bias_add", "fl_activation", "fl_tile_grid", "fl_tile_of_program"):
         getattr(lib, f).restype = c_int
     lib.fl_status_string.argtypes = [c_int]
     lib.fl_status_string.restype = ctypes.c_char_p
@@ -184,6 +188,33 @@ def fused_linear_quant(A, B, bias=None, Y=None, act="relu", scale=1.0, qfmt="fp8
         _dev_ptr(A, "A", dt), _dev_ptr(B, "B", dt, (K, N)), _dev_ptr(bias, "bias", dt, (N,)),
         _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(out, "out", torch.uint8, (M, N)), float(scale), M, N, K, ACTS[act],
         _dtype_code(dt), QFORMATS[qfmt], _stream(A, stream), ctypes.byref(opt)))
+    return out
+
+
+def fused_linear_fp8(A8, B8, ab_scale, bias=None, Y=None, act="relu", out_dtype=None, out=None, *, stream=None,
+                     **options):
+    """out = act(ab_scale * (A8@B8) + bias) (fl_fused_linear_fp8): A8 (M,K) and
+    B8 (K,N) hold OCP FP8 E4M3 codes (torch.uint8 or torch.float8_e4m3fn);
+    bias (N,), Y (M,N) and out are fp16 or bf16 (out_dtype, default fp16 or
+    bias's dtype)."""
+    import torch
+    lib = load_library()
+    if A8.dim() != 2 or B8.dim() != 2 or A8.shape[1] != B8.shape[0]:
+        raise ValueError("A8 must be (M,K) and B8 (K,N)")
+    M, K = A8.shape
+    N = B8.shape[1]
+    if out_dtype is None:
+        out_dtype = bias.dtype if bias is not None else torch.float16
+    A8 = A8.view(torch.uint8) if A8.dtype != torch.uint8 else A8
+    B8 = B8.view(torch.uint8) if B8.dtype != torch.uint8 else B8
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A8.device)
+    opt = _options(**options)
+    _check(lib.fl_fused_linear_fp8(
+        _dev_ptr(A8, "A8", torch.uint8), _dev_ptr(B8, "B8", torch.uint8, (K, N)), float(ab_scale),
+        _dev_ptr(bias, "bias", out_dtype, (N,)), _dev_ptr(Y, "Y", out_dtype, (M, N)),
+        _dev_ptr(out, "out", out_dtype, (M, N)), M, N, K, ACTS[act], _dtype_code(out_dtype), _stream(A8, stream),
+        ctypes.byref(opt)))
     return out
 
 

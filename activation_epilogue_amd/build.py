@@ -1,8 +1,9 @@
 """Build libfused_linear.so for gfx950 with hipcc, in-tree.
 
-Six translation units compiled in parallel: the host/ABI unit (with the
-elementwise kernels), one unit of fused GEMM kernels per dtype and one of
-quantized-output kernels per 16-bit dtype; then the
+Eight translation units compiled in parallel: the host/ABI unit (with the
+elementwise kernels), one unit of fused GEMM kernels per dtype, one of
+quantized-output kernels per 16-bit dtype and one of FP8-input kernels per
+16-bit output dtype; then the
 separate MFMA-rate probe library used by the benchmark.  Every
 device compile carries -Xclang -target-feature -Xclang -packed-fp32-ops so
 that no packed fp32 instructions are generated.
@@ -34,6 +35,8 @@ UNITS = [
     ("fl_fused_inst.hip", ["-DFL_INST_DTYPE=2"]),
     ("fl_quant_inst.hip", ["-DFL_INST_DTYPE=1"]),
     ("fl_quant_inst.hip", ["-DFL_INST_DTYPE=2"]),
+    ("fl_fp8_inst.hip", ["-DFL_INST_DTYPE=1"]),
+    ("fl_fp8_inst.hip", ["-DFL_INST_DTYPE=2"]),
 ]
 
 

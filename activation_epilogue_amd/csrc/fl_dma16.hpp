@@ -42,6 +42,8 @@ namespace fl {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // Buffer descriptor in SGPRs (gfx9 layout: 48-bit base, stride 0,
 // num_records, word 3 = 32-bit data format) for the inline-asm copies.
@@ -97,23 +99,30 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // and start-up overlap the other's K loop.  RES: the epilogue adds the
 // residual a.R (compiled in only where it is used, so the plain epilogue
 // keeps its registers).  QF: -1 stores the I/O dtype; FL_Q_FP8_E4M3 or
-// FL_Q_INT8 store one-byte codes of the epilogue value times a.scale.
+// FL_Q_INT8 store one-byte codes of the epilogue value times a.scale.  IN:
+// the type of A and B, DT (fp16/bf16) or kInFp8 (OCP E4M3 codes, fp8 MFMA,
+// the accumulator scaled by a.ab_scale before the bias; bias, Y and out
+// stay in DT).
 template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false,
-          int QF = -1>
+          int QF = -1, int IN = DT>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
+    static constexpr bool F8 = IN == kInFp8;
+    static constexpr int IES = F8 ? 1 : 2;           // bytes per A/B element
+    static constexpr int EPCH = 16 / IES;            // A/B elements per 16-byte chunk
+    static constexpr int KPM = F8 ? 64 : 16;         // K per MFMA (32x32x64 fp8, 32x32x16 fp16/bf16)
     static constexpr int BM = 256, BN = BN_, BK = BK_;
-    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(BK * IES == 64 || BK * IES == 128, "stage depth: 64- or 128-byte A rows");
     static_assert(BN == 256 || BN == 128, "tile width");
     static_assert(WAVES_N == 2 || WAVES_N == 4, "wave grid");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
     static constexpr int NI = WN / 32;               // 32-wide MFMA blocks per wave along N
-    static constexpr int KK = BK / 16;               // MFMA blocks (k16) per stage
-    static constexpr int CA = BK / 8;                // 16-byte chunks per A row
-    static constexpr int CB = BN / 8;                // 16-byte chunks per B row
-    static constexpr int A_BYTES = BM * BK * 2;      // rows of BK*2 bytes
-    static constexpr int B_BYTES = BK * BN * 2;      // rows of BN*2 bytes
+    static constexpr int KK = BK / KPM;              // MFMA blocks per stage
+    static constexpr int CA = BK * IES / 16;         // 16-byte chunks per A row
+    static constexpr int CB = BN * IES / 16;         // 16-byte chunks per B row
+    static constexpr int A_BYTES = BM * BK * IES;    // rows of BK*IES bytes
+    static constexpr int B_BYTES = BK * BN * IES;    // rows of BN*IES bytes
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
     static constexpr int NBUF = (OCC == 2 ? 73728 : BN == 256 ? 131072 : 147456) / BUF_BYTES;  // LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
@@ -122,7 +131,9 @@ struct Dma16 {
     static constexpr int NB = BK / (B_ROWS_PER_COPY * WAVES);  // B copies per wave per stage
     static constexpr int DMA_PER_WAVE = NA + NB;
     static constexpr int SLOTS = 4 * NI;             // MFMAs per block
-    static constexpr int READS = 4 + 2 * NI;         // operand reads per block
+    static constexpr int RPA = F8 ? 2 : 1;           // LDS reads per A operand (16 bytes each)
+    static constexpr int RPB = F8 ? 4 : 2;           // transposed 8-byte reads per B operand
+    static constexpr int READS = 4 * RPA + NI * RPB; // operand reads per block
     static_assert(NA * WAVES * A_ROWS_PER_COPY == BM, "A copies cover the tile");
     static_assert(NB * WAVES * B_ROWS_PER_COPY == BK, "B copies cover the stage");
     // The swizzle of a copy's rows repeats with period 2 in the copy index
@@ -144,11 +155,18 @@ struct Dma16 {
         else
             return ((r >> 1) ^ ((r & 1) << 2)) & 7;
     }
-    // B swizzle: chunk c of k-row r sits at c ^ fb(r), fb in {0,6,12,10} by
-    // r % 4 (rows are 256 or 512 bytes, a multiple of the bank width);
-    // conflict-free for the transposed 8-byte reads (4 rows x 2 or 4 chunks
-    // per 16 or 32 lanes).
-    __device__ __forceinline__ static int fb(int r) { return (0xAC60 >> (4 * (r & 3))) & 0xF; }
+    // B swizzle: chunk c of k-row r sits at c ^ fb(r).  16-bit B: fb in
+    // {0,6,12,10} by r % 4 (rows are 256 or 512 bytes, a multiple of the bank
+    // width); conflict-free for the transposed 8-byte reads (4 rows x 2 or 4
+    // chunks per 16 or 32 lanes).  FP8 B: fb = r % 8, so the 8 k-rows a
+    // 16-lane transposed read touches (one 16-byte chunk each) fall in 8
+    // different chunks.
+    __device__ __forceinline__ static int fb(int r) {
+        if constexpr (F8)
+            return r & 7;
+        else
+            return (0xAC60 >> (4 * (r & 3))) & 0xF;
+    }
 
     // Per-lane copy offsets and operand-read addresses, fixed for a tile.
     // A is addressed through a descriptor based at row m0 and B through one
@@ -174,31 +192,51 @@ struct Dma16 {
     __device__ __forceinline__ static void setup(const GemmArgs &a, int m0, int n0, int wave, int lane, int wm,
                                                  int wn, Lane &L) {
         const size_t a_org = (size_t)m0 * a.K;
-        L.rA = sgpr_rsrc(static_cast<const char *>(a.A) + a_org * 2, ((size_t)a.M * a.K - a_org) * 2);
-        L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * 2, ((size_t)a.K * a.N - n0) * 2);
+        L.rA = sgpr_rsrc(static_cast<const char *>(a.A) + a_org * IES, ((size_t)a.M * a.K - a_org) * IES);
+        L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * IES, ((size_t)a.K * a.N - n0) * IES);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int ra = A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
             const int ca = (lane % CA) ^ fa(ra);
-            L.a_off[i] = (uint32_t)(ra * a.K + ca * 8) * 2;
-            L.a_k[i] = ca * 8;
+            L.a_off[i] = (uint32_t)(ra * a.K + ca * EPCH) * IES;
+            L.a_k[i] = ca * EPCH;
             const int rb = B_ROWS_PER_COPY * (wave * NB + i) + lane / CB;
             const int cb = (lane % CB) ^ fb(rb);
-            L.b_off[i] = (n0 + cb * 8 < a.N) ? (uint32_t)(rb * a.N + cb * 8) * 2 : kOob;
+            L.b_off[i] = (n0 + cb * EPCH < a.N) ? (uint32_t)(rb * a.N + cb * EPCH) * IES : kOob;
         }
         L.b_k0 = B_ROWS_PER_COPY * wave * NB + lane / CB;
-        L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * 2;
-        L.b_step = (uint32_t)(2 * B_ROWS_PER_COPY * a.N) * 2;
+        L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * IES;
+        L.b_step = (uint32_t)(2 * B_ROWS_PER_COPY * a.N) * IES;
         const int lrow = lane & 31, lg = lane >> 5;
         const int r = wm * 128 + lrow;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
         const int g16 = lane >> 4, i16 = lane & 15;
-        const int rk = (g16 >> 1) * 8 + (i16 >> 2);  // k-row for kk = 0, h = 0
+        if constexpr (!F8) {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            const int n = wn * WN + ni * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-            L.b_frag[ni] = A_BYTES + rk * (BN * 2) + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
+            for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
+            const int rk = (g16 >> 1) * 8 + (i16 >> 2);  // k-row for kk = 0, h = 0
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = wn * WN + ni * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+                L.b_frag[ni] = A_BYTES + rk * (BN * 2) + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
+            }
+        } else {
+            // A: lane (row r, half lg) takes k = lg*32 .. lg*32+31 of each
+            // 64-deep block: chunks kk*4 + lg*2 and the next one, whose
+            // swizzled address differs in bit 4 (c even: (c+1)^f = (c^f)^1).
+            // The fp8 MFMA pairs byte j of lane half lg in both operands, so
+            // any k order works if A and B use the same one.
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r * (BK * IES) + (((kk * 4 + lg * 2) ^ fa(r)) * 16);
+            // B: a 16-lane transposed read gives lane i byte i%8 from lanes
+            // i/8 + 2j (j = 0..7), so lane L of group g16 points at k-row
+            // lg*32 + L/2 (+8 per read t), 8 columns at 8*(L%2): the lane
+            // then holds 8 k-values of column (g16 & 1)*16 + i16.
+            const int rk = lg * 32 + (i16 >> 1);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = wn * WN + ni * 32 + (g16 & 1) * 16 + 8 * (i16 & 1);
+                L.b_frag[ni] = A_BYTES + rk * BN + (((n >> 4) ^ fb(rk)) * 16) + (n & 15);
+            }
         }
     }
 
@@ -212,8 +250,8 @@ struct Dma16 {
         const int k0 = kt * BK;
         Stage s;
         s.kleft = a.K - k0;
-        s.soa = (uint32_t)k0 * 2;
-        s.sob = (uint32_t)k0 * (uint32_t)a.N * 2;
+        s.soa = (uint32_t)k0 * IES;
+        s.sob = (uint32_t)k0 * (uint32_t)a.N * IES;
         s.adst = __builtin_amdgcn_readfirstlane(buf_addr + wave * NA * 1024);
         s.bdst = __builtin_amdgcn_readfirstlane(buf_addr + A_BYTES + wave * NB * 1024);
         return s;
@@ -297,24 +335,30 @@ struct Dma16 {
     }
 
     struct Frags {
-        u32x4_t a[4];      // A operand per mi
-        s16x4_t b[NI][2];  // B operand per ni, two halves of 4 k values
+        u32x4_t a[4][RPA];  // A operand per mi (16 bytes per read)
+        i32x2_t b[NI][RPB]; // B operand per ni (8 bytes per transposed read)
     };
 
     // Operand read number P of the READS that make up one kk block, in the
-    // order the MFMAs of a block consume them: a0, b0 (2 halves) .. b(NI-1),
-    // a1..a3.
+    // order the MFMAs of a block consume them: a0, b0 (RPB pieces) ..
+    // b(NI-1), a1..a3 (RPA pieces each).
     template <int P>
     __device__ __forceinline__ static void read_piece(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
-        if constexpr (P == 0) {
-            f.a[0] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk]);
-        } else if constexpr (P <= 2 * NI) {
-            constexpr int ni = (P - 1) / 2, h = (P - 1) % 2;
-            f.b[ni][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 16 * (BN * 2) + h * 4 * (BN * 2)));
+        if constexpr (P < RPA) {
+            f.a[0][P] = *(const FL_LDS u32x4_t *)(buf + (L.a_frag[kk] ^ (P * 16)));
+        } else if constexpr (P < RPA + NI * RPB) {
+            constexpr int ni = (P - RPA) / RPB, h = (P - RPA) % RPB;
+            if constexpr (!F8)
+                f.b[ni][h] = __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                             (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 16 * (BN * 2) +
+                                                                                h * 4 * (BN * 2))));
+            else
+                f.b[ni][h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (FL_LDS i32x2_t *)(buf + L.b_frag[ni] + kk * 64 * BN + h * 8 * BN));
         } else {
-            constexpr int mi = P - 2 * NI;
-            f.a[mi] = *(const FL_LDS u32x4_t *)(buf + L.a_frag[kk] + mi * 32 * BK * 2);
+            constexpr int Q = P - RPA - NI * RPB;
+            constexpr int mi = 1 + Q / RPA, h = Q % RPA;
+            f.a[mi][h] = *(const FL_LDS u32x4_t *)(buf + ((L.a_frag[kk] + mi * 32 * BK * IES) ^ (h * 16)));
         }
     }
 
@@ -325,19 +369,37 @@ struct Dma16 {
             read_all<P + 1>(L, buf, kk, f);
         }
     }
+    template <int P0, int P1>
+    __device__ __forceinline__ static void read_range(const Lane &L, const FL_LDS char *buf, int kk, Frags &f) {
+        if constexpr (P0 < P1) {
+            read_piece<P0>(L, buf, kk, f);
+            read_range<P0 + 1, P1>(L, buf, kk, f);
+        }
+    }
 
     template <int I>
     __device__ __forceinline__ static void mma_one(const Frags &f, f32x16_t (&acc)[4][NI]) {
         constexpr int mi = I / NI, ni = I % NI;
-        const s16x8_t bv = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (F8) {
+            const i32x4_t b01 = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3);
+            const i32x4_t b23 = __builtin_shufflevector(f.b[ni][2], f.b[ni][3], 0, 1, 2, 3);
+            const i32x8_t bv = __builtin_shufflevector(b01, b23, 0, 1, 2, 3, 4, 5, 6, 7);
+            const i32x8_t av = __builtin_shufflevector(__builtin_bit_cast(i32x4_t, f.a[mi][0]),
+                                                       __builtin_bit_cast(i32x4_t, f.a[mi][1]), 0, 1, 2, 3, 4, 5, 6, 7);
+            // format codes 0, 0: both operands FP8 E4M3; no block scales
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+            return;
+        }
+        const s16x8_t bv = __builtin_bit_cast(
+            s16x8_t, __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3));
         if constexpr (DT == FL_F16)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bv),
-                                                                 __builtin_bit_cast(f16x8_t, f.a[mi]), acc[mi][ni], 0,
-                                                                 0, 0);
+                                                                 __builtin_bit_cast(f16x8_t, f.a[mi][0]), acc[mi][ni],
+                                                                 0, 0, 0);
         else
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv),
-                                                                  __builtin_bit_cast(bf16x8_t, f.a[mi]), acc[mi][ni],
-                                                                  0, 0, 0);
+                                                                  __builtin_bit_cast(bf16x8_t, f.a[mi][0]),
+                                                                  acc[mi][ni], 0, 0, 0);
     }
 
     // Copies [C0, C1) of a look-ahead stage.
@@ -360,8 +422,12 @@ struct Dma16 {
             constexpr int NC = C1 - C0;
             mma_one<I>(use, acc);
             copy_range<C0 + (I * NC + SLOTS - 1) / SLOTS, C0 + ((I + 1) * NC + SLOTS - 1) / SLOTS>(L, s);
-            constexpr int R = NC > 0 ? I - (SLOTS - READS) : I;
-            if constexpr (R >= 0 && R < READS) read_piece<R>(L, src, kk_next, fill);
+            if constexpr (READS <= SLOTS) {
+                constexpr int R = NC > 0 ? I - (SLOTS - READS) : I;
+                if constexpr (R >= 0 && R < READS) read_piece<R>(L, src, kk_next, fill);
+            } else {
+                read_range<I * READS / SLOTS, (I + 1) * READS / SLOTS>(L, src, kk_next, fill);
+            }
             __builtin_amdgcn_sched_barrier(0);
             block<I + 1, C0, C1>(L, src, kk_next, s, use, fill, acc);
         }
@@ -403,8 +469,9 @@ struct Dma16 {
             const int nbuf = buf + 1 == NBUF ? 0 : buf + 1;
             const FL_LDS char *nxt = lds + nbuf * BUF_BYTES;
             wait_vm<(NBUF - 2) * DMA_PER_WAVE>();
-            if (((a.K | a.N) & 7) && kt + 2 == nk)
-                fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
+            if constexpr (!F8)
+                if (((a.K | a.N) & 7) && kt + 2 == nk)
+                    fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
             __syncthreads();
             pend = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
             block<0, 0, part_lo(1)>(L, nxt, 0, pend, f[J & 1], f[(J + 1) & 1], acc);
@@ -502,7 +569,11 @@ struct Dma16 {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
-                    float x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
+                    float x;
+                    if constexpr (F8)
+                        x = __builtin_fmaf(acc[mi][ni][q * 4 + e], a.ab_scale, base::elem_f32(bq[g], e));
+                    else
+                        x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
                     if constexpr (has_r) x += base::elem_f32(rq[mi % (RA + 1)][g], e);
                     v[e] = activate<ACT>(x, y);
                 }
@@ -604,7 +675,8 @@ struct Dma16 {
             Stage pend = stage_of(a, NBUF - 1, wave, lds_addr + (NBUF - 1) * BUF_BYTES);
             copy_range<0, part_lo(1)>(L, pend);
             wait_vm<(NBUF - 2) * DMA_PER_WAVE + part_lo(1)>();
-            if (((a.K | a.N) & 7) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
+            if constexpr (!F8)
+                if (((a.K | a.N) & 7) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
             __syncthreads();
             Frags f[2];
             read_all(L, lds, 0, f[0]);
@@ -634,9 +706,9 @@ struct Dma16 {
 // 4096^3 fp16, 8192x14336x4096 bf16 and 1024x21568x4096 fp16 shapes.
 constexpr int kCopySpread = 2;
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF, int IN = DT>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF>;
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF, IN>;
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

@@ -53,6 +53,7 @@ typedef unsigned int v2u32_t __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr int kInFp8 = 3;  // A/B element type "OCP FP8 E4M3 codes" (template argument, not an fl_dtype)
 constexpr int kChunks = 8;  // 16-byte chunks of K per LDS row per stage
 constexpr int kNumXcd = 8;
 
@@ -209,6 +210,7 @@ struct GemmArgs {
     const void *R;     // residual (M,N) added before the activation, or null
     float scale;       // quantized output: codes of (epilogue value) * scale
     int stream_out;    // nonzero: every output row starts on a 128-byte line (streaming stores)
+    float ab_scale;    // FP8 inputs: accumulator scale (product of A's and B's per-tensor scales)
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;
@@ -651,5 +653,11 @@ fused_launcher pick_fused_for(int act, bool vec, int variant, bool residual);
 // instantiation unit (fp16/bf16 only).
 template <int DT>
 fused_launcher pick_quant_for(int act, int variant, int qfmt);
+
+// Launcher of the FP8-input kernel with output dtype DT for (act, variant),
+// or nullptr when that variant has none; defined in the per-output-dtype
+// FP8 instantiation unit.
+template <int DT>
+fused_launcher pick_fp8_for(int act, int variant);
 
 }  // namespace fl

@@ -186,7 +186,7 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
 
 fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
                       int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt,
-                      int qfmt = -1, float scale = 1.0f) {
+                      int qfmt = -1, float scale = 1.0f, bool fp8_in = false, float ab_scale = 1.0f) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
@@ -209,6 +209,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     a.scale = scale;
     const int64_t out_row_bytes = N * (qfmt >= 0 ? 1 : es);
     a.stream_out = (out_row_bytes % 128 == 0) && aligned(out, 128);
+    a.ab_scale = ab_scale;
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
@@ -224,6 +225,13 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (a.persistent) {
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
+    }
+    if (fp8_in) {
+        const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
+                                                     : fl::pick_fp8_for<FL_BF16>(act, t.variant);
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 2 and 5 only");
+        f(a, grid, static_cast<hipStream_t>(stream));
+        return check_launch("fused_linear_fp8");
     }
     if (qfmt >= 0) {
         const fl::fused_launcher q = dtype == FL_F16 ? fl::pick_quant_for<FL_F16>(act, t.variant, qfmt)
@@ -285,6 +293,42 @@ fl_status fl_fused_linear_quant(const void *A, const void *B, const void *bias, 
         return fail(FL_ERR_INVALID_ARG, "out overlaps bias");
     if (overlaps(out_q, q_bytes, Y, Y ? (size_t)M * N * es : 0)) return fail(FL_ERR_INVALID_ARG, "out overlaps Y");
     return launch_gemm(A, B, bias, nullptr, Y, out_q, M, N, K, act, dtype, stream, opt, (int)qfmt, scale);
+}
+
+fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, const void *bias, const void *Y,
+                              void *out, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype out_dtype, void *stream,
+                              const fl_options *opt) {
+    clear_error();
+    if (!(ab_scale == ab_scale) || ab_scale - ab_scale != 0.0f) return fail(FL_ERR_INVALID_ARG, "ab_scale must be finite");
+    if (out_dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs produce fp16 or bf16 outputs");
+    // Bias, Y and out are checked as for a 16-bit layer (A and B apart: one
+    // byte per element).
+    fl_status s = validate_gemm(nullptr, nullptr, bias, nullptr, Y, out, M, N, 0, act, out_dtype, opt);
+    if (s != FL_OK) return s;
+    s = check_dims(M, N, K);
+    if (s != FL_OK) return s;
+    if (K % 16 != 0 || N % 16 != 0)
+        return fail(FL_ERR_UNSUPPORTED, "FP8 inputs need K and N multiples of 16 (whole 16-byte chunks)");
+    if (!aligned(A8, 16) || !aligned(B8, 16)) return fail(FL_ERR_INVALID_ARG, "A8 and B8 must be 16-byte aligned");
+    if (opt) {
+        TileShape t;
+        s = tile_shape(FL_F16, M, N, K, opt, t);
+        if (s != FL_OK) return s;
+    }
+    const size_t a_bytes = (size_t)M * K, b_bytes = (size_t)K * N, o_bytes = (size_t)M * N * elem_size(out_dtype);
+    if (!A8 && a_bytes) return fail(FL_ERR_INVALID_ARG, "A is NULL");
+    if (!B8 && b_bytes) return fail(FL_ERR_INVALID_ARG, "B is NULL");
+    if (K * 256 >= 0x80000000ll) return fail(FL_ERR_UNSUPPORTED, "K too large (256 rows must span < 2 GiB)");
+    if (overlaps(out, o_bytes, A8, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
+    if (overlaps(out, o_bytes, B8, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
+    // The two-per-CU variant has no FP8 build: short reductions run 256x128.
+    fl_options o = opt ? *opt : fl_options{};
+    if (o.tile_cfg == 0) {
+        TileShape t;
+        tile_shape(FL_F16, M, N, K, &o, t);
+        if (t.variant == fl::kDirect32x128Occ2) o.tile_cfg = 2;
+    }
+    return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }
 
 fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

@@ -34,6 +34,7 @@ class Workload:
     residual: bool = False
     qfmt: str = ""       # quantized output ("fp8_e4m3" or "int8"), else the I/O dtype
     scale: float = 1.0   # quantized output scale
+    in8: bool = False    # A and B as FP8 E4M3 codes (dtype is then the output / bias / Y dtype)
 
     @property
     def flops(self) -> int:
@@ -58,6 +59,10 @@ WORKLOADS = {w.name: w for w in [
     # FFN up-projection whose GELU output is stored as FP8 E4M3 codes for the next layer
     Workload("gelu_fp8out_bf16_8192x14336x4096", 8192, 14336, 4096, "bf16", "gelu_tanh", bias_var=0.1,
              qfmt="fp8_e4m3", scale=64.0),
+    # the projection in FP8 (A, B as E4M3 codes, ab_scale 1/sqrt(K)), 16-bit epilogue: the gate at the
+    # TLX page's shape, and ReLU at 4096^3
+    Workload("glu_fp8in_f16_1024x21568x4096", 1024, 21568, 4096, "f16", "glu", in8=True),
+    Workload("relu_fp8in_f16_4096x4096x4096", 4096, 4096, 4096, "f16", "relu", in8=True),
 ]}
 
 
@@ -94,7 +99,30 @@ def draw(M, N, K, dtype, act, bias_var=1.0, seed=0, with_bias=True, residual=Fal
 
 
 def draw_workload(w: Workload, with_bias=True):
+    if w.in8:
+        return draw_fp8(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed)
     return draw(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed, with_bias, w.residual)
+
+
+def to_e4m3(x64: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) of float64 data, RNE via torch's float32 ->
+    float8_e4m3fn cast (the data drawn here stays far inside +-448)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def draw_fp8(M, N, K, out_dtype, act, bias_var=1.0, seed=0):
+    """FP8-operand inputs: A, B ~ N(0, 1) stored as E4M3 codes ("A8", "B8"),
+    ab_scale = 1/sqrt(K) (so A@B*ab_scale ~ N(0, 1)); bias ~ N(0, bias_var)
+    and Y ~ U(-1, 1) in out_dtype.  Draw order A, B, bias, Y."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K))
+    B = rng.standard_normal((K, N))
+    bias = rng.standard_normal(N) * np.sqrt(bias_var)
+    Y = rng.uniform(-1.0, 1.0, (M, N)) if act == "glu" else None
+    return {"A8": to_e4m3(A), "B8": to_e4m3(B), "ab_scale": float(np.float32(1.0 / np.sqrt(max(K, 1)))),
+            "bias": to_storage(bias, out_dtype), "Y": None if Y is None else to_storage(Y, out_dtype), "R": None}
 
 
 def draw_integer(M, N, K, dtype, act, seed=0, amax=2, bias_max=4):

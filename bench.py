@@ -27,7 +27,7 @@ METRIC = "fused GEMM+bias+act TFLOP/s and % of MFMA peak (fp16, 4096^3) on 1 MI3
 DEFAULT_WORKLOAD = "relu_f16_4096x4096x4096"
 # MI355X dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s): 256 CUs at
 # 2.4 GHz; fp16/bf16 4096 flop/clk/CU, fp32 256 flop/clk/CU.
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 ES = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -103,7 +103,10 @@ def cpu_baseline(w, d, target_s):
     while True:
         rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        if w.qfmt:
+        if w.in8:
+            oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act,
+                                    out_dtype=w.dtype, rows=rows)
+        elif w.qfmt:
             oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, qfmt=w.qfmt,
                                       scale=w.scale, rows=rows)
         else:
@@ -179,7 +182,11 @@ def main():
             t = t.view(torch.int16).view(torch.bfloat16)
         return t.to("cuda")
 
-    A, B, bias, Y, R = dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["Y"]), dev(d["R"])
+    if w.in8:
+        A, B = (torch.from_numpy(d[k]).to("cuda") for k in ("A8", "B8"))
+    else:
+        A, B = dev(d["A"]), dev(d["B"])
+    bias, Y, R = dev(d["bias"]), dev(d["Y"]), dev(d["R"])
     out = torch.empty((w.M, w.N), dtype=torch.uint8 if w.qfmt else tdt, device="cuda")
     stream = torch.cuda.current_stream()
     opts = {}
@@ -195,7 +202,9 @@ def main():
               "fused_linear_stg16_kernel" if args.tile_cfg == 5 else "fused_linear_dma16_kernel")
 
     def step():
-        if w.qfmt:
+        if w.in8:
+            fl.fused_linear_fp8(A, B, d["ab_scale"], bias, Y, act=w.act, out_dtype=tdt, out=out, **opts)
+        elif w.qfmt:
             fl.fused_linear_quant(A, B, bias, Y, act=w.act, scale=w.scale, qfmt=w.qfmt, out=out, **opts)
         else:
             fl.fused_linear(A, B, bias, Y, act=w.act, out=out, R=R, **opts)
@@ -220,10 +229,11 @@ def main():
     flops = w.flops
     tflops = flops / (ms_wall * 1e-3) / 1e12
     achieved = flops / (ms_event * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    peak = PEAK_TFLOPS["fp8" if w.in8 else w.dtype]
     es = ES[w.dtype]
     mn_arrays = (0 if w.qfmt else 1) + (w.act == "glu") + w.residual  # out, Y, R in the I/O dtype
-    alg_bytes = (w.M * w.K + w.K * w.N + w.N + w.M * w.N * mn_arrays) * es + (w.M * w.N if w.qfmt else 0)
+    alg_bytes = ((w.M * w.K + w.K * w.N) * (1 if w.in8 else es) + (w.N + w.M * w.N * mn_arrays) * es
+                 + (w.M * w.N if w.qfmt else 0))
 
     result = {
         "metric": METRIC,
@@ -237,11 +247,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded numpy PCG64: A,B ~ N(0,1/K), bias ~ N(0,%g)%s%s)" % (
+        "dtype": "fp8->" + w.dtype if w.in8 else w.dtype,
+        "data": "synthetic (seeded numpy PCG64: %s, bias ~ N(0,%g)%s%s)" % (
+            "A,B ~ N(0,1) as FP8 E4M3 codes, ab_scale 1/sqrt(K)" if w.in8 else "A,B ~ N(0,1/K)",
             w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else "", ", R ~ N(0,1)" if w.residual else ""),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "residual": w.residual,
                    "out": w.qfmt or w.dtype, "scale": w.scale if w.qfmt else None,
+                   "operands": "fp8_e4m3" if w.in8 else w.dtype,
                    "io_dtype": w.dtype,
                    "accumulate": "f32", "tile": f"{bm}x{bn}", "tiles": tiles_m * tiles_n,
                    "tile_cfg": args.tile_cfg, "group_m": args.group_m or 4, "persistent": bool(args.persistent)},
@@ -252,8 +264,8 @@ def main():
                      "algorithmic_bytes": alg_bytes},
     }
 
-    if w.residual or w.qfmt:
-        result["unfused"] = None  # the unfused chain has no residual or quantizing pass
+    if w.residual or w.qfmt or w.in8:
+        result["unfused"] = None  # the unfused chain has no residual, quantizing or FP8 form
     elif not args.no_unfused:
         X = torch.empty_like(out)
 

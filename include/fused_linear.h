@@ -192,6 +192,30 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
                                 fl_act act, fl_dtype dtype, fl_qformat qfmt,
                                 void *stream, const fl_options *opt);
 
+/*
+ * out = act(ab_scale * (A8 @ B8) + bias): the fused linear layer with FP8
+ * operands ("Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next":
+ * the projection in FP8, which CDNA4's matrix cores run at twice the 16-bit
+ * rate and which halves the operand traffic).  A8 (M,K) and B8 (K,N) are OCP
+ * FP8 E4M3 codes, row-major; the products are summed in fp32 by
+ * v_mfma_f32_32x32x64_f8f6f4, the sum is multiplied by ab_scale (the product
+ * of the two per-tensor scales) in fp32, then bias, activation (the gate with
+ * Y), one rounding to out_dtype and one store, as fl_fused_linear.
+ *   A8, B8    device pointers to M*K and K*N bytes, 16-byte aligned.
+ *   ab_scale  finite fp32.
+ *   bias, Y, out  in out_dtype (FL_F16 or FL_BF16; FL_F32 is
+ *             FL_ERR_UNSUPPORTED), conventions as fl_fused_linear.
+ *   K and N must be multiples of 16 (FL_ERR_UNSUPPORTED otherwise); any M.
+ *   opt       tile_cfg 0 (automatic: the 8-wave 256x256 kernel, or 256x128
+ *             where fl_fused_linear would use 256-wide-by-128 tiles), 2 or 5;
+ *             others are FL_ERR_UNSUPPORTED.
+ */
+fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
+                              const void *bias, const void *Y, void *out,
+                              int64_t M, int64_t N, int64_t K, fl_act act,
+                              fl_dtype out_dtype, void *stream,
+                              const fl_options *opt);
+
 /* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
  * traffic": GEMM writes X, a bias pass reads and writes it, an activation
  * pass reads and writes it).  Each call is one launch and stores its result

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_symbols_are_exported(lib):
     text = open(HEADER).read()
-    declared = sorted(set(re.findall(r"\b(fl_[a-z_]+)\s*\(", text)))
+    declared = sorted(set(re.findall(r"\b(fl_[a-z0-9_]+)\s*\(", text)))
     assert declared, "no declarations found"
     for name in declared:
         assert hasattr(lib, name), f"{name} declared in the header but not exported"
@@ -197,3 +197,25 @@ def test_quant_rejects_bad_arguments(lib, kwargs, status, msg):
 def test_quant_degenerate_shapes_return_ok(lib):
     assert _quant(lib, out=None, M=0) == OK
     assert _quant(lib, out=None, N=0) == OK
+
+
+def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=RELU, Y=None, opt=None):
+    return lib.fl_fused_linear_fp8(A, B, ab, BIAS_P, Y, out, M, N, K, act, dt, None,
+                                   ctypes.byref(opt) if opt is not None else None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(ab=float("nan")), INVALID, "ab_scale must be finite"),
+    (dict(dt=F32), UNSUPPORTED, "fp16 or bf16"),
+    (dict(K=72), UNSUPPORTED, "multiples of 16"),
+    (dict(N=40), UNSUPPORTED, "multiples of 16"),
+    (dict(A=A_P + 8), INVALID, "16-byte aligned"),
+    (dict(A=None), INVALID, "A is NULL"),
+    (dict(out=A_P + 64), INVALID, "out overlaps A"),
+    (dict(act=GLU), INVALID, "the gate needs Y"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 9, 0, None)), UNSUPPORTED, "tile_cfg 9"),
+])
+def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):
+    assert _fp8(lib, **kwargs) == status
+    assert msg in lib.fl_last_error().decode()

@@ -429,3 +429,82 @@ def test_quant_full_size_sampled_rows():
                                        scale=w.scale, rows=rows, want_u=True)
     res = oracle.compare_quant(got[rows], ref, u, w.qfmt)
     assert res["ok"], res
+
+
+# ------------------------------------------------------------ FP8 operands
+# out = act(ab_scale * (A8@B8) + bias) through fl_fused_linear_fp8 ("Optimizing
+# GEMM + Activation on CDNA4 with TLX", "What's Next": the projection in FP8).
+
+FP8_CODES = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}  # exact small integers in OCP E4M3
+
+
+def _run_fp8(d, act, out_dtype, **opts):
+    M, K = d["A8"].shape
+    N = d["B8"].shape[1]
+    A8, B8 = (torch.from_numpy(np.ascontiguousarray(d[k])).to("cuda") for k in ("A8", "B8"))
+    bias, Y = to_dev(d["bias"], out_dtype), to_dev(d["Y"], out_dtype)
+    out, buf = sentinel_out(M, N, out_dtype)
+    fl.fused_linear_fp8(A8, B8, d["ab_scale"], bias, Y, act=act, out_dtype=TORCH_DT[out_dtype], out=out, **opts)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, M, N), "write past the end of out"
+    return to_host(out, out_dtype)
+
+
+def _fp8_integer_inputs(M, N, K, out_dtype, act, seed):
+    rng = np.random.default_rng(seed)
+    lut = np.array([FP8_CODES[v] for v in (-2, -1, 0, 1, 2)], dtype=np.uint8)
+    return {"A8": lut[rng.integers(0, 5, (M, K))], "B8": lut[rng.integers(0, 5, (K, N))], "ab_scale": 0.5,
+            "bias": synth.to_storage(rng.integers(-4, 5, N).astype(np.float64), out_dtype),
+            "Y": synth.to_storage(rng.integers(-1, 2, (M, N)).astype(np.float64), out_dtype) if act == "glu" else None}
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("shape", [(1, 16, 16), (67, 48, 64), (257, 272, 128), (513, 784, 160), (300, 528, 1008)])
+def test_fp8_integer_inputs_bit_exact(out_dtype, act, shape):
+    """Small-integer E4M3 codes, a power-of-two scale: every product and sum is
+    exact in fp32, so the output must match bit for bit (this also pins the
+    operand k-order and the transposed 8-bit reads)."""
+    M, N, K = shape
+    d = _fp8_integer_inputs(M, N, K, out_dtype, act, seed=M + N + K)
+    say("fp8 integer", out_dtype, act, shape)
+    out = _run_fp8(d, act, out_dtype)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act, out_dtype=out_dtype)
+    bad = out.view(np.uint16) != ref.view(np.uint16)
+    assert not bad.any(), (np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("shape", [(300, 528, 1008), (513, 272, 4096)])
+def test_fp8_random_inputs_within_tolerance(out_dtype, act, shape):
+    M, N, K = shape
+    d = synth.draw_fp8(M, N, K, out_dtype, act, seed=23)
+    say("fp8 random", out_dtype, act, shape)
+    out = _run_fp8(d, act, out_dtype)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act, out_dtype=out_dtype)
+    _assert_close(out, ref, out_dtype, f"fp8 {out_dtype} {act} {shape}")
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+def test_fp8_kernel_variants_bit_identical(out_dtype):
+    d = synth.draw_fp8(513, 784, 1024, out_dtype, "relu", seed=24)
+    outs = {}
+    for cfg in (0, 2, 5):
+        say("fp8 variant", cfg, out_dtype)
+        outs[cfg] = _run_fp8(d, "relu", out_dtype, tile_cfg=cfg)
+    for cfg, o in outs.items():
+        assert np.array_equal(o.view(np.uint16), outs[2].view(np.uint16)), cfg
+
+
+@pytest.mark.parametrize("name", ["glu_fp8in_f16_1024x21568x4096", "relu_fp8in_f16_4096x4096x4096"])
+def test_fp8_full_size_sampled_rows(name):
+    w = synth.WORKLOADS[name]
+    d = synth.draw_workload(w)
+    say("full size", name)
+    out = _run_fp8(d, w.act, w.dtype)
+    assert not np.isnan(oracle.decode(out, w.dtype)).any(), "unwritten (NaN sentinel) outputs"
+    rows = sample_rows(w.M)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act, out_dtype=w.dtype,
+                                  rows=rows)
+    _assert_close(out[rows], ref, w.dtype, name)
