@@ -114,7 +114,7 @@ __device__ __forceinline__ float activate(float x, float y) {
 }
 
 // The quantized store ("Triton: Fused Matmul + Bias + ReLU (Epilogue
-// Fusion)", "Variants": scale, clamp, cast to int8/fp8 before the store):
+// Fusion)", "Variants": the value is scaled, limited and written as 8-bit codes):
 // four epilogue values times the scale, in fp32, packed as four one-byte
 // codes (first value in the low byte).  FP8: clamp to the largest finite
 // E4M3 value 448, then the hardware conversion (round to nearest even, OCP

@@ -170,8 +170,8 @@ fl_status fl_fused_linear_residual(const void *A, const void *B,
 /*
  * out_q = Q(scale * act(A@B + bias)): the fused linear layer with a
  * quantized store ("Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)",
- * "Variants": a scale and a clamp applied to the accumulator's epilogue
- * value and a cast to int8/fp8 before the store).  The epilogue value is the
+ * "Variants": the epilogue value is scaled, limited to the code's range and
+ * written as 8-bit integer or FP8 codes).  The epilogue value is the
  * fp32 one fl_fused_linear would round to dtype; it is multiplied by scale
  * in fp32 and
  *   FL_Q_FP8_E4M3: clamped to [-448, 448] and rounded to nearest even on the

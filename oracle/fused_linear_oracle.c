@@ -29,10 +29,11 @@
  *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block":
  *     X = A@B + bias, out = X + X*Y.
  *   - "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants":
- *     a same-shape residual tile is added to the accumulator after the K
- *     loop, before the activation; and the quantized output: a scale and a
- *     clamp applied to the epilogue value, then a cast to int8 or fp8
- *     before the one store (see orc_fused_linear_quant).
+ *     a residual of the output's shape is summed into the accumulator after
+ *     the K loop, ahead of the activation; and the quantized output: the
+ *     epilogue value times a scale, limited to the target range and
+ *     converted to int8 or FP8 codes as it is stored (see
+ *     orc_fused_linear_quant).
  *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next" (FP8
  *     precision): the projection itself in FP8, i.e. A and B as OCP E4M3
  *     codes with a per-tensor scale, fp32 accumulation, and the same

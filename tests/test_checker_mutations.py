@@ -120,8 +120,8 @@ def test_bias_in_reduction_passes_at_k1_fails_at_k3():
 
 @pytest.mark.parametrize("mistake", ["residual_after_relu", "residual_row_broadcast", "residual_transposed"])
 def test_residual_mutant_is_flagged(mistake):
-    """The residual variant ("Variants": add the same-shape tile before the
-    activation) with the mistakes a kernel could make; each must fail the
+    """The residual variant ("Variants": the residual is summed in ahead of
+    the activation) with the mistakes a kernel could make; each must fail the
     tolerance check on the ragged workload."""
     w = synth.WORKLOADS["relu_f32_127x129x96"]
     d = synth.draw(w.M, w.N, w.K, "f32", "relu", seed=0)

@@ -301,7 +301,7 @@ def test_tile_map_rejects_bad_arguments():
 
 # -------------------------------------------------------------- residual add
 # "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a
-# same-shape residual tile is added to the accumulator after the K loop,
+# residual of the output's shape is summed into the accumulator after the K loop,
 # before the activation.
 
 def _draw_residual(M, N, dtype, seed, rmax=3):
@@ -380,9 +380,9 @@ def test_residual_fp64_value_matches_numpy():
 
 
 # ---------------------------------------------------------- quantized output
-# "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a scale
-# and a clamp applied to the epilogue value, cast to int8 / fp8 before the
-# store.  FP8 is OCP E4M3 (largest finite 448, no infinities).
+# "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": the
+# epilogue value times a scale, limited to the code's range, written as int8
+# or FP8 codes.  FP8 is OCP E4M3 (largest finite 448, no infinities).
 
 def test_e4m3_decode_every_code_matches_torch():
     codes = np.arange(256, dtype=np.uint8)
