@@ -54,11 +54,18 @@ def parse():
 
 
 def source_hash():
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that counters recorded for a kernel stay valid across comment edits and
+    become stale on any change to the code."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "activation_epilogue_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
