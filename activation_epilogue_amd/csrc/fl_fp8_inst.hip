@@ -36,6 +36,7 @@ fused_launcher pick_fp8_for<FL_INST_DTYPE>(int act, int variant) {
     static_assert(DT != FL_F32, "FP8 inputs produce fp16 or bf16 outputs");
     switch (variant) {
     case kDirect64x256W8: return pick_f8_act<DT, 256, 4>(act);
+    case kDirect64x256: return pick_f8_act<DT, 256, 2>(act);
     case kDirect64x128: return pick_f8_act<DT, 128, 2>(act);
     default: return nullptr;
     }

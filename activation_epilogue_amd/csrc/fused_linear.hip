@@ -229,7 +229,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (fp8_in) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
                                                      : fl::pick_fp8_for<FL_BF16>(act, t.variant);
-        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 2 and 5 only");
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2 and 5 only");
         f(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_fp8");
     }

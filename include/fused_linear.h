@@ -207,8 +207,8 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
  *             FL_ERR_UNSUPPORTED), conventions as fl_fused_linear.
  *   K and N must be multiples of 16 (FL_ERR_UNSUPPORTED otherwise); any M.
  *   opt       tile_cfg 0 (automatic: the 8-wave 256x256 kernel, or 256x128
- *             where fl_fused_linear would use 256-wide-by-128 tiles), 2 or 5;
- *             others are FL_ERR_UNSUPPORTED.
+ *             where fl_fused_linear would use 256-wide-by-128 tiles), 1, 2 or
+ *             5; others are FL_ERR_UNSUPPORTED.
  */
 fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               const void *bias, const void *Y, void *out,

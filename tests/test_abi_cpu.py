@@ -213,7 +213,7 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
     (dict(A=None), INVALID, "A is NULL"),
     (dict(out=A_P + 64), INVALID, "out overlaps A"),
     (dict(act=GLU), INVALID, "the gate needs Y"),
-    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
     (dict(opt=fl.Options(0, 0, 9, 0, None)), UNSUPPORTED, "tile_cfg 9"),
 ])
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):
