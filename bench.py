@@ -53,14 +53,15 @@ def parse():
     return p.parse_args()
 
 
-def source_hash():
-    """Hash of the kernel sources with comments and whitespace removed, so
-    that counters recorded for a kernel stay valid across comment edits and
-    become stale on any change to the code."""
+def source_hash(files=None):
+    """Hash of the kernel sources (all of csrc/, or the listed files) with
+    comments and whitespace removed, so that counters recorded for a kernel
+    stay valid across comment edits and become stale on any change to the
+    code it is built from."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "activation_epilogue_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files or os.listdir(csrc)):
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -79,7 +80,7 @@ def measured_traffic(workload):
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(rec.get("sources")):
         return None
     return rec.get("bytes_per_launch")
 
