@@ -113,8 +113,10 @@ struct Dma16 {
     static constexpr int KPM = F8 ? 64 : 16;         // K per MFMA (32x32x64 fp8, 32x32x16 fp16/bf16)
     static constexpr int BM = 256, BN = BN_, BK = BK_;
     static_assert(BK * IES == 64 || BK * IES == 128, "stage depth: 64- or 128-byte A rows");
-    static_assert(BN == 256 || BN == 128, "tile width");
+    static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
     static_assert(WAVES_N == 2 || WAVES_N == 4, "wave grid");
+    static_assert(BN % (32 * WAVES_N) == 0, "whole 32-column MFMA blocks per wave");
+    static_assert(BN != 192 || !F8, "the 192-wide swizzle is for 16-bit B");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
     static constexpr int NI = WN / 32;               // 32-wide MFMA blocks per wave along N
@@ -124,22 +126,32 @@ struct Dma16 {
     static constexpr int A_BYTES = BM * BK * IES;    // rows of BK*IES bytes
     static constexpr int B_BYTES = BK * BN * IES;    // rows of BN*IES bytes
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-    static constexpr int NBUF = (OCC == 2 ? 73728 : BN == 256 ? 131072 : 147456) / BUF_BYTES;  // LDS ring
+    static constexpr int LDS_RING = OCC == 2 ? 73728 : BN == 256 ? 131072 : BN == 128 ? 147456 : 163840;
+    static constexpr int NBUF = LDS_RING / BUF_BYTES;  // LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
-    static constexpr int B_ROWS_PER_COPY = 64 / CB;  // B rows per 1 KB copy
     static constexpr int NA = BM / (A_ROWS_PER_COPY * WAVES);  // A copies per wave per stage
-    static constexpr int NB = BK / (B_ROWS_PER_COPY * WAVES);  // B copies per wave per stage
+    // B: copy j of a stage covers its 16-byte chunks 64j .. 64j+63 in row
+    // order (a copy may start and end inside a row when a row is not a
+    // divisor of 1 KB).  The lane -> (row offset, chunk) pattern and the
+    // swizzle repeat every PB copies, which span B_ROWS_PER_PERIOD rows (a
+    // multiple of the swizzle's period in rows, FBP).
+    static constexpr int FBP = F8 ? 8 : 4;
+    static constexpr int pb_of(int p) { return ((64 * p) % CB == 0 && ((64 * p) / CB) % FBP == 0) ? p : pb_of(p + 1); }
+    static constexpr int PB = pb_of(2);  // 2 for every power-of-two width
+    static constexpr int B_ROWS_PER_PERIOD = 64 * PB / CB;
+    static constexpr int NB = BK * CB / (64 * WAVES);  // B copies per wave per stage
     static constexpr int DMA_PER_WAVE = NA + NB;
     static constexpr int SLOTS = 4 * NI;             // MFMAs per block
     static constexpr int RPA = F8 ? 2 : 1;           // LDS reads per A operand (16 bytes each)
     static constexpr int RPB = F8 ? 4 : 2;           // transposed 8-byte reads per B operand
     static constexpr int READS = 4 * RPA + NI * RPB; // operand reads per block
     static_assert(NA * WAVES * A_ROWS_PER_COPY == BM, "A copies cover the tile");
-    static_assert(NB * WAVES * B_ROWS_PER_COPY == BK, "B copies cover the stage");
-    // The swizzle of a copy's rows repeats with period 2 in the copy index
-    // (Lane below keeps two offsets and a stride), so each wave's first copy
-    // must have an even index: an even number of copies per wave.
-    static_assert(NA % 2 == 0 && NB % 2 == 0, "copies per wave");
+    static_assert(NB * WAVES * 64 == BK * CB, "B copies cover the stage");
+    static_assert(NB % PB == 0, "each wave's first B copy starts a swizzle period");
+    // The swizzle of an A copy's rows repeats with period 2 in the copy
+    // index (Lane below keeps two offsets and a stride), so each wave's
+    // first copy must have an even index: an even number of copies per wave.
+    static_assert(NA % 2 == 0, "A copies per wave");
     static_assert(SPREAD >= 1 && SPREAD <= KK, "copies spread over the blocks of one stage at most");
     // Copies [part_lo(p), part_lo(p+1)) of a stage form part p.
     static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPREAD; }
@@ -161,9 +173,17 @@ struct Dma16 {
     // chunks per 16 or 32 lanes).  FP8 B: fb = r % 8, so the 8 k-rows a
     // 16-lane transposed read touches (one 16-byte chunk each) fall in 8
     // different chunks.
+    //
+    // 16-bit B, BN = 192: rows of 384 bytes, so odd rows already start half
+    // a bank width (128 bytes) over; fb = r & 2 moves rows 2 and 3 of every
+    // four by two chunks, which again leaves the 4 rows x 2 chunks of a
+    // transposed read in 8 different bank groups.  An XOR below 8 keeps
+    // every chunk inside its row of 24.
     __device__ __forceinline__ static int fb(int r) {
         if constexpr (F8)
             return r & 7;
+        else if constexpr (BN == 192)
+            return r & 2;
         else
             return (0xAC60 >> (4 * (r & 3))) & 0xF;
     }
@@ -174,16 +194,16 @@ struct Dma16 {
     // (k0*2 bytes for A, k0*N*2 for B).  A lane whose chunk lies past K (or
     // past N) uses kOob so the hardware range check writes zeros; rows past
     // M are beyond num_records of A's descriptor.  Copy i of a wave covers
-    // A rows A_ROWS_PER_COPY*(wave*NA + i) + lane/CA and B k-rows
-    // B_ROWS_PER_COPY*(wave*NB + i) + lane/CB; the swizzle of those rows
-    // repeats with period 2 in i (or 1), so two offsets per operand plus a
-    // stride describe all copies.
+    // A rows A_ROWS_PER_COPY*(wave*NA + i) + lane/CA, whose swizzle repeats
+    // with period 2 in i, and B stage chunk 64*(wave*NB + i) + lane, whose
+    // row offset and swizzle repeat with period PB; so PB + 2 offsets and
+    // two strides describe all copies.
     struct Lane {
         i32x4_t rA, rB;
         uint32_t a_off[2];  // byte offset (k0 = 0) of copies i = 0, 1; +i/2 * a_step
         int a_k[2];         // K index within the stage of those chunks
-        uint32_t b_off[2];  // same for B (kOob when the columns are past N); +i/2 * b_step
-        int b_k0;           // K row within the stage of copy 0 (copy i: + B_ROWS_PER_COPY*i)
+        uint32_t b_off[PB]; // same for B (kOob when the columns are past N); +i/PB * b_step
+        int b_kr[PB];       // K row within the stage of copies i = 0..PB-1 (+i/PB * B_ROWS_PER_PERIOD)
         uint32_t a_step, b_step;
         int a_frag[KK];     // LDS byte address of A operand reads per kk (mi adds 32 rows)
         int b_frag[NI];     // LDS byte address of B operand reads per ni (kk adds 16 rows, h 4 rows)
@@ -195,18 +215,24 @@ struct Dma16 {
         L.rA = sgpr_rsrc(static_cast<const char *>(a.A) + a_org * IES, ((size_t)a.M * a.K - a_org) * IES);
         L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * IES, ((size_t)a.K * a.N - n0) * IES);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ra = A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
-            const int ca = (lane % CA) ^ fa(ra);
-            L.a_off[i] = (uint32_t)(ra * a.K + ca * EPCH) * IES;
-            L.a_k[i] = ca * EPCH;
-            const int rb = B_ROWS_PER_COPY * (wave * NB + i) + lane / CB;
-            const int cb = (lane % CB) ^ fb(rb);
-            L.b_off[i] = (n0 + cb * EPCH < a.N) ? (uint32_t)(rb * a.N + cb * EPCH) * IES : kOob;
+        for (int i = 0; i < (PB > 2 ? PB : 2); ++i) {
+            if (i < 2) {
+                const int ra = A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
+                const int ca = (lane % CA) ^ fa(ra);
+                L.a_off[i] = (uint32_t)(ra * a.K + ca * EPCH) * IES;
+                L.a_k[i] = ca * EPCH;
+            }
+            if (i < PB) {
+                // chunk q of the stage in row order: row q / CB, chunk q % CB
+                const int q = 64 * (wave * NB + i) + lane;
+                const int rb = (64 % CB == 0) ? (64 / CB) * (wave * NB + i) + lane / CB : q / CB;
+                const int cb = ((64 % CB == 0) ? lane % CB : q % CB) ^ fb(rb);
+                L.b_off[i] = (n0 + cb * EPCH < a.N) ? (uint32_t)(rb * a.N + cb * EPCH) * IES : kOob;
+                L.b_kr[i] = rb;
+            }
         }
-        L.b_k0 = B_ROWS_PER_COPY * wave * NB + lane / CB;
         L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * IES;
-        L.b_step = (uint32_t)(2 * B_ROWS_PER_COPY * a.N) * IES;
+        L.b_step = (uint32_t)(B_ROWS_PER_PERIOD * a.N) * IES;
         const int lrow = lane & 31, lg = lane >> 5;
         const int r = wm * 128 + lrow;
         const int g16 = lane >> 4, i16 = lane & 15;
@@ -240,6 +266,14 @@ struct Dma16 {
         }
     }
 
+    // K row within the stage of this lane's chunk of B copy i.
+    __device__ __forceinline__ static int b_row(const Lane &L, int i) {
+        if constexpr (64 % CB == 0)
+            return L.b_kr[0] + (64 / CB) * i;
+        else
+            return L.b_kr[i % PB] + B_ROWS_PER_PERIOD * (i / PB);
+    }
+
     struct Stage {  // scalar state of the copies of one stage
         int kleft;
         uint32_t soa, sob;
@@ -268,8 +302,8 @@ struct Dma16 {
             lds_copy16(L.rA, L.a_k[I & 1] < s.kleft ? off : kOob, s.soa, s.adst + I * 1024);
         } else {
             constexpr int i = I - NA;
-            const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
-            const bool ok = (L.b_k0 + B_ROWS_PER_COPY * i < s.kleft) && (L.b_off[i & 1] != kOob);
+            const uint32_t off = L.b_off[i % PB] + (uint32_t)(i / PB) * L.b_step;
+            const bool ok = (b_row(L, i) < s.kleft) && (L.b_off[i % PB] != kOob);
             lds_copy16(L.rB, ok ? off : kOob, s.sob, s.bdst + i * 1024);
         }
     }
@@ -321,8 +355,8 @@ struct Dma16 {
         if (a.N & 7) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                const int rb = L.b_k0 + B_ROWS_PER_COPY * i;  // K row within the stage
-                const int cb = (lane % CB) ^ fb(rb);
+                const int rb = b_row(L, i);  // K row within the stage
+                const int cb = ((64 % CB == 0) ? lane % CB : (64 * (wave * NB + i) + lane) % CB) ^ fb(rb);
                 const int col = n0 + cb * 8;
                 if (rb == kleft - 1 && col <= a.N - 1 && a.N - 1 < col + 8) {
                     const int e = a.N - 1 - col;
@@ -490,15 +524,133 @@ struct Dma16 {
     // Phase 1 (registers): bias, activation and the one conversion, exactly
     // as FusedTile::epilogue computes them (same arithmetic, same order);
     // each lane writes its 4-value groups into the wave's private LDS area
-    // (128 rows of 256 bytes, rows padded to EPI_ROW bytes so the 32 rows a
+    // (rows of WN output elements, padded to EPI_ROW bytes so the 32 rows a
     // write instruction touches fall in different banks).  Phase 2: each
     // lane reads 16 bytes of a row back and stores them, so a store
-    // instruction writes 4 whole rows of 256 bytes (full 128-byte lines).
+    // instruction writes whole rows of the wave tile (full 128-byte lines).
     static constexpr int OES = QF < 0 ? 2 : 1;  // bytes per output element
     static constexpr int EPI_ROW = WN * OES + 16;
-    static constexpr int EPI_WAVE = 128 * EPI_ROW;
+    static constexpr int EPI_ROWS = 128;  // wave rows staged
+    static constexpr int EPI_WAVE = EPI_ROWS * EPI_ROW;
     static constexpr int EPI_BYTES = WAVES * EPI_WAVE;
+    static_assert(EPI_BYTES <= (OCC == 2 ? 73728 : 163840), "epilogue staging fits in the workgroup's LDS");
     static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
+
+    // Phase 2: the wave's rows, staged at wbuf, go to out.
+    __device__ __forceinline__ static void store_rows(const GemmArgs &a, __amdgpu_buffer_rsrc_t rO, int m0, int n0,
+                                                      int wm, int wn, int lane, const FL_LDS char *wbuf) {
+        constexpr int EPC = 16 / OES;  // output elements per 16-byte chunk
+        constexpr int CPR = WN / EPC;  // 16-byte chunks per row of the wave tile
+        constexpr int BATCH = 8;       // LDS reads issued ahead of their stores
+        const int row0 = wm * 128;     // tile row of the wave's first row
+        if constexpr (64 % CPR == 0) {
+            constexpr int RPP = 64 / CPR;  // rows per store instruction
+            constexpr int PASSES = EPI_ROWS / RPP;
+            static_assert(PASSES % BATCH == 0, "whole batches");
+            const int cchunk = lane % CPR;
+            const int ccol = wn * WN + cchunk * EPC;
+            const int cvalid = a.N - n0 - ccol;
+            const FL_LDS char *rbase = wbuf + (lane / CPR) * EPI_ROW + cchunk * 16;
+            auto out_off = [&](int rr) -> uint32_t {
+                const int row = row0 + rr * RPP + lane / CPR;
+                return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * OES : kOob;
+            };
+            if (cvalid >= EPC) {
+                // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
+#pragma unroll 1
+                for (int rb = 0; rb < PASSES; rb += BATCH) {
+                    u32x4_t v[BATCH];
+#pragma unroll
+                    for (int j = 0; j < BATCH; ++j)
+                        v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
+                    if (a.stream_out) {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
+                                                                   out_off(rb + j), 0, kStreamStore);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
+                                                                   out_off(rb + j), 0, 0);
+                    }
+                }
+            } else {
+                // The chunk that holds column N-1 (and chunks past it): elements.
+#pragma unroll 1
+                for (int rr = 0; rr < PASSES; ++rr)
+                    store_chunk_elems(*(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW), rO, out_off(rr), cvalid);
+            }
+        } else {
+            // Rows of CPR chunks, CPR not a divisor of 64: pass p covers the
+            // wave's chunks 64p .. 64p+63 in row order, so a store
+            // instruction writes 64 / CPR whole rows and pieces of its
+            // neighbours' rows, still whole 128-byte lines together.
+            constexpr int PASSES = EPI_ROWS * CPR / 64;
+            constexpr int BATCH = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : 4;
+            static_assert(EPI_ROWS * CPR % 64 == 0 && PASSES % BATCH == 0, "whole passes and batches");
+            auto chunk_at = [&](int p, int &row, int &cc) {
+                const int q = p * 64 + lane;
+                row = q / CPR;
+                cc = q % CPR;
+            };
+            auto out_off = [&](int row, int col) -> uint32_t {
+                return m0 + row0 + row < a.M ? (uint32_t)((row0 + row) * a.N + col) * OES : kOob;
+            };
+            if (a.N - n0 - wn * WN >= WN) {
+                // every column of this wave's tile is below N
+#pragma unroll 1
+                for (int rb = 0; rb < PASSES; rb += BATCH) {
+                    u32x4_t v[BATCH];
+                    uint32_t off[BATCH];
+#pragma unroll
+                    for (int j = 0; j < BATCH; ++j) {
+                        int row, cc;
+                        chunk_at(rb + j, row, cc);
+                        v[j] = *(const FL_LDS u32x4_t *)(wbuf + row * EPI_ROW + cc * 16);
+                        off[j] = out_off(row, wn * WN + cc * EPC);
+                    }
+                    if (a.stream_out) {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0,
+                                                                   kStreamStore);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0, 0);
+                    }
+                }
+            } else {
+                // the wave's tile reaches past column N-1: element stores
+#pragma unroll 1
+                for (int p = 0; p < PASSES; ++p) {
+                    int row, cc;
+                    chunk_at(p, row, cc);
+                    const int col = wn * WN + cc * EPC;
+                    store_chunk_elems(*(const FL_LDS u32x4_t *)(wbuf + row * EPI_ROW + cc * 16), rO,
+                                      out_off(row, col), a.N - n0 - col);
+                }
+            }
+        }
+    }
+
+    // The elements e < cvalid of one 16-byte chunk bound for byte offset
+    // off of out (nothing for off == kOob).
+    __device__ __forceinline__ static void store_chunk_elems(const u32x4_t v, __amdgpu_buffer_rsrc_t rO, uint32_t off,
+                                                             int cvalid) {
+        constexpr int EPC = 16 / OES;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            if constexpr (OES == 2) {
+                const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+                store_elem<2>(h, rO, (off != kOob && e < cvalid) ? off + e * 2 : kOob);
+            } else {
+                const uint8_t b = (uint8_t)(v[e >> 2] >> (8 * (e & 3)));
+                __builtin_amdgcn_raw_buffer_store_b8(b, rO, (off != kOob && e < cvalid) ? off + e : kOob, 0, 0);
+            }
+        }
+    }
 
     __device__ __forceinline__ static void epilogue_lds(const GemmArgs &a, int m0, int n0, int wave, int wm, int wn,
                                                         int lane, const f32x16_t (&acc)[4][NI], FL_LDS char *lds) {
@@ -593,57 +745,7 @@ struct Dma16 {
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
         asm volatile("" ::: "memory");
-        constexpr int EPC = 16 / OES;       // output elements per 16-byte chunk
-        constexpr int CPR = WN / EPC;       // 16-byte chunks per row of the wave tile
-        constexpr int RPP = 64 / CPR;       // rows per store instruction
-        constexpr int BATCH = 8;            // LDS reads issued ahead of their stores
-        constexpr int PASSES = 128 / RPP;
-        static_assert(PASSES % BATCH == 0, "whole batches");
-        const int cchunk = lane % CPR;
-        const int ccol = wn * WN + cchunk * EPC;
-        const int cvalid = a.N - n0 - ccol;
-        const FL_LDS char *rbase = wbuf + (lane / CPR) * EPI_ROW + cchunk * 16;
-        auto out_off = [&](int rr) -> uint32_t {
-            const int row = wm * 128 + rr * RPP + lane / CPR;
-            return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * OES : kOob;
-        };
-        if (cvalid >= EPC) {
-            // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
-#pragma unroll 1
-            for (int rb = 0; rb < PASSES; rb += BATCH) {
-                u32x4_t v[BATCH];
-#pragma unroll
-                for (int j = 0; j < BATCH; ++j) v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
-                if (a.stream_out) {
-#pragma unroll
-                    for (int j = 0; j < BATCH; ++j)
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j),
-                                                               0, kStreamStore);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < BATCH; ++j)
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, out_off(rb + j),
-                                                               0, 0);
-                }
-            }
-        } else {
-            // The chunk that holds column N-1 (and chunks past it): elements.
-#pragma unroll 1
-            for (int rr = 0; rr < PASSES; ++rr) {
-                const u32x4_t v = *(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW);
-                const uint32_t off = out_off(rr);
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    if constexpr (OES == 2) {
-                        const uint16_t h = (uint16_t)((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
-                        store_elem<2>(h, rO, (off != kOob && e < cvalid) ? off + e * 2 : kOob);
-                    } else {
-                        const uint8_t b = (uint8_t)(v[e >> 2] >> (8 * (e & 3)));
-                        __builtin_amdgcn_raw_buffer_store_b8(b, rO, (off != kOob && e < cvalid) ? off + e : kOob, 0, 0);
-                    }
-                }
-            }
-        }
+        store_rows(a, rO, m0, n0, wm, wn, lane, wbuf);
     }
 
     __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {

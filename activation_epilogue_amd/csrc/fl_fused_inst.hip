@@ -50,6 +50,8 @@ fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant, boo
         case kDirect64x128: return pick_dma<DT, 64, 128>(act, residual);
         case kDirect64x256W8: return pick_dma<DT, 64, 256, 4>(act, residual);
         case kDirect32x128Occ2: return pick_dma<DT, 32, 128, 2, 2>(act, residual);
+        case kDirect64x192: return pick_dma<DT, 64, 192>(act, residual);
+        case kDirect32x192: return pick_dma<DT, 32, 192>(act, residual);
         default: break;
         }
     }

@@ -640,6 +640,8 @@ enum Variant {
     kDirect64x128 = 4,  // Dma16 BK 64, 256x128
     kDirect64x256W8 = 5,  // Dma16 BK 64, 256x256, 8 waves (two per SIMD)
     kDirect32x128Occ2 = 6,  // Dma16 BK 32, 256x128, two workgroups per CU
+    kDirect64x192 = 7,  // Dma16 BK 64, 256x192 (a width that is not a power of two), 4 waves
+    kDirect32x192 = 8,  // Dma16 BK 32, 256x192, 4 waves
 };
 
 // Returns the launcher of the fused kernel for (DT, act, variant, residual);

@@ -43,6 +43,7 @@ fused_launcher pick_quant_for<FL_INST_DTYPE>(int act, int variant, int qfmt) {
     case kDirect64x256W8: return pick_q<DT, 64, 256, 4, 1>(act, qfmt);
     case kDirect64x128: return pick_q<DT, 64, 128, 2, 1>(act, qfmt);
     case kDirect32x128Occ2: return pick_q<DT, 32, 128, 2, 2>(act, qfmt);
+    case kDirect64x192: return pick_q<DT, 64, 192, 2, 1>(act, qfmt);
     default: return nullptr;
     }
 }

@@ -76,22 +76,31 @@ struct TileShape {
 // Kernel and tile for a problem.  tile_cfg: 0 automatic, 1 256x256, 2 256x128
 // (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
 // (fp16/bf16), 5 256x256 direct with 8 waves (fp16/bf16), 6 256x128 with
-// 32-deep K stages, two workgroups per CU (fp16/bf16).  fp32 always runs the
+// 32-deep K stages, two workgroups per CU (fp16/bf16), 7 and 8 256x192 with
+// 64- and 32-deep K stages (fp16/bf16).  fp32 always runs the
 // register-staged kernel.
-// Automatic fp16/bf16 choice: the width (256 or 128) with the smaller
-// waves * relative tile time, a 256x128 tile taking 0.55 of a 256x256 one;
-// ties go to 256, which runs the 8-wave kernel (1.5-14% faster than the
-// 4-wave one on every measured shape).  Then, when the 256x128 grid fills
-// both workgroup slots of every CU, short reductions switch to the
-// two-per-CU kernel, whose epilogues and start-ups overlap the other
-// workgroup's K loop: K <= 3072 where 256x128 was chosen (measured +16% to
-// +29% at K 256..1024, +4% at 3072, -2% at 4096 on 1024x21568), K <= 512
-// where 256x256 was (+5% at 8192^2 x 512, -3% at 1024).
+// Automatic fp16/bf16 choice: the width (256, 192 or 128) with the
+// smallest waves * relative time of a wave, a wave of 256x192 tiles taking
+// 0.79 and one of 256x128 tiles 0.55 of a 256x256 wave (measured at K =
+// 4096); ties go to the wider tile.  256 runs the 8-wave kernel (1.5-14%
+// faster than the 4-wave one on every measured shape).  192 wins where the
+// 256-wide grid leaves its last wave mostly empty and the 192-wide one
+// fills it (measured +3% on 1024x21568x4096, +6% on 4096x4608x4096, +10%
+// on 3072x12288x4096 over the best power-of-two width).  Then, when the
+// 256x128 grid fills both workgroup slots of every CU, short reductions
+// switch to the two-per-CU kernel, whose epilogues and start-ups overlap
+// the other workgroup's K loop: K <= 3072 where 256x128 was chosen
+// (measured +16% to +29% at K 256..1024, +4% at 3072, -2% at 4096 on
+// 1024x21568), K <= 2048 where 256x192 was (+2% at 2048, -3% at 3072), K
+// <= 512 where 256x256 was (+5% at 8192^2 x 512, -3% at 1024).
+constexpr int64_t kOcc2MaxK192 = 2048;
+
 fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 8) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
         if (cfg == 2 || cfg == 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
+        if (cfg == 7 || cfg == 8) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x192) is fp16/bf16 only", cfg);
         t = {256, 256, fl::kRegStaged};
         return FL_OK;
     }
@@ -102,18 +111,23 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     case 4: t = {256, 256, fl::kDirect32x256}; return FL_OK;
     case 5: t = {256, 256, fl::kDirect64x256W8}; return FL_OK;
     case 6: t = {256, 128, fl::kDirect32x128Occ2}; return FL_OK;
+    case 7: t = {256, 192, fl::kDirect64x192}; return FL_OK;
+    case 8: t = {256, 192, fl::kDirect32x192}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
     const int64_t tm = (M + 255) / 256;
-    const int64_t waves256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
-    const int64_t waves128 = (tm * ((N + 127) / 128) + cus - 1) / cus;
-    const bool narrow = waves128 * 55 < waves256 * 100;
+    auto waves = [&](int64_t bn) { return (tm * ((N + bn - 1) / bn) + cus - 1) / cus; };
+    // waves x time of one wave of tiles, in hundredths of a 256x256 wave
+    const int64_t c256 = waves(256) * 100, c192 = waves(192) * 79, c128 = waves(128) * 55;
+    const int bn = (c256 <= c192 && c256 <= c128) ? 256 : (c192 <= c128 ? 192 : 128);
     const bool fills_two = tm * ((N + 127) / 128) >= 2 * cus;
-    if (fills_two && K <= (narrow ? 3072 : 512))
+    if (fills_two && K <= (bn == 256 ? 512 : bn == 192 ? kOcc2MaxK192 : 3072))
         t = {256, 128, fl::kDirect32x128Occ2};
-    else if (narrow)
+    else if (bn == 128)
         t = {256, 128, fl::kDirect64x128};
+    else if (bn == 192)
+        t = {256, 192, fl::kDirect64x192};
     else
         t = {256, 256, fl::kDirect64x256W8};
     return FL_OK;
@@ -236,7 +250,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (qfmt >= 0) {
         const fl::fused_launcher q = dtype == FL_F16 ? fl::pick_quant_for<FL_F16>(act, t.variant, qfmt)
                                                      : fl::pick_quant_for<FL_BF16>(act, t.variant, qfmt);
-        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5 and 6 only");
+        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5, 6 and 7 only");
         q(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_quant");
     }
@@ -321,12 +335,13 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (K * 256 >= 0x80000000ll) return fail(FL_ERR_UNSUPPORTED, "K too large (256 rows must span < 2 GiB)");
     if (overlaps(out, o_bytes, A8, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
     if (overlaps(out, o_bytes, B8, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
-    // The two-per-CU variant has no FP8 build: short reductions run 256x128.
+    // The two-per-CU and 256x192 variants have no FP8 build: where the
+    // automatic choice names them, 256x128 runs.
     fl_options o = opt ? *opt : fl_options{};
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(FL_F16, M, N, K, &o, t);
-        if (t.variant == fl::kDirect32x128Occ2) o.tile_cfg = 2;
+        if (t.variant == fl::kDirect32x128Occ2 || t.variant == fl::kDirect64x192) o.tile_cfg = 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }

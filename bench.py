@@ -206,8 +206,11 @@ def main():
         opts["tile_cfg"] = args.tile_cfg
     code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **opts)
-    kernel = ("fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else
-              "fused_linear_stg16_kernel" if args.tile_cfg == 5 else "fused_linear_dma16_kernel")
+    if w.in8 and not args.tile_cfg and bn != 256:
+        # the FP8 entry point runs 256x128 where the automatic choice names
+        # the two-per-CU or the 256x192 kernel (neither has an FP8 build)
+        bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **dict(opts, tile_cfg=2))
+    kernel = "fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else "fused_linear_dma16_kernel"
 
     def step():
         if w.in8:

@@ -97,10 +97,11 @@ typedef struct {
     int32_t tile_cfg;   /* Kernel and tile.  0 = automatic: fp32 runs the
                            register-staged 256x256 kernel; fp16/bf16 run the
                            direct-to-LDS kernel with 256x256 tiles (8 waves,
-                           as 6), or 256x128 (4 waves, as 2) when that takes
-                           fewer waves x relative tile time on this GPU's
-                           compute units; short reductions (K <= 3072 for a
-                           256x128 choice, K <= 512 for 256x256) whose
+                           as 5), 256x192 (as 7) or 256x128 (4 waves, as 2),
+                           whichever takes the fewest waves x relative wave
+                           time on this GPU's compute units; short
+                           reductions (K <= 3072 for a 256x128 choice, K <=
+                           2048 for 256x192, K <= 512 for 256x256) whose
                            256x128 grid fills two workgroups per compute unit
                            run as 6.  1 = 256x256 direct, 4 waves
                            (fp16/bf16; fp32 as 0); 2 = 256x128 direct
@@ -109,8 +110,10 @@ typedef struct {
                            stages; 5 = 256x256 direct with 8 waves (two per
                            SIMD, 128x64 each; fp16/bf16; fp32 as 0);
                            6 = 256x128 direct with 32-deep K stages and two
-                           workgroups per compute unit (fp16/bf16 only).
-                           Every
+                           workgroups per compute unit (fp16/bf16 only);
+                           7 and 8 = 256x192 direct (a tile width that is not
+                           a power of two, 4 waves of 128x96) with 64- and
+                           32-deep K stages (fp16/bf16 only).  Every
                            variant gives bit-identical results.  Any other
                            value, or a variant the problem does not allow,
                            is FL_ERR_UNSUPPORTED. */
@@ -181,8 +184,9 @@ fl_status fl_fused_linear_residual(const void *A, const void *B,
  *          A, B, bias or Y.
  *   scale  finite fp32 (a per-tensor output scale).
  *   dtype  FL_F16 or FL_BF16 (FL_F32 inputs are FL_ERR_UNSUPPORTED).
- *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5 or 6 (the kernels
- *          the automatic choice uses); other values are FL_ERR_UNSUPPORTED.
+ *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5, 6 or 7 (the
+ *          kernels the automatic choice uses); other values are
+ *          FL_ERR_UNSUPPORTED.
  * Errors as fl_fused_linear_ex; an unknown qfmt or a non-finite scale is
  * FL_ERR_INVALID_ARG.
  */
@@ -207,8 +211,8 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
  *             FL_ERR_UNSUPPORTED), conventions as fl_fused_linear.
  *   K and N must be multiples of 16 (FL_ERR_UNSUPPORTED otherwise); any M.
  *   opt       tile_cfg 0 (automatic: the 8-wave 256x256 kernel, or 256x128
- *             where fl_fused_linear would use 256-wide-by-128 tiles), 1, 2 or
- *             5; others are FL_ERR_UNSUPPORTED.
+ *             where fl_fused_linear would use 128- or 192-wide tiles), 1, 2
+ *             or 5; others are FL_ERR_UNSUPPORTED.
  */
 fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               const void *bias, const void *Y, void *out,

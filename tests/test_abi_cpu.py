@@ -106,7 +106,10 @@ def test_tile_grid(lib):
     assert fl.tile_grid(4096, 4096, 4096, F16) == (256, 256, 16, 16)
     assert fl.tile_grid(4097, 3071, 1537, BF16) == (256, 256, 17, 12)
     assert fl.tile_grid(8192, 14336, 4096, BF16) == (256, 256, 32, 56)
-    assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 128, 4, 169)
+    assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 192, 4, 113)
+    assert fl.tile_grid(4096, 4608, 4096, F16) == (256, 192, 16, 24)
+    assert fl.tile_grid(1024, 21568, 2048, F16) == (256, 128, 4, 169)  # two per CU
+    assert fl.tile_grid(1024, 21568, 3072, F16) == (256, 192, 4, 113)
     assert fl.tile_grid(127, 129, 96, F16) == (256, 128, 1, 2)
     assert fl.tile_grid(127, 129, 96, F32) == (256, 256, 1, 1)
     assert fl.tile_grid(1024, 21568, 4096, F16, tile_cfg=1) == (256, 256, 4, 85)
@@ -121,8 +124,14 @@ def test_tile_grid(lib):
     assert fl.tile_grid(8192, 8192, 1024, F16) == (256, 256, 32, 32)
     with pytest.raises(fl.FusedLinearError):
         fl.tile_grid(64, 64, 64, F32, tile_cfg=6)
+    # 256x192 tiles (192 = 3*64, not a power of two): N = 21568 = 112*192 + 64
+    assert fl.tile_grid(1024, 21568, 4096, F16, tile_cfg=7) == (256, 192, 4, 113)
+    assert fl.tile_grid(4097, 3071, 1537, BF16, tile_cfg=8) == (256, 192, 17, 16)
+    for cfg in (7, 8):
+        with pytest.raises(fl.FusedLinearError):
+            fl.tile_grid(64, 64, 64, F32, tile_cfg=cfg)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=7)
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=9)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
@@ -186,8 +195,8 @@ def _quant(lib, out=OUT_P, scale=1.0, q=0, dt=F16, act=RELU, Y=None, opt=None, M
     (dict(out=None), INVALID, "out is NULL"),
     (dict(out=A_P + 100), INVALID, "out overlaps A"),
     (dict(act=GLU, Y=Y_P, out=Y_P + 8191), INVALID, "out overlaps Y"),
-    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5 and 6"),
-    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5 and 6"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6 and 7"),
+    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6 and 7"),
 ])
 def test_quant_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _quant(lib, **kwargs) == status

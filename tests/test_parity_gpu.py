@@ -240,6 +240,31 @@ def test_tile_order_does_not_change_bits(name):
             assert np.array_equal(h, base), opts
 
 
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_npot_tiles_full_gate_shape(cfg):
+    """256x192 tiles (a width that is not a power of two; "Optimizing GEMM +
+    Activation on CDNA4 with TLX", "Future Work") on the gate workload
+    M=1024, N=21568, K=4096: 4 x 113 tiles, the last column of tiles 64
+    wide.  Each tile is written exactly once, sampled rows match the oracle,
+    and the whole output is bit-identical to the 256x256 kernel's."""
+    w = synth.WORKLOADS["glu_f16_1024x21568x4096"]
+    d = synth.draw_workload(w)
+    A, B, bias, Y = (to_dev(d[k], w.dtype) for k in ("A", "B", "bias", "Y"))
+    _, bn, tm, tn = fl.tile_grid(w.M, w.N, w.K, 1, tile_cfg=cfg)
+    assert (bn, tm, tn) == (192, 4, 113)
+    say("npot full", cfg)
+    counts = torch.zeros(tm * tn, dtype=torch.int32, device="cuda")
+    out = fl.fused_linear(A, B, bias, Y, act=w.act, tile_cfg=cfg, debug_tile_count=counts)
+    ref256 = fl.fused_linear(A, B, bias, Y, act=w.act, tile_cfg=1)
+    torch.cuda.synchronize()
+    assert bool((counts == 1).all().item())
+    h = to_host(out, w.dtype)
+    assert np.array_equal(h.view(np.uint8), to_host(ref256, w.dtype).view(np.uint8))
+    rows = sample_rows(w.M)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+    _assert_close(h[rows], ref, w.dtype, f"{w.name} tile_cfg {cfg}")
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = synth.WORKLOADS["relu_f16_4096x4096x4096"]
     d = synth.draw_workload(w)
@@ -267,16 +292,17 @@ def test_y_may_alias_out():
 @pytest.mark.parametrize("act", ["relu", "glu"])
 @pytest.mark.parametrize("shape", [(127, 129, 96), (300, 520, 1000), (513, 264, 72), (1024, 2048, 1024)])
 def test_kernel_variants_bit_identical_and_within_tolerance(dtype, act, shape):
-    """Every fp16/bf16 kernel variant (256x256 or 256x128 tiles, 64- or
-    32-deep K stages, 4 or 8 waves, one or two workgroups per CU, direct or
-    register-staged loads) sums each output in
-    the same k order, so results are bit-identical; each also passes the
-    oracle check."""
+    """Every fp16/bf16 kernel variant (256x256, 256x192 or 256x128 tiles,
+    64- or 32-deep K stages, 4 or 8 waves, one or two workgroups per CU,
+    direct or register-staged loads) sums each output in the same k order,
+    so results are bit-identical; each also passes the oracle check.  The
+    shapes leave ragged last tiles for every width (N = 129, 520, 264 and
+    2048 are not multiples of 192)."""
     M, N, K = shape
     d = synth.draw(M, N, K, dtype, act, seed=21)
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
     outs = {}
-    cfgs = [0, 1, 2, 3, 4, 5, 6]
+    cfgs = [0, 1, 2, 3, 4, 5, 6, 7, 8]
     for cfg in cfgs:
         say("variant", cfg, dtype, act, shape)
         outs[cfg] = _run_fused(d, act, dtype, tile_cfg=cfg)
@@ -332,7 +358,7 @@ def test_residual_kernel_variants_bit_identical(dtype, act):
     d = _with_residual(synth.draw(M, N, K, dtype, act, seed=22), dtype, seed=23)
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=d["R"])
     outs = {}
-    for cfg in range(7):
+    for cfg in range(9):
         say("residual variant", cfg, dtype, act)
         outs[cfg] = _run_fused(d, act, dtype, tile_cfg=cfg)
         _assert_close(outs[cfg], ref, dtype, f"tile_cfg {cfg}")
@@ -412,7 +438,7 @@ def test_quant_kernel_variants_identical(dtype, qfmt):
     M, N, K = 513, 770, 600
     d = synth.draw(M, N, K, dtype, "relu", seed=19)
     outs = {}
-    for cfg in (0, 2, 5, 6):
+    for cfg in (0, 2, 5, 6, 7):
         say("quant variant", cfg, dtype, qfmt)
         outs[cfg] = _run_quant(d, "relu", dtype, qfmt, 50.0, tile_cfg=cfg)
     for cfg, o in outs.items():
