@@ -523,117 +523,23 @@ struct Dma16 {
     // --- epilogue through LDS ---
     // Phase 1 (registers): bias, activation and the one conversion, exactly
     // as FusedTile::epilogue computes them (same arithmetic, same order);
-    // each lane writes its 4-value groups into the wave's private LDS area
-    // (rows of WN output elements, padded to EPI_ROW bytes so the 32 rows a
-    // write instruction touches fall in different banks).  Phase 2: each
-    // lane reads 16 bytes of a row back and stores them, so a store
-    // instruction writes whole rows of the wave tile (full 128-byte lines).
+    // each lane writes its 4-value groups into LDS (rows padded to EPI_ROW
+    // bytes so the 32 rows a write instruction touches fall in different
+    // banks).  Phase 2: each lane reads 16 bytes of a row back and stores
+    // them, so a store instruction writes whole 128-byte lines.  Where a
+    // wave's slice of an output row is a whole number of lines, each wave
+    // stages its 128 x WN tile in an area of its own and stores it; where it
+    // is not (a 192-byte slice of a 384-byte row, or 64-byte slices of
+    // one-byte codes), the waves stage the whole tile, meet at a barrier,
+    // and each stores BM / WAVES whole tile rows, so no line is written in
+    // two pieces by two waves.
     static constexpr int OES = QF < 0 ? 2 : 1;  // bytes per output element
-    static constexpr int EPI_ROW = WN * OES + 16;
-    static constexpr int EPI_ROWS = 128;  // wave rows staged
-    static constexpr int EPI_WAVE = EPI_ROWS * EPI_ROW;
-    static constexpr int EPI_BYTES = WAVES * EPI_WAVE;
+    static constexpr bool SHARED_EPI = (WN * OES) % 128 != 0;
+    static constexpr int EPI_ROW = (SHARED_EPI ? BN : WN) * OES + 16;
+    static constexpr int EPI_WAVE = 128 * EPI_ROW;  // one wave's area (own-area layout)
+    static constexpr int EPI_BYTES = SHARED_EPI ? BM * EPI_ROW : WAVES * EPI_WAVE;
     static_assert(EPI_BYTES <= (OCC == 2 ? 73728 : 163840), "epilogue staging fits in the workgroup's LDS");
     static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
-
-    // Phase 2: the wave's rows, staged at wbuf, go to out.
-    __device__ __forceinline__ static void store_rows(const GemmArgs &a, __amdgpu_buffer_rsrc_t rO, int m0, int n0,
-                                                      int wm, int wn, int lane, const FL_LDS char *wbuf) {
-        constexpr int EPC = 16 / OES;  // output elements per 16-byte chunk
-        constexpr int CPR = WN / EPC;  // 16-byte chunks per row of the wave tile
-        constexpr int BATCH = 8;       // LDS reads issued ahead of their stores
-        const int row0 = wm * 128;     // tile row of the wave's first row
-        if constexpr (64 % CPR == 0) {
-            constexpr int RPP = 64 / CPR;  // rows per store instruction
-            constexpr int PASSES = EPI_ROWS / RPP;
-            static_assert(PASSES % BATCH == 0, "whole batches");
-            const int cchunk = lane % CPR;
-            const int ccol = wn * WN + cchunk * EPC;
-            const int cvalid = a.N - n0 - ccol;
-            const FL_LDS char *rbase = wbuf + (lane / CPR) * EPI_ROW + cchunk * 16;
-            auto out_off = [&](int rr) -> uint32_t {
-                const int row = row0 + rr * RPP + lane / CPR;
-                return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * OES : kOob;
-            };
-            if (cvalid >= EPC) {
-                // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
-#pragma unroll 1
-                for (int rb = 0; rb < PASSES; rb += BATCH) {
-                    u32x4_t v[BATCH];
-#pragma unroll
-                    for (int j = 0; j < BATCH; ++j)
-                        v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
-                    if (a.stream_out) {
-#pragma unroll
-                        for (int j = 0; j < BATCH; ++j)
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
-                                                                   out_off(rb + j), 0, kStreamStore);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < BATCH; ++j)
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
-                                                                   out_off(rb + j), 0, 0);
-                    }
-                }
-            } else {
-                // The chunk that holds column N-1 (and chunks past it): elements.
-#pragma unroll 1
-                for (int rr = 0; rr < PASSES; ++rr)
-                    store_chunk_elems(*(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW), rO, out_off(rr), cvalid);
-            }
-        } else {
-            // Rows of CPR chunks, CPR not a divisor of 64: pass p covers the
-            // wave's chunks 64p .. 64p+63 in row order, so a store
-            // instruction writes 64 / CPR whole rows and pieces of its
-            // neighbours' rows, still whole 128-byte lines together.
-            constexpr int PASSES = EPI_ROWS * CPR / 64;
-            constexpr int BATCH = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : 4;
-            static_assert(EPI_ROWS * CPR % 64 == 0 && PASSES % BATCH == 0, "whole passes and batches");
-            auto chunk_at = [&](int p, int &row, int &cc) {
-                const int q = p * 64 + lane;
-                row = q / CPR;
-                cc = q % CPR;
-            };
-            auto out_off = [&](int row, int col) -> uint32_t {
-                return m0 + row0 + row < a.M ? (uint32_t)((row0 + row) * a.N + col) * OES : kOob;
-            };
-            if (a.N - n0 - wn * WN >= WN) {
-                // every column of this wave's tile is below N
-#pragma unroll 1
-                for (int rb = 0; rb < PASSES; rb += BATCH) {
-                    u32x4_t v[BATCH];
-                    uint32_t off[BATCH];
-#pragma unroll
-                    for (int j = 0; j < BATCH; ++j) {
-                        int row, cc;
-                        chunk_at(rb + j, row, cc);
-                        v[j] = *(const FL_LDS u32x4_t *)(wbuf + row * EPI_ROW + cc * 16);
-                        off[j] = out_off(row, wn * WN + cc * EPC);
-                    }
-                    if (a.stream_out) {
-#pragma unroll
-                        for (int j = 0; j < BATCH; ++j)
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0,
-                                                                   kStreamStore);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < BATCH; ++j)
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0, 0);
-                    }
-                }
-            } else {
-                // the wave's tile reaches past column N-1: element stores
-#pragma unroll 1
-                for (int p = 0; p < PASSES; ++p) {
-                    int row, cc;
-                    chunk_at(p, row, cc);
-                    const int col = wn * WN + cc * EPC;
-                    store_chunk_elems(*(const FL_LDS u32x4_t *)(wbuf + row * EPI_ROW + cc * 16), rO,
-                                      out_off(row, col), a.N - n0 - col);
-                }
-            }
-        }
-    }
 
     // The elements e < cvalid of one 16-byte chunk bound for byte offset
     // off of out (nothing for off == kOob).
@@ -668,7 +574,7 @@ struct Dma16 {
         const __amdgpu_buffer_rsrc_t rBias =
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * 2 : nullptr,
                       a.bias ? (size_t)(a.N - n0) * 2 : 0);
-        FL_LDS char *wbuf = lds + wave * EPI_WAVE;
+        FL_LDS char *wbuf = SHARED_EPI ? lds + (wm * 128) * EPI_ROW + wn * WN * OES : lds + wave * EPI_WAVE;
         const int lrow = lane & 31, lg = lane >> 5;
         int col[NG], valid[NG];
 #pragma unroll
@@ -743,9 +649,114 @@ struct Dma16 {
             // every accumulator out of the AGPRs up front and spills.
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
-        asm volatile("" ::: "memory");
-        store_rows(a, rO, m0, n0, wm, wn, lane, wbuf);
+        if constexpr (SHARED_EPI) {
+            __syncthreads();  // every wave's part of the tile is in LDS
+        } else {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are visible to itself
+            asm volatile("" ::: "memory");
+        }
+        // Phase 2, written out here: as a separate (inlined) function it
+        // made the register allocator spill in the 256-register kernels.
+        // This wave stores P_ROWS rows of P_W output elements, from tile row
+        // row0 and column col0, staged at pbase.
+        constexpr int P_ROWS = SHARED_EPI ? BM / WAVES : 128;
+        constexpr int P_W = SHARED_EPI ? BN : WN;
+        constexpr int EPC = 16 / OES;   // output elements per 16-byte chunk
+        constexpr int CPR = P_W / EPC;  // 16-byte chunks per staged row
+        constexpr int BATCH = 8;        // LDS reads issued ahead of their stores
+        const int row0 = SHARED_EPI ? wave * P_ROWS : wm * 128;
+        const int col0 = SHARED_EPI ? 0 : wn * WN;
+        const FL_LDS char *pbase = SHARED_EPI ? lds + row0 * EPI_ROW : wbuf;
+        if constexpr (64 % CPR == 0) {
+            constexpr int RPP = 64 / CPR;  // rows per store instruction
+            constexpr int PASSES = P_ROWS / RPP;
+            static_assert(PASSES % BATCH == 0, "whole batches");
+            const int cchunk = lane % CPR;
+            const int ccol = col0 + cchunk * EPC;
+            const int cvalid = a.N - n0 - ccol;
+            const FL_LDS char *rbase = pbase + (lane / CPR) * EPI_ROW + cchunk * 16;
+            auto out_off = [&](int rr) -> uint32_t {
+                const int row = row0 + rr * RPP + lane / CPR;
+                return m0 + row < a.M ? (uint32_t)(row * a.N + ccol) * OES : kOob;
+            };
+            if (cvalid >= EPC) {
+                // Whole 16-byte chunks: BATCH reads, one wait, BATCH stores.
+#pragma unroll 1
+                for (int rb = 0; rb < PASSES; rb += BATCH) {
+                    u32x4_t v[BATCH];
+#pragma unroll
+                    for (int j = 0; j < BATCH; ++j)
+                        v[j] = *(const FL_LDS u32x4_t *)(rbase + (rb + j) * RPP * EPI_ROW);
+                    if (a.stream_out) {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
+                                                                   out_off(rb + j), 0, kStreamStore);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO,
+                                                                   out_off(rb + j), 0, 0);
+                    }
+                }
+            } else {
+                // The chunk that holds column N-1 (and chunks past it): elements.
+#pragma unroll 1
+                for (int rr = 0; rr < PASSES; ++rr)
+                    store_chunk_elems(*(const FL_LDS u32x4_t *)(rbase + rr * RPP * EPI_ROW), rO, out_off(rr), cvalid);
+            }
+        } else {
+            // Rows of CPR chunks, CPR not a divisor of 64: pass p covers
+            // chunks 64p .. 64p+63 of this wave's rows in row order, so a
+            // store instruction writes 64 / CPR whole rows and pieces of its
+            // neighbours' rows, still whole 128-byte lines together.
+            constexpr int PASSES = P_ROWS * CPR / 64;
+            constexpr int BATCH = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : 4;
+            static_assert(P_ROWS * CPR % 64 == 0 && PASSES % BATCH == 0, "whole passes and batches");
+            auto chunk_at = [&](int p, int &row, int &cc) {
+                const int q = p * 64 + lane;
+                row = q / CPR;
+                cc = q % CPR;
+            };
+            auto out_off = [&](int row, int col) -> uint32_t {
+                return m0 + row0 + row < a.M ? (uint32_t)((row0 + row) * a.N + col) * OES : kOob;
+            };
+            if (a.N - n0 - col0 >= P_W) {
+                // every column this wave stores is below N
+#pragma unroll 1
+                for (int rb = 0; rb < PASSES; rb += BATCH) {
+                    u32x4_t v[BATCH];
+                    uint32_t off[BATCH];
+#pragma unroll
+                    for (int j = 0; j < BATCH; ++j) {
+                        int row, cc;
+                        chunk_at(rb + j, row, cc);
+                        v[j] = *(const FL_LDS u32x4_t *)(pbase + row * EPI_ROW + cc * 16);
+                        off[j] = out_off(row, col0 + cc * EPC);
+                    }
+                    if (a.stream_out) {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0,
+                                                                   kStreamStore);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < BATCH; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v[j]), rO, off[j], 0, 0);
+                    }
+                }
+            } else {
+                // the rows reach past column N-1: element stores
+#pragma unroll 1
+                for (int p = 0; p < PASSES; ++p) {
+                    int row, cc;
+                    chunk_at(p, row, cc);
+                    const int col = col0 + cc * EPC;
+                    store_chunk_elems(*(const FL_LDS u32x4_t *)(pbase + row * EPI_ROW + cc * 16), rO,
+                                      out_off(row, col), a.N - n0 - col);
+                }
+            }
+        }
     }
 
     __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
