@@ -101,6 +101,42 @@ def time_loop(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall / steps * 1e3
 
 
+def launch_times(fn, n, stream, scrub=None):
+    """Per-launch durations (ms) of n calls, each bracketed by its own HIP
+    events on the kernel's stream, after the timed region.  With scrub (a
+    device buffer), the buffer is overwritten before every call, so the
+    operands no longer sit in the L2 or the 256 MB MALL (a cold call)."""
+    import torch
+    evs = []
+    for _ in range(n):
+        if scrub is not None:
+            scrub.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    ts = sorted(s.elapsed_time(e) for s, e in evs)
+    return {"n": n, "median_ms": round(ts[n // 2], 4), "min_ms": round(ts[0], 4), "max_ms": round(ts[-1], 4)}
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, d, target_s):
     """Time the FP64 oracle (as it is) on a bounded sample of output rows,
     growing the sample until one call takes at least half of target_s."""
@@ -124,7 +160,7 @@ def cpu_baseline(w, d, target_s):
             break
         nrows = int(min(w.M, nrows * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
     flops = 2.0 * nrows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{nrows} of {w.M} output rows of {w.name}, FP64, evenly spaced; "
                       f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
 
@@ -228,6 +264,12 @@ def main():
             step()
         torch.cuda.synchronize()
     ms_event, ms_wall = time_loop(step, args.steps, args.warmup, stream)
+    # Outside the timed region: per-launch durations (median / min), warm and
+    # with a 512 MiB scrub buffer written before each call (cold caches).
+    warm = launch_times(step, 20, stream)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = launch_times(step, 20, stream, scrub=scrub)
+    del scrub
     if args.calib_copy_mib:
         # A plain copy of known size, outside the timed region, so that memory
         # counters taken over this run can be scaled to bytes.
@@ -273,6 +315,9 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
                      "kernel": kernel, "avg_launch_ms": round(ms_event, 4),
                      "algorithmic_bytes": alg_bytes},
+        "launches": {"warm": warm, "cold_512MiB_scrub": cold,
+                     "cold_tflops_median": round(flops / (cold["median_ms"] * 1e-3) / 1e12, 2)},
+        "device": device_info(),
     }
 
     if w.residual or w.qfmt or w.in8:
