@@ -159,6 +159,23 @@ def test_random_inputs_within_tolerance(dtype, act, shape):
     _assert_close(out, ref, dtype, f"{dtype} {act} {shape}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,act", [((1, 8200, 1024), "glu"), ((4097, 1, 300), "relu"), ((1, 1, 65536), "relu"),
+                                       ((3, 5, 100003), "gelu_tanh"), ((2, 70000, 16), "relu"),
+                                       ((70000, 24, 8), "none"), ((33, 7, 4099), "glu")])
+def test_extreme_shapes(dtype, shape, act):
+    """Degenerate tile grids: one output row or column, a single output,
+    reductions of 65536 and of a prime length, and very wide or very tall
+    outputs (one tile deep in one direction, hundreds in the other).  The
+    whole output is compared and nothing is written past it."""
+    M, N, K = shape
+    d = synth.draw(M, N, K, dtype, act, bias_var=0.1 if act == "gelu_tanh" else 1.0, seed=31)
+    say("extreme shape", dtype, act, shape)
+    out = _run_fused(d, act, dtype)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    _assert_close(out, ref, dtype, f"{dtype} {act} {shape}")
+
+
 def test_relu_f32_127x129x96_full():
     w = synth.WORKLOADS["relu_f32_127x129x96"]
     d = synth.draw_workload(w)
