@@ -20,6 +20,9 @@ Sources (page title, section):
   * "Triton: Fused Matmul + Bias + ReLU (Epilogue Fusion)", "Variants": a
     same-shape residual added to the accumulator before the activation.
   * GELU(tanh): not printed on the pages; Hendrycks & Gimpel (2016).
+  * "Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work": the
+    epilogue fusion in the backward pass (``fused_linear_bwd``; derivatives
+    by the chain rule from the forward definitions).
 """
 from __future__ import annotations
 
@@ -82,6 +85,10 @@ def _load():
             lib.orc_tile_of_pid.argtypes = [i64, i64, i64, i64, p, p]
             lib.orc_gelu_tanh.argtypes = [ctypes.c_double]
             lib.orc_gelu_tanh.restype = ctypes.c_double
+            lib.orc_gelu_tanh_grad.argtypes = [ctypes.c_double]
+            lib.orc_gelu_tanh_grad.restype = ctypes.c_double
+            lib.orc_fused_linear_bwd.argtypes = [c_int, c_int, p, p, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
+            lib.orc_fused_linear_bwd.restype = c_int
             lib.orc_max_threads.restype = c_int
             _lib = lib
     return _lib
@@ -195,6 +202,53 @@ def fused_linear_fp8(A8, B8, ab_scale, bias, Y=None, act="relu", out_dtype="f16"
     if st != 0:
         raise RuntimeError(f"orc_fused_linear_fp8 failed with status {st}")
     return (out, x) if want_x else out
+
+
+def gelu_tanh_grad(x):
+    return _load().orc_gelu_tanh_grad(float(x))
+
+
+def fused_linear_bwd(G, W, X, Y=None, act="relu", dtype="f16", rows=None, threads=None, want_dx=False):
+    """Backward epilogue: D = G @ W^T (G (M,K), W (N,K), FP64), then
+    dX = round(D * act'(X)), for the gate also dY = round(D * X), and
+    dbias = sum over rows of the unrounded dX (FP64; over the selected rows
+    when ``rows`` is given).  X and Y (M,N) are the saved forward values.
+    Returns (dX, dY or None, dbias[, unrounded dX])."""
+    lib = _load()
+    G, W, X, Y = (_raw(a, dtype) for a in (G, W, X, Y))
+    M, K = G.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError("G is (M,K) and W is (N,K)")
+    if X.shape != (M, N):
+        raise ValueError("X must be (M,N)")
+    if act == "glu" and (Y is None or Y.shape != (M, N)):
+        raise ValueError("the gate needs Y of shape (M,N)")
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = M if rows_arr is None else rows_arr.size
+    dX = np.empty((nrows, N), dtype=STORAGE[dtype])
+    dY = np.empty((nrows, N), dtype=STORAGE[dtype]) if act == "glu" else None
+    dbias = np.empty(N, dtype=np.float64)
+    dx = np.empty((nrows, N), dtype=np.float64) if want_dx else None
+    st = lib.orc_fused_linear_bwd(DTYPES[dtype], ACTS[act], _ptr(G), _ptr(W), _ptr(X), _ptr(Y), _ptr(dX), _ptr(dY),
+                                  _ptr(dbias), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(dx))
+    if st != 0:
+        raise RuntimeError(f"orc_fused_linear_bwd failed with status {st}")
+    return (dX, dY, dbias, dx) if want_dx else (dX, dY, dbias)
+
+
+def compare_dbias(dev, ref, abs_colsum, M):
+    """Bias-gradient parity: |dev - ref| <= (M * 2^-24 + 1e-4) * sum_i |dX[i,j]|
+    + 1e-6 per column: the worst-case error of an fp32 sum of M terms
+    (M * unit roundoff, relative to the sum of magnitudes) plus 1e-4 for the
+    fp32 accumulation and epilogue of each term."""
+    dev = np.asarray(dev, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    tol = (M * 2.0 ** -24 + 1e-4) * np.asarray(abs_colsum, dtype=np.float64) + 1e-6
+    err = np.abs(dev - ref)
+    bad = err > tol
+    return {"ok": not bad.any(), "violations": int(bad.sum()), "max_abs_err": float(err.max(initial=0.0)),
+            "worst": int(np.argmax(err / tol)) if err.size else -1}
 
 
 def quantize(u, qfmt):

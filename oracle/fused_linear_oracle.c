@@ -38,6 +38,10 @@
  *     precision): the projection itself in FP8, i.e. A and B as OCP E4M3
  *     codes with a per-tensor scale, fp32 accumulation, and the same
  *     epilogue in the 16-bit output dtype (see orc_fused_linear_fp8).
+ *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work":
+ *     the epilogue fusion carried over to the backward pass (see
+ *     orc_fused_linear_bwd; the derivatives follow from the forward
+ *     definitions by the chain rule).
  *   - GELU: the pages name it as a fusable activation but print no formula;
  *     this file uses the tanh form of Hendrycks & Gimpel (2016),
  *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with libm tanh.
@@ -438,6 +442,111 @@ int orc_fused_linear_fp8(int out_dtype, int act, const uint8_t *A8,
         free(arow);
     }
     free(B64);
+    return status;
+}
+
+/* ---------------------------------------------------- backward epilogue */
+
+/* Derivative of the tanh-form GELU, from the product and chain rules:
+ * with u = c (x + a x^3) and t = tanh(u),
+ * g'(x) = 0.5 (1 + t) + 0.5 x (1 - t^2) c (1 + 3 a x^2). */
+double orc_gelu_tanh_grad(double x) {
+    const double c = sqrt(2.0 / M_PI), a = 0.044715;
+    const double t = tanh(c * (x + a * x * x * x));
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * a * x * x);
+}
+
+/* d act(x) / dx; for the gate X + X*Y the derivative in X is 1 + Y.  ReLU's
+ * derivative is taken as 0 at x = 0 (max(0, x) has no derivative there; the
+ * usual subgradient choice). */
+static double act_grad(int act, double x, double y) {
+    switch (act) {
+    case ORC_RELU: return x > 0.0 ? 1.0 : 0.0;
+    case ORC_GELU_TANH: return orc_gelu_tanh_grad(x);
+    case ORC_GLU: return 1.0 + y;
+    default: return 1.0;
+    }
+}
+
+/*
+ * Backward of out = act(X) fused into the epilogue of the GEMM that brings
+ * its incoming gradient ("Optimizing GEMM + Activation on CDNA4 with TLX",
+ * "Future Work": the same epilogue fusion in the backward pass).  For a
+ * layer whose output feeds a product with a weight W (N, K) row-major (the
+ * next layer's B, so its transpose is taken), the gradient of the loss with
+ * respect to out is D = G @ W^T, G (M, K) the gradient at the next layer's
+ * pre-activation.  By the chain rule
+ *   D[i,j]   = sum_k G[i,k] * W[j,k]        (FP64, k ascending)
+ *   dX[i,j]  = D[i,j] * act'(X[i,j])        (X: the saved pre-activation)
+ *   dY[i,j]  = D[i,j] * X[i,j]              (the gate only: d(X + X*Y)/dY)
+ *   dbias[j] = sum_i dX[i,j]                (X = A@B + bias, so the bias
+ *                                            gradient is dX summed over rows;
+ *                                            FP64 sum of unrounded dX)
+ * dX and dY are rounded once to dtype.  rows / nrows select output rows as
+ * in orc_fused_linear; dbias then sums the selected rows only.  dx_out, when
+ * not NULL, receives the unrounded dX (nrows x N).
+ */
+int orc_fused_linear_bwd(int dtype, int act, const void *G, const void *W,
+                         const void *X, const void *Y, void *dX, void *dY,
+                         double *dbias, int64_t M, int64_t N, int64_t K,
+                         const int64_t *rows, int64_t nrows, int nthreads,
+                         double *dx_out) {
+    if (dtype < 0 || dtype > 2 || act < 0 || act > 3) return 1;
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if ((!G && M * K > 0) || (!W && N * K > 0) || (!X && M * N > 0) || (!dX && M * N > 0)) return 1;
+    if (act == ORC_GLU && (!Y || !dY) && M * N > 0) return 1;
+    if (!rows) nrows = M;
+    if (nrows < 0) return 1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= M) return 1;
+    if (dbias)
+        for (int64_t j = 0; j < N; ++j) dbias[j] = 0.0;
+    if (nrows == 0 || N == 0) return 0;
+    double *W64 = (double *)malloc(sizeof(double) * (size_t)(N * K + 1));
+    double *D = (double *)malloc(sizeof(double) * (size_t)(nrows * N));
+    if (!W64 || !D) { free(W64); free(D); return 2; }
+    orc_decode(dtype, W, N * K, W64);
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *grow = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+        if (!grow) {
+#pragma omp atomic write
+            status = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t i = rows ? rows[r] : r;
+                for (int64_t k = 0; k < K; ++k) grow[k] = dec_one(dtype, G, i * K + k);
+                for (int64_t j = 0; j < N; ++j) {
+                    double d = 0.0;
+                    const double *w = W64 + j * K;
+                    for (int64_t k = 0; k < K; ++k) d += grow[k] * w[k];
+                    const double x = dec_one(dtype, X, i * N + j);
+                    const double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
+                    const double dx = d * act_grad(act, x, y);
+                    D[r * N + j] = dx;
+                    if (dx_out) dx_out[r * N + j] = dx;
+                    enc_one(dtype, dx, dX, r * N + j);
+                    if (act == ORC_GLU) enc_one(dtype, d * x, dY, r * N + j);
+                }
+            }
+        }
+        free(grow);
+    }
+    /* the column sums in row order, one thread, so the result does not
+       depend on the thread count */
+    if (dbias && status == 0)
+        for (int64_t r = 0; r < nrows; ++r)
+            for (int64_t j = 0; j < N; ++j) dbias[j] += D[r * N + j];
+    free(W64);
+    free(D);
     return status;
 }
 

@@ -514,3 +514,127 @@ def test_fp8_inputs_match_decoded_matmul():
     A = torch.from_numpy(A8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     B = torch.from_numpy(B8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     np.testing.assert_allclose(x, A @ B * 0.125 + oracle.decode(bias, "bf16")[None, :], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------ backward epilogue
+# D = G @ W^T; dX = D * act'(X); dY = D * X (gate); dbias = sum_i dX
+# ("Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work").
+
+def _bwd_integer(M, N, K, dtype, act, seed):
+    rng = np.random.default_rng(seed)
+    G = rng.integers(-2, 3, (M, K)).astype(np.float64)
+    W = rng.integers(-2, 3, (N, K)).astype(np.float64)
+    X = rng.integers(-3, 4, (M, N)).astype(np.float64)  # includes exact zeros
+    Y = rng.integers(-2, 3, (M, N)).astype(np.float64)
+    return {k: synth.to_storage(v, dtype) for k, v in dict(G=G, W=W, X=X, Y=Y).items()}, (G, W, X, Y)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+def test_bwd_integer_inputs_brute_force(dtype, act):
+    """Small integers make every value exact in every dtype: int64 brute
+    force of the chain rule (ReLU's derivative 0 at X = 0)."""
+    M, N, K = 37, 29, 7
+    s, (G, W, X, Y) = _bwd_integer(M, N, K, dtype, act, seed=3)
+    dX, dY, dbias = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act=act, dtype=dtype)
+    D = (G.astype(np.int64) @ W.astype(np.int64).T)
+    grad = {"none": np.ones_like(X), "relu": (X > 0).astype(np.float64), "glu": 1 + Y}[act]
+    want = D * grad
+    assert np.array_equal(oracle.decode(dX, dtype), want)
+    assert np.array_equal(dbias, want.sum(axis=0))
+    if act == "glu":
+        assert np.array_equal(oracle.decode(dY, dtype), D * X)
+    else:
+        assert dY is None
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+def test_bwd_matches_torch_autograd_float64(act):
+    """The derivative from an independent implementation: torch autograd in
+    float64 of loss = sum(act(X) * D) with X = A@B + bias as leaves."""
+    M, N, K, Kf = 19, 23, 11, 13
+    rng = np.random.default_rng(7)
+    A, B = rng.standard_normal((M, Kf)), rng.standard_normal((Kf, N))
+    bias, Y = rng.standard_normal(N), rng.uniform(-1, 1, (M, N))
+    G, W = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    tA, tB, tb, tY = (torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in (A, B, bias, Y))
+    Xt = tA @ tB + tb
+    Xt.retain_grad()
+    out = {"none": Xt, "relu": torch.relu(Xt), "gelu_tanh": torch.nn.functional.gelu(Xt, approximate="tanh"),
+           "glu": Xt + Xt * tY}[act]
+    D = torch.tensor(G @ W.T)
+    (out * D).sum().backward()
+    X = Xt.detach().numpy()
+    s = {k: synth.to_storage(v, "f32") for k, v in dict(G=G, W=W, X=X, Y=Y).items()}
+    # the oracle sees the inputs rounded to f32: compare against torch on those
+    Xf, Yf = (oracle.decode(s[k], "f32") for k in ("X", "Y"))
+    Gf, Wf = (oracle.decode(s[k], "f32") for k in ("G", "W"))
+    dX, dY, dbias, dx = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="f32", want_dx=True)
+    tX2 = torch.tensor(Xf, requires_grad=True)
+    tY2 = torch.tensor(Yf, requires_grad=True)
+    out2 = {"none": tX2, "relu": torch.relu(tX2), "gelu_tanh": torch.nn.functional.gelu(tX2, approximate="tanh"),
+            "glu": tX2 + tX2 * tY2}[act]
+    (out2 * torch.tensor(Gf @ Wf.T)).sum().backward()
+    assert np.allclose(dx, tX2.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dbias, tX2.grad.numpy().sum(axis=0), rtol=1e-12, atol=1e-12)
+    if act == "glu":
+        assert np.allclose(oracle.decode(dY, "f32"), tY2.grad.numpy(), rtol=1e-6, atol=1e-6)
+    # and the bias gradient is the gradient of the leaf bias of X = A@B + bias
+    assert np.allclose(tb.grad.numpy(), Xt.grad.numpy().sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_gelu_tanh_grad_central_differences():
+    """The closed-form derivative against central differences of the forward
+    GELU (h = 1e-5: truncation ~h^2, cancellation ~1e-16/h)."""
+    h = 1e-5
+    for x in np.concatenate([np.linspace(-8, 8, 161), [0.0, 1e-3, -1e-3, 0.7071]]):
+        fd = (oracle.gelu_tanh(x + h) - oracle.gelu_tanh(x - h)) / (2 * h)
+        assert abs(oracle.gelu_tanh_grad(x) - fd) < 1e-8, x
+    assert oracle.gelu_tanh_grad(0.0) == 0.5
+
+
+def test_bwd_rows_subset_and_threads():
+    s, _ = _bwd_integer(40, 33, 9, "f16", "glu", seed=4)
+    full = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act="glu", dtype="f16", threads=1)
+    rows = np.array([0, 5, 39, 17])
+    sub = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act="glu", dtype="f16", rows=rows, threads=4)
+    assert np.array_equal(sub[0], full[0][rows]) and np.array_equal(sub[1], full[1][rows])
+    dx = oracle.decode(full[0], "f16")
+    assert np.array_equal(sub[2], dx[rows].sum(axis=0))
+
+
+@pytest.mark.parametrize("mistake", ["act_not_derivative", "w_not_transposed", "dbias_over_columns",
+                                     "gate_derivative_y", "relu_grad_at_zero_one", "dy_uses_y"])
+def test_bwd_checker_flags_planted_mistakes(mistake):
+    """Mistakes a backward epilogue could make, planted in a numpy copy of
+    the definition, must fail the parity checks against the oracle."""
+    M = N = K = 24  # square, so an untransposed W still has the right shape
+    act = "glu" if mistake in ("gate_derivative_y", "dy_uses_y") else "relu"
+    s, (G, W, X, Y) = _bwd_integer(M, N, K, "f32", act, seed=9)
+    dX, dY, dbias = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="f32")
+    D = G @ W.T
+    relu_grad = (X > 0).astype(np.float64)
+    bad_dX, bad_dY, bad_db = None, None, None
+    if mistake == "act_not_derivative":
+        bad_dX = D * np.maximum(X, 0.0)
+    elif mistake == "w_not_transposed":
+        bad_dX = (G @ W) * relu_grad
+    elif mistake == "dbias_over_columns":
+        bad_db = (D * relu_grad).sum(axis=1)
+    elif mistake == "gate_derivative_y":
+        bad_dX = D * Y
+    elif mistake == "relu_grad_at_zero_one":
+        bad_dX = D * (X >= 0)
+    elif mistake == "dy_uses_y":
+        bad_dY = D * Y
+    if bad_dX is not None:
+        assert not oracle.compare(bad_dX.astype(np.float32), dX, "f32")["ok"]
+    if bad_dY is not None:
+        assert not oracle.compare(bad_dY.astype(np.float32), dY, "f32")["ok"]
+    if bad_db is not None:
+        absum = np.abs(oracle.decode(dX, "f32")).sum(axis=0)
+        assert not oracle.compare_dbias(bad_db, dbias, absum, M)["ok"]
+    # the correct values pass the same checks
+    good = D * ((1 + Y) if act == "glu" else relu_grad)
+    assert oracle.compare(good.astype(np.float32), dX, "f32")["ok"]
+    assert oracle.compare_dbias(good.sum(axis=0), dbias, np.abs(good).sum(axis=0), M)["ok"]
