@@ -14,6 +14,8 @@ Entry points (same names as the C ABI, without the ``fl_`` prefix):
                                           # uint8 codes of Q(scale * act(A@B + bias))
   fused_linear_fp8(A8, B8, ab_scale, bias=None, Y=None, act="relu", out_dtype=torch.float16, out=None, **options)
                                           # FP8 E4M3 operands, 16-bit epilogue and output
+  fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, **options)
+                                          # backward epilogue: dX = (G @ W^T) * act'(X), gate dY, dbias
   gemm(A, B, X=None)                      # unfused step 1: X = A@B
   bias_add(X, bias)                       # unfused step 2: X += bias (in place)
   activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
@@ -30,7 +32,7 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
 EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
-           "fl_fused_linear_fp8", "fl_gemm", "fl_bias_add", "fl_activation",
+           "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_gemm", "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
 
@@ -71,6 +73,8 @@ def load_library():
     lib.fl_fused_linear_quant.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i64, i64, i64, c_int, c_int, c_int, vp,
                                           ctypes.POINTER(Options)]
     lib.fl_fused_linear_fp8.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
+                                        ctypes.POINTER(Options)]
+    lib.fl_fused_linear_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
                                         ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
@@ -216,6 +220,35 @@ def fused_linear_fp8(A8, B8, ab_scale, bias=None, Y=None, act="relu", out_dtype=
         _dev_ptr(out, "out", out_dtype, (M, N)), M, N, K, ACTS[act], _dtype_code(out_dtype), _stream(A8, stream),
         ctypes.byref(opt)))
     return out
+
+
+def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, *, stream=None, **options):
+    """The backward epilogue (fl_fused_linear_bwd): D = G @ W^T with G (M,K)
+    and W (N,K), then dX = D * act'(X) at the saved pre-activation X (M,N),
+    for the gate also dY = D * X, and dbias = column sums of dX (fp32).
+    dbias=True allocates the (N,) fp32 result, a tensor is overwritten,
+    None/False skips it.  Returns (dX, dY or None, dbias or None)."""
+    import torch
+    lib = load_library()
+    if G.dim() != 2 or W.dim() != 2 or G.shape[1] != W.shape[1]:
+        raise ValueError("G must be (M,K) and W (N,K)")
+    M, K = G.shape
+    N = W.shape[0]
+    dt = G.dtype
+    if dX is None:
+        dX = torch.empty((M, N), dtype=dt, device=G.device)
+    if act == "glu" and dY is None:
+        dY = torch.empty((M, N), dtype=dt, device=G.device)
+    if dbias is True:
+        dbias = torch.empty((N,), dtype=torch.float32, device=G.device)
+    elif dbias is False:
+        dbias = None
+    opt = _options(**options)
+    _check(lib.fl_fused_linear_bwd(
+        _dev_ptr(G, "G", dt), _dev_ptr(W, "W", dt, (N, K)), _dev_ptr(X, "X", dt, (M, N)), _dev_ptr(Y, "Y", dt, (M, N)),
+        _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)), _dev_ptr(dbias, "dbias", torch.float32, (N,)),
+        M, N, K, ACTS[act], _dtype_code(dt), _stream(G, stream), ctypes.byref(opt)))
+    return dX, dY, dbias
 
 
 def gemm(A, B, X=None, *, stream=None):

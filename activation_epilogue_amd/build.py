@@ -1,9 +1,10 @@
 """Build libfused_linear.so for gfx950 with hipcc, in-tree.
 
-Eight translation units compiled in parallel: the host/ABI unit (with the
+Ten translation units compiled in parallel: the host/ABI unit (with the
 elementwise kernels), one unit of fused GEMM kernels per dtype, one of
-quantized-output kernels per 16-bit dtype and one of FP8-input kernels per
-16-bit output dtype; then the
+quantized-output kernels per 16-bit dtype, one of FP8-input kernels per
+16-bit output dtype and one of backward-epilogue kernels per 16-bit dtype;
+then the
 separate MFMA-rate probe library used by the benchmark.  Every
 device compile carries -Xclang -target-feature -Xclang -packed-fp32-ops so
 that no packed fp32 instructions are generated.
@@ -37,6 +38,8 @@ UNITS = [
     ("fl_quant_inst.hip", ["-DFL_INST_DTYPE=2"]),
     ("fl_fp8_inst.hip", ["-DFL_INST_DTYPE=1"]),
     ("fl_fp8_inst.hip", ["-DFL_INST_DTYPE=2"]),
+    ("fl_bwd_inst.hip", ["-DFL_INST_DTYPE=1"]),
+    ("fl_bwd_inst.hip", ["-DFL_INST_DTYPE=2"]),
 ]
 
 

@@ -102,12 +102,16 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // FL_Q_INT8 store one-byte codes of the epilogue value times a.scale.  IN:
 // the type of A and B, DT (fp16/bf16) or kInFp8 (OCP E4M3 codes, fp8 MFMA,
 // the accumulator scaled by a.ab_scale before the bias; bias, Y and out
-// stay in DT).
+// stay in DT).  BWD: the backward epilogue (see epilogue_lds), with B given
+// as (N, K) row-major (the weight read as its transpose): its tile is
+// staged and read exactly like A's, and a lane's 16-byte read of a row is
+// already the MFMA's B fragment (8 consecutive k of one column).
 template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false,
-          int QF = -1, int IN = DT>
+          int QF = -1, int IN = DT, bool BWD = false>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr bool F8 = IN == kInFp8;
+    static constexpr bool BT = BWD;  // B is (N, K) row-major, K contiguous
     static constexpr int IES = F8 ? 1 : 2;           // bytes per A/B element
     static constexpr int EPCH = 16 / IES;            // A/B elements per 16-byte chunk
     static constexpr int KPM = F8 ? 64 : 16;         // K per MFMA (32x32x64 fp8, 32x32x16 fp16/bf16)
@@ -140,14 +144,18 @@ struct Dma16 {
     static constexpr int PB = pb_of(2);  // 2 for every power-of-two width
     static constexpr int B_ROWS_PER_PERIOD = 64 * PB / CB;
     static constexpr int NB = BK * CB / (64 * WAVES);  // B copies per wave per stage
+    static constexpr int B_ROWS_PER_COPY_T = 64 / CA;  // K-contiguous B: its rows per 1 KB copy
     static constexpr int DMA_PER_WAVE = NA + NB;
     static constexpr int SLOTS = 4 * NI;             // MFMAs per block
     static constexpr int RPA = F8 ? 2 : 1;           // LDS reads per A operand (16 bytes each)
-    static constexpr int RPB = F8 ? 4 : 2;           // transposed 8-byte reads per B operand
+    static constexpr int RPB = F8 ? 4 : BT ? 1 : 2;  // reads per B operand (transposed 8-byte, or one 16-byte)
+    static constexpr int BPARTS = F8 ? 4 : 2;        // 8-byte parts of a B operand
     static constexpr int READS = 4 * RPA + NI * RPB; // operand reads per block
     static_assert(NA * WAVES * A_ROWS_PER_COPY == BM, "A copies cover the tile");
     static_assert(NB * WAVES * 64 == BK * CB, "B copies cover the stage");
     static_assert(NB % PB == 0, "each wave's first B copy starts a swizzle period");
+    static_assert(!BT || (NB * WAVES * B_ROWS_PER_COPY_T == BN && NB % 2 == 0 && !F8 && QF < 0 && !RES),
+                  "K-contiguous B: A-like copies with period 2; 16-bit operands, plain output");
     // The swizzle of an A copy's rows repeats with period 2 in the copy
     // index (Lane below keeps two offsets and a stride), so each wave's
     // first copy must have an even index: an even number of copies per wave.
@@ -204,16 +212,21 @@ struct Dma16 {
         int a_k[2];         // K index within the stage of those chunks
         uint32_t b_off[PB]; // same for B (kOob when the columns are past N); +i/PB * b_step
         int b_kr[PB];       // K row within the stage of copies i = 0..PB-1 (+i/PB * B_ROWS_PER_PERIOD)
+        int b_k[2];         // K-contiguous B: K index within the stage of copies 0, 1 (as a_k)
         uint32_t a_step, b_step;
         int a_frag[KK];     // LDS byte address of A operand reads per kk (mi adds 32 rows)
-        int b_frag[NI];     // LDS byte address of B operand reads per ni (kk adds 16 rows, h 4 rows)
+        int b_frag[BT ? KK : NI];  // B operand reads per ni (kk adds 16 rows, h 4 rows); per kk when K-contiguous
     };
 
     __device__ __forceinline__ static void setup(const GemmArgs &a, int m0, int n0, int wave, int lane, int wm,
                                                  int wn, Lane &L) {
         const size_t a_org = (size_t)m0 * a.K;
         L.rA = sgpr_rsrc(static_cast<const char *>(a.A) + a_org * IES, ((size_t)a.M * a.K - a_org) * IES);
-        L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * IES, ((size_t)a.K * a.N - n0) * IES);
+        if constexpr (BT)
+            L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * a.K * IES,
+                             ((size_t)a.N * a.K - (size_t)n0 * a.K) * IES);
+        else
+            L.rB = sgpr_rsrc(static_cast<const char *>(a.B) + (size_t)n0 * IES, ((size_t)a.K * a.N - n0) * IES);
 #pragma unroll
         for (int i = 0; i < (PB > 2 ? PB : 2); ++i) {
             if (i < 2) {
@@ -222,7 +235,14 @@ struct Dma16 {
                 L.a_off[i] = (uint32_t)(ra * a.K + ca * EPCH) * IES;
                 L.a_k[i] = ca * EPCH;
             }
-            if (i < PB) {
+            if (BT && i < 2) {
+                // as A: rows of B^T (output columns), chunks along K
+                const int rb = B_ROWS_PER_COPY_T * (wave * NB + i) + lane / CA;
+                const int cb = (lane % CA) ^ fa(rb);
+                L.b_off[i] = (uint32_t)(rb * a.K + cb * EPCH) * IES;
+                L.b_k[i] = cb * EPCH;
+            }
+            if (!BT && i < PB) {
                 // chunk q of the stage in row order: row q / CB, chunk q % CB
                 const int q = 64 * (wave * NB + i) + lane;
                 const int rb = (64 % CB == 0) ? (64 / CB) * (wave * NB + i) + lane / CB : q / CB;
@@ -232,11 +252,20 @@ struct Dma16 {
             }
         }
         L.a_step = (uint32_t)(2 * A_ROWS_PER_COPY * a.K) * IES;
-        L.b_step = (uint32_t)(B_ROWS_PER_PERIOD * a.N) * IES;
+        L.b_step = BT ? (uint32_t)(2 * B_ROWS_PER_COPY_T * a.K) * IES : (uint32_t)(B_ROWS_PER_PERIOD * a.N) * IES;
         const int lrow = lane & 31, lg = lane >> 5;
         const int r = wm * 128 + lrow;
         const int g16 = lane >> 4, i16 = lane & 15;
-        if constexpr (!F8) {
+        if constexpr (BT) {
+            // rows of the B^T tile are output columns; fa depends on the row
+            // modulo 16 only, so one address per kk serves every ni (+32 rows)
+            const int rn = wn * WN + lrow;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
+                L.b_frag[kk] = A_BYTES + rn * (BK * 2) + (((kk * 2 + lg) ^ fa(rn)) * 16);
+            }
+        } else if constexpr (!F8) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
             const int rk = (g16 >> 1) * 8 + (i16 >> 2);  // k-row for kk = 0, h = 0
@@ -285,7 +314,7 @@ struct Dma16 {
         Stage s;
         s.kleft = a.K - k0;
         s.soa = (uint32_t)k0 * IES;
-        s.sob = (uint32_t)k0 * (uint32_t)a.N * IES;
+        s.sob = BT ? (uint32_t)k0 * IES : (uint32_t)k0 * (uint32_t)a.N * IES;
         s.adst = __builtin_amdgcn_readfirstlane(buf_addr + wave * NA * 1024);
         s.bdst = __builtin_amdgcn_readfirstlane(buf_addr + A_BYTES + wave * NB * 1024);
         return s;
@@ -300,6 +329,10 @@ struct Dma16 {
         if constexpr (I < NA) {
             const uint32_t off = L.a_off[I & 1] + (uint32_t)(I >> 1) * L.a_step;
             lds_copy16(L.rA, L.a_k[I & 1] < s.kleft ? off : kOob, s.soa, s.adst + I * 1024);
+        } else if constexpr (BT) {
+            constexpr int i = I - NA;
+            const uint32_t off = L.b_off[i & 1] + (uint32_t)(i >> 1) * L.b_step;
+            lds_copy16(L.rB, L.b_k[i & 1] < s.kleft ? off : kOob, s.sob, s.bdst + i * 1024);
         } else {
             constexpr int i = I - NA;
             const uint32_t off = L.b_off[i % PB] + (uint32_t)(i / PB) * L.b_step;
@@ -352,7 +385,32 @@ struct Dma16 {
                 *(FL_LDS u32x4_t *)p = v;
             }
         }
-        if (a.N & 7) {
+        if constexpr (BT) {
+            // B^T rows are K-contiguous like A's: the same two fixes
+            const i32x4_t rBt = sgpr_rsrc(a.B, (size_t)a.N * a.K * 2);
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int kb = L.b_k[i & 1];
+                const int valid = kleft - kb;
+                if (valid > 0 && valid < 8) {
+                    FL_LDS char *p = buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16;
+                    u32x4_t v = *(FL_LDS u32x4_t *)p;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t keep = (2 * d + 1 < valid) ? 0xffffffffu : (2 * d < valid) ? 0x0000ffffu : 0u;
+                        v[d] &= keep;
+                    }
+                    const int row = n0 + B_ROWS_PER_COPY_T * (wave * NB + i) + lane / CA;
+                    if (row == a.N - 1) {
+                        const uint32_t e = (uint32_t)(valid - 1);
+                        const uint32_t x = load_u16_now(rBt, (uint32_t)((size_t)a.N * a.K - 1) * 2);
+                        v[e >> 1] =
+                            (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
+                    }
+                    *(FL_LDS u32x4_t *)p = v;
+                }
+            }
+        } else if (a.N & 7) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int rb = b_row(L, i);  // K row within the stage
@@ -369,8 +427,8 @@ struct Dma16 {
     }
 
     struct Frags {
-        u32x4_t a[4][RPA];  // A operand per mi (16 bytes per read)
-        i32x2_t b[NI][RPB]; // B operand per ni (8 bytes per transposed read)
+        u32x4_t a[4][RPA];     // A operand per mi (16 bytes per read)
+        i32x2_t b[NI][BPARTS]; // B operand per ni (8 bytes per transposed read, or halves of one 16-byte read)
     };
 
     // Operand read number P of the READS that make up one kk block, in the
@@ -382,7 +440,11 @@ struct Dma16 {
             f.a[0][P] = *(const FL_LDS u32x4_t *)(buf + (L.a_frag[kk] ^ (P * 16)));
         } else if constexpr (P < RPA + NI * RPB) {
             constexpr int ni = (P - RPA) / RPB, h = (P - RPA) % RPB;
-            if constexpr (!F8)
+            if constexpr (BT) {
+                const u32x4_t v = *(const FL_LDS u32x4_t *)(buf + L.b_frag[kk] + ni * 32 * (BK * 2));
+                f.b[ni][0] = i32x2_t{(int)v[0], (int)v[1]};
+                f.b[ni][1] = i32x2_t{(int)v[2], (int)v[3]};
+            } else if constexpr (!F8)
                 f.b[ni][h] = __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                              (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 16 * (BN * 2) +
                                                                                 h * 4 * (BN * 2))));
@@ -540,6 +602,11 @@ struct Dma16 {
     static constexpr int EPI_BYTES = SHARED_EPI ? BM * EPI_ROW : WAVES * EPI_WAVE;
     static_assert(EPI_BYTES <= (OCC == 2 ? 73728 : 163840), "epilogue staging fits in the workgroup's LDS");
     static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
+    // Backward: the lanes' fp32 column sums of dX meet in the wave's own LDS
+    // area as 32 rows (one per lane row) of WN floats, padded like EPI_ROW.
+    static constexpr int DB_ROW = WN * 4 + 16;
+    static_assert(!BWD || (!SHARED_EPI && WN == 64 && 32 * DB_ROW <= EPI_WAVE),
+                  "backward: own-area staging, one bias column per lane");
 
     // The elements e < cvalid of one 16-byte chunk bound for byte offset
     // off of out (nothing for off == kOob).
@@ -568,9 +635,15 @@ struct Dma16 {
             make_rsrc(static_cast<char *>(a.out) + o_org * OES, ((size_t)a.M * a.N - o_org) * OES);
         const __amdgpu_buffer_rsrc_t rY =
             make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * 2 : nullptr, a.Y ? o_bytes : 0);
-        constexpr bool has_r = RES;
+        // R is the residual, or in the backward epilogue the saved X (same
+        // shape, same loads)
+        constexpr bool has_r = RES || BWD;
+        const void *r_src = BWD ? a.Xs : a.R;
         const __amdgpu_buffer_rsrc_t rR =
-            make_rsrc(has_r ? static_cast<const char *>(a.R) + o_org * 2 : nullptr, has_r ? o_bytes : 0);
+            make_rsrc(has_r ? static_cast<const char *>(r_src) + o_org * 2 : nullptr, has_r ? o_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rDY = make_rsrc(
+            (BWD && ACT == FL_ACT_GLU) ? static_cast<char *>(a.dY) + o_org * 2 : nullptr,
+            (BWD && ACT == FL_ACT_GLU) ? o_bytes : 0);
         const __amdgpu_buffer_rsrc_t rBias =
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * 2 : nullptr,
                       a.bias ? (size_t)(a.N - n0) * 2 : 0);
@@ -581,6 +654,13 @@ struct Dma16 {
         for (int g = 0; g < NG; ++g) {
             col[g] = wn * WN + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
             valid[g] = a.N - n0 - col[g];
+        }
+        float dsum[BWD ? NG : 1][4];  // backward: this lane's column sums of dX
+        if constexpr (BWD) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dsum[g][e] = 0.0f;
         }
         quad_t bq[NG];
 #pragma unroll
@@ -624,6 +704,40 @@ struct Dma16 {
             for (int g = 0; g < NG; ++g) {
                 const int ni = g >> 2, q = g & 3;
                 float v[4];
+                if constexpr (BWD) {
+                    // dX = D * act'(X), and for the gate dY = D * X (D: the
+                    // accumulator; no bias on this side)
+                    float dy[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
+                        const float d = acc[mi][ni][q * 4 + e];
+                        const float xs = base::elem_f32(rq[mi % (RA + 1)][g], e);
+                        float dx = d * activate_grad<ACT>(xs, y);
+                        asm("" : "+v"(dx));
+                        v[e] = dx;
+                        dsum[g][e] += dx;
+                        // held in fp32 before the cast, as in activate(): a
+                        // multiply folded into a mixed-precision fma with a +0
+                        // addend turned -0 (D < 0, X = 0) into +0
+                        dy[e] = d * xs;
+                        asm("" : "+v"(dy[e]));
+                    }
+                    if constexpr (ACT == FL_ACT_GLU) {
+                        const uint32_t off = yoff(mi, g);
+                        u32x2_t w;
+                        w[0] = io::from_f32(dy[0]) | ((uint32_t)io::from_f32(dy[1]) << 16);
+                        w[1] = io::from_f32(dy[2]) | ((uint32_t)io::from_f32(dy[3]) << 16);
+                        if (valid[g] >= 4) {
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, w), rDY, off, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                store_elem<2>((uint16_t)(w[e >> 1] >> (16 * (e & 1))), rDY,
+                                              (off != kOob && e < valid[g]) ? off + e * 2 : kOob);
+                        }
+                    }
+                } else
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
@@ -757,6 +871,28 @@ struct Dma16 {
                 }
             }
         }
+        if (BWD && a.dbias) {
+            // Column sums of dX for dbias: the lanes' sums over their 4 rows
+            // meet in the wave's LDS area (row lrow, phase 2 has read it
+            // already), lane t adds up column t over the 32 rows, and one
+            // fp32 atomic per column and wave adds that into dbias (so the
+            // order of the additions across tiles is not fixed).  Rows past
+            // M and columns past N contribute zeros (A and B^T read as zero
+            // there).
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int c = (g >> 2) * 32 + (g & 3) * 8 + lg * 4;
+                const f32x4_t t = {dsum[g][0], dsum[g][1], dsum[g][2], dsum[g][3]};
+                *(FL_LDS f32x4_t *)(wbuf + lrow * DB_ROW + c * 4) = t;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            asm volatile("" ::: "memory");
+            float sum = 0.0f;
+#pragma unroll 8
+            for (int r = 0; r < 32; ++r) sum += *(const FL_LDS float *)(wbuf + r * DB_ROW + lane * 4);
+            const int col = n0 + wn * WN + lane;
+            if (col < a.N) unsafeAtomicAdd(a.dbias + col, sum);
+        }
     }
 
     __device__ __forceinline__ static void run_tile(const GemmArgs &a, int pid, char *smem) {
@@ -825,6 +961,24 @@ __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kern
     __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.
+    const int ntiles = a.tiles_m * a.tiles_n;
+    const int G = gridDim.x;
+    const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
+    for (int pid = slot; pid < ntiles; pid += G) {
+        T::run_tile(a, pid, smem);
+        __syncthreads();
+    }
+}
+
+// The backward epilogue kernel ("Optimizing GEMM + Activation on CDNA4 with
+// TLX", "Future Work": the epilogue fusion in the backward pass): D = A @
+// B^T with B given as (N, K) row-major, then dX = D * act'(Xs), the gate's
+// dY = D * Xs, and dbias += column sums of dX.  Same tile body and launch
+// loop as the forward kernel.
+template <int DT, int ACT, int BK, int BN, int WAVES_N>
+__global__ void __launch_bounds__(64 * 2 * WAVES_N, 1) fused_linear_bwd_kernel(GemmArgs a) {
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, kCopySpread, 1, false, -1, DT, true>;
+    __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     const int G = gridDim.x;
     const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;

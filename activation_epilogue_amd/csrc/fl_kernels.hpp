@@ -101,6 +101,30 @@ __device__ __forceinline__ float activate_math(float x, float y) {
     }
 }
 
+// Derivative of the activation at x (the gate: d(X + X*Y)/dX = 1 + Y), in
+// fp32, for the backward epilogue.  GELU(tanh) with s = sigmoid(2u) (the
+// form used above): g = x s, so g' = s + x s (1 - s) 2 u', u' = sqrt(2/pi)
+// (1 + 3 * 0.044715 x^2).  ReLU: 0 at x = 0.
+template <int ACT>
+__device__ __forceinline__ float activate_grad(float x, float y) {
+    float r;
+    if constexpr (ACT == FL_ACT_RELU) {
+        r = x > 0.0f ? 1.0f : 0.0f;
+    } else if constexpr (ACT == FL_ACT_GELU_TANH) {
+        constexpr float kc = 0.7978845608028654f;
+        constexpr float k2u = 2.0f * kc * 1.4426950408889634f;
+        const float u = x * __builtin_fmaf(0.044715f * x, x, 1.0f);
+        const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-k2u * u));
+        const float du2 = 2.0f * kc * __builtin_fmaf(3.0f * 0.044715f * x, x, 1.0f);
+        r = __builtin_fmaf(x * s * (1.0f - s), du2, s);
+    } else if constexpr (ACT == FL_ACT_GLU) {
+        r = 1.0f + y;
+    } else {
+        r = 1.0f;
+    }
+    return r;
+}
+
 // The epilogue value, held as an fp32 register before any cast.  Without the
 // empty asm the compiler may fold a following cast to a 16-bit type into the
 // last fma (v_fma_mix with a 16-bit result rounds once where fp32 math and a
@@ -211,6 +235,9 @@ struct GemmArgs {
     float scale;       // quantized output: codes of (epilogue value) * scale
     int stream_out;    // nonzero: every output row starts on a 128-byte line (streaming stores)
     float ab_scale;    // FP8 inputs: accumulator scale (product of A's and B's per-tensor scales)
+    const void *Xs;    // backward: the saved pre-activation X (M,N); B is then (N,K) row-major
+    void *dY;          // backward, gate: the second output D*X (M,N)
+    float *dbias;      // backward: column sums of dX (N,), fp32, added to atomically
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;
@@ -649,6 +676,11 @@ enum Variant {
 // test a.R at run time; the direct ones are compiled with or without it.
 template <int DT>
 fused_launcher pick_fused_for(int act, bool vec, int variant, bool residual);
+
+// The backward-epilogue kernel for (DT, act, variant), or null where none is
+// built (defined in the per-dtype backward instantiation unit).
+template <int DT>
+fused_launcher pick_bwd_for(int act, int variant);
 
 // Launcher of the quantized-output kernel for (DT, act, variant, qfmt), or
 // nullptr when that variant has none; defined in the per-dtype quantized

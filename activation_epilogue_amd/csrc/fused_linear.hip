@@ -200,8 +200,10 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
 
 fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
                       int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt,
-                      int qfmt = -1, float scale = 1.0f, bool fp8_in = false, float ab_scale = 1.0f) {
+                      int qfmt = -1, float scale = 1.0f, bool fp8_in = false, float ab_scale = 1.0f,
+                      const void *Xs = nullptr, void *dY = nullptr, float *dbias = nullptr) {
     if (M == 0 || N == 0) return FL_OK;
+    const bool bwd = Xs != nullptr;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
@@ -224,6 +226,9 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     const int64_t out_row_bytes = N * (qfmt >= 0 ? 1 : es);
     a.stream_out = (out_row_bytes % 128 == 0) && aligned(out, 128);
     a.ab_scale = ab_scale;
+    a.Xs = Xs;
+    a.dY = dY;
+    a.dbias = dbias;
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
@@ -239,6 +244,13 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (a.persistent) {
         const int slots = cu_count();
         grid = ntiles < slots ? ntiles : slots;
+    }
+    if (bwd) {
+        const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_bwd_for<FL_F16>(act, t.variant)
+                                                     : fl::pick_bwd_for<FL_BF16>(act, t.variant);
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2 and 5 only");
+        f(a, grid, static_cast<hipStream_t>(stream));
+        return check_launch("fused_linear_bwd");
     }
     if (fp8_in) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
@@ -257,6 +269,13 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     const bool use_vec = t.variant != fl::kRegStaged || aligned_rows;
     pick_fused(dtype, act, use_vec, t.variant, R != nullptr)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
+}
+
+// Zeroes n floats (the bias gradient before the tiles add into it); a
+// kernel rather than a memset, so that a captured graph replays it as work.
+__global__ void zero_f32_kernel(float *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
 }
 
 }  // namespace
@@ -344,6 +363,63 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
         if (t.variant == fl::kDirect32x128Occ2 || t.variant == fl::kDirect64x192) o.tile_cfg = 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
+}
+
+fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY,
+                              float *dbias, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
+                              void *stream, const fl_options *opt) {
+    clear_error();
+    if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for fp16 and bf16");
+    // G plays A (M,K) and W (N,K) has B's size; X is checked as a residual
+    // would be (it may be dX itself), Y as the gate's operand.
+    fl_status s = validate_gemm(G, W, nullptr, X, Y, dX, M, N, K, act, dtype, opt);
+    if (s != FL_OK) return s;
+    const size_t es = elem_size(dtype);
+    const size_t g_bytes = (size_t)M * K * es, w_bytes = (size_t)N * K * es, o_bytes = (size_t)M * N * es;
+    if (!X && o_bytes) return fail(FL_ERR_INVALID_ARG, "X (the saved pre-activation) is NULL");
+    if (act == FL_ACT_GLU && !dY && o_bytes) return fail(FL_ERR_INVALID_ARG, "the gate's backward needs dY");
+    if (act != FL_ACT_GLU && dY) return fail(FL_ERR_INVALID_ARG, "dY is only written for the gate (FL_ACT_GLU)");
+    if (overlaps(X, o_bytes, G, g_bytes) || overlaps(X, o_bytes, W, w_bytes))
+        return fail(FL_ERR_INVALID_ARG, "X overlaps G or W");
+    if (dY) {
+        if (!aligned(dY, es)) return fail(FL_ERR_INVALID_ARG, "dY is not aligned to the element size");
+        const void *others[4] = {G, W, X, dX};
+        const size_t sizes[4] = {g_bytes, w_bytes, o_bytes, o_bytes};
+        for (int i = 0; i < 4; ++i)
+            if (overlaps(dY, o_bytes, others[i], sizes[i]))
+                return fail(FL_ERR_INVALID_ARG, "dY overlaps G, W, X or dX");
+        if (dY != Y && overlaps(dY, o_bytes, Y, o_bytes))
+            return fail(FL_ERR_INVALID_ARG, "dY partially overlaps Y (only dY == Y is allowed)");
+    }
+    if (dbias) {
+        if (!aligned(dbias, 4)) return fail(FL_ERR_INVALID_ARG, "dbias is not 4-byte aligned");
+        const size_t db_bytes = (size_t)N * 4;
+        const void *others[5] = {G, W, X, Y, dX};
+        const size_t sizes[5] = {g_bytes, w_bytes, o_bytes, Y ? o_bytes : 0, o_bytes};
+        for (int i = 0; i < 5; ++i)
+            if (overlaps(dbias, db_bytes, others[i], sizes[i])) return fail(FL_ERR_INVALID_ARG, "dbias overlaps an operand");
+        if (dY && overlaps(dbias, db_bytes, dY, o_bytes)) return fail(FL_ERR_INVALID_ARG, "dbias overlaps dY");
+    }
+    fl_options o = opt ? *opt : fl_options{};
+    if (o.tile_cfg == 0) {
+        TileShape t;
+        tile_shape(dtype, M, N, K, &o, t);
+        o.tile_cfg = t.variant == fl::kDirect64x256W8 ? 5 : 2;
+    } else if (o.tile_cfg != 2 && o.tile_cfg != 5) {
+        return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2 and 5 only");
+    }
+    // dbias is a sum over every tile row: zero it first (a fill kernel on
+    // the same stream), then the tiles add into it.
+    if (dbias && N > 0) {
+        const int blocks = grid_elementwise(N);
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(fl::kThreads), 0, static_cast<hipStream_t>(stream),
+                           dbias, (int64_t)N);
+        s = check_launch("fused_linear_bwd (dbias fill)");
+        if (s != FL_OK) return s;
+    }
+    if (M == 0 || N == 0) return FL_OK;
+    return launch_gemm(G, W, nullptr, nullptr, Y, dX, M, N, K, act, dtype, stream, &o, -1, 1.0f, false, 1.0f, X, dY,
+                       dbias);
 }
 
 fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

@@ -35,6 +35,7 @@ class Workload:
     qfmt: str = ""       # quantized output ("fp8_e4m3" or "int8"), else the I/O dtype
     scale: float = 1.0   # quantized output scale
     in8: bool = False    # A and B as FP8 E4M3 codes (dtype is then the output / bias / Y dtype)
+    bwd: bool = False    # the backward epilogue: G (M,K), W (N,K), saved X (M,N) [, Y]; see draw_bwd
 
     @property
     def flops(self) -> int:
@@ -63,6 +64,11 @@ WORKLOADS = {w.name: w for w in [
     # TLX page's shape, and ReLU at 4096^3
     Workload("glu_fp8in_f16_1024x21568x4096", 1024, 21568, 4096, "f16", "glu", in8=True),
     Workload("relu_fp8in_f16_4096x4096x4096", 4096, 4096, 4096, "f16", "relu", in8=True),
+    # the backward of the GELU FFN's up-projection: the gradient reaching its output is
+    # dOut2 (8192x4096) @ W_down^T with W_down (14336x4096), then gelu'(X) and the bias gradient
+    Workload("gelu_bwd_bf16_8192x14336x4096", 8192, 14336, 4096, "bf16", "gelu_tanh", bwd=True),
+    # the same for the gate at the TLX page's shape (dX and dY)
+    Workload("glu_bwd_f16_1024x21568x4096", 1024, 21568, 4096, "f16", "glu", bwd=True),
 ]}
 
 
@@ -98,7 +104,35 @@ def draw(M, N, K, dtype, act, bias_var=1.0, seed=0, with_bias=True, residual=Fal
     }
 
 
+def draw_bwd(M, N, K, dtype, act, seed=0):
+    """Backward-epilogue inputs: G ~ N(0, 1) (M,K), W ~ N(0, 1/K) (N,K) (so
+    G @ W^T ~ N(0, 1)), the saved pre-activation X ~ N(0, 1) (M,N), and Y ~
+    U(-1, 1) (M,N) for the gate.  Draw order G, W, X, Y."""
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal((M, K))
+    W = rng.standard_normal((N, K)) / np.sqrt(max(K, 1))
+    X = rng.standard_normal((M, N))
+    Y = rng.uniform(-1.0, 1.0, (M, N)) if act == "glu" else None
+    return {"G": to_storage(G, dtype), "W": to_storage(W, dtype), "X": to_storage(X, dtype),
+            "Y": None if Y is None else to_storage(Y, dtype)}
+
+
+def draw_bwd_integer(M, N, K, dtype, act, seed=0):
+    """Small integers for the backward epilogue: G, W in {-2..2}, X in
+    {-3..3} (exact zeros included), Y in {-2..2}; with K <= 8 every value the
+    epilogue forms is exact in the 16-bit dtypes."""
+    rng = np.random.default_rng(seed)
+    G = rng.integers(-2, 3, (M, K)).astype(np.float64)
+    W = rng.integers(-2, 3, (N, K)).astype(np.float64)
+    X = rng.integers(-3, 4, (M, N)).astype(np.float64)
+    Y = rng.integers(-2, 3, (M, N)).astype(np.float64) if act == "glu" else None
+    return {"G": to_storage(G, dtype), "W": to_storage(W, dtype), "X": to_storage(X, dtype),
+            "Y": None if Y is None else to_storage(Y, dtype)}
+
+
 def draw_workload(w: Workload, with_bias=True):
+    if w.bwd:
+        return draw_bwd(w.M, w.N, w.K, w.dtype, w.act, w.seed)
     if w.in8:
         return draw_fp8(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed)
     return draw(w.M, w.N, w.K, w.dtype, w.act, w.bias_var, w.seed, with_bias, w.residual)

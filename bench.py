@@ -147,7 +147,9 @@ def cpu_baseline(w, d, target_s):
     while True:
         rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        if w.in8:
+        if w.bwd:
+            oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+        elif w.in8:
             oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act,
                                     out_dtype=w.dtype, rows=rows)
         elif w.qfmt:
@@ -228,9 +230,14 @@ def main():
 
     if w.in8:
         A, B = (torch.from_numpy(d[k]).to("cuda") for k in ("A8", "B8"))
+    elif w.bwd:
+        # the backward epilogue: A = G (M,K), B = W (N,K), saved X, gate Y
+        A, B, Xs = dev(d["G"]), dev(d["W"]), dev(d["X"])
+        dY = torch.empty((w.M, w.N), dtype=tdt, device="cuda") if w.act == "glu" else None
+        dbias = torch.empty((w.N,), dtype=torch.float32, device="cuda")
     else:
         A, B = dev(d["A"]), dev(d["B"])
-    bias, Y, R = dev(d["bias"]), dev(d["Y"]), dev(d["R"])
+    bias, Y, R = dev(d.get("bias")), dev(d["Y"]), dev(d.get("R"))
     out = torch.empty((w.M, w.N), dtype=torch.uint8 if w.qfmt else tdt, device="cuda")
     stream = torch.cuda.current_stream()
     opts = {}
@@ -242,14 +249,17 @@ def main():
         opts["tile_cfg"] = args.tile_cfg
     code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **opts)
-    if w.in8 and not args.tile_cfg and bn != 256:
-        # the FP8 entry point runs 256x128 where the automatic choice names
-        # the two-per-CU or the 256x192 kernel (neither has an FP8 build)
+    if (w.in8 or w.bwd) and not args.tile_cfg and bn != 256:
+        # the FP8 and backward entry points run 256x128 where the automatic
+        # choice names the two-per-CU or the 256x192 kernel (not built there)
         bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **dict(opts, tile_cfg=2))
-    kernel = "fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else "fused_linear_dma16_kernel"
+    kernel = ("fused_linear_bwd_kernel" if w.bwd else
+              "fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else "fused_linear_dma16_kernel")
 
     def step():
-        if w.in8:
+        if w.bwd:
+            fl.fused_linear_bwd(A, B, Xs, Y, act=w.act, dX=out, dY=dY, dbias=dbias, **opts)
+        elif w.in8:
             fl.fused_linear_fp8(A, B, d["ab_scale"], bias, Y, act=w.act, out_dtype=tdt, out=out, **opts)
         elif w.qfmt:
             fl.fused_linear_quant(A, B, bias, Y, act=w.act, scale=w.scale, qfmt=w.qfmt, out=out, **opts)
@@ -287,6 +297,9 @@ def main():
     mn_arrays = (0 if w.qfmt else 1) + (w.act == "glu") + w.residual  # out, Y, R in the I/O dtype
     alg_bytes = ((w.M * w.K + w.K * w.N) * (1 if w.in8 else es) + (w.N + w.M * w.N * mn_arrays) * es
                  + (w.M * w.N if w.qfmt else 0))
+    if w.bwd:
+        # G, W, X (+Y) read, dX (+dY) written once, dbias (fp32) zeroed and added to
+        alg_bytes = (w.M * w.K + w.K * w.N + 2 * w.M * w.N * (2 if w.act == "glu" else 1)) * es + 2 * w.N * 4
 
     result = {
         "metric": METRIC,
@@ -301,12 +314,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8->" + w.dtype if w.in8 else w.dtype,
-        "data": "synthetic (seeded numpy PCG64: %s, bias ~ N(0,%g)%s%s)" % (
+        "data": ("synthetic (seeded numpy PCG64: G ~ N(0,1), W ~ N(0,1/K), X ~ N(0,1)%s)" % (
+            ", Y ~ U(-1,1)" if w.act == "glu" else "") if w.bwd else
+            "synthetic (seeded numpy PCG64: %s, bias ~ N(0,%g)%s%s)" % (
             "A,B ~ N(0,1) as FP8 E4M3 codes, ab_scale 1/sqrt(K)" if w.in8 else "A,B ~ N(0,1/K)",
-            w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else "", ", R ~ N(0,1)" if w.residual else ""),
+            w.bias_var, ", Y ~ U(-1,1)" if w.act == "glu" else "", ", R ~ N(0,1)" if w.residual else "")),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "act": w.act, "residual": w.residual,
                    "out": w.qfmt or w.dtype, "scale": w.scale if w.qfmt else None,
                    "operands": "fp8_e4m3" if w.in8 else w.dtype,
+                   "pass": "backward: dX = (G @ W^T) * act'(X), dbias" if w.bwd else "forward",
                    "io_dtype": w.dtype,
                    "accumulate": "f32", "tile": f"{bm}x{bn}", "tiles": tiles_m * tiles_n,
                    "tile_cfg": args.tile_cfg, "group_m": args.group_m or 4, "persistent": bool(args.persistent)},
@@ -320,8 +336,8 @@ def main():
         "device": device_info(),
     }
 
-    if w.residual or w.qfmt or w.in8:
-        result["unfused"] = None  # the unfused chain has no residual, quantizing or FP8 form
+    if w.residual or w.qfmt or w.in8 or w.bwd:
+        result["unfused"] = None  # the unfused chain has no residual, quantizing, FP8 or backward form
     elif not args.no_unfused:
         X = torch.empty_like(out)
 

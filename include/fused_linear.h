@@ -220,6 +220,45 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               fl_dtype out_dtype, void *stream,
                               const fl_options *opt);
 
+/*
+ * The backward epilogue ("Optimizing GEMM + Activation on CDNA4 with TLX",
+ * "Future Work": the same epilogue fusion applied to the backward pass).  For
+ * a layer out = act(X), X = A@B + bias, whose output is multiplied by a
+ * weight W (N,K) in the next product, the loss gradient reaching out is
+ * D = G @ W^T (G (M,K): the gradient at that product's output).  One launch
+ * computes D with fp32 accumulation (W read as its transpose, K-contiguous:
+ * no transposed copy is made) and in its epilogue
+ *   dX = D * act'(X)     (ReLU: 1 where X > 0, else 0; GELU(tanh): its
+ *                          derivative; none: 1; gate X + X*Y: 1 + Y),
+ *   dY = D * X           (the gate only),
+ *   dbias = sum over the M rows of dX (fp32, before dX is rounded),
+ * then one rounding of dX and dY to dtype.
+ *   G      (M,K) device pointer, dtype.
+ *   W      (N,K) row-major device pointer, dtype.
+ *   X      (M,N) the saved pre-activation, dtype; may equal dX (read before
+ *          it is overwritten), must not otherwise overlap an output.
+ *   Y      (M,N) the gate's operand, for FL_ACT_GLU only (NULL otherwise).
+ *   dX     (M,N) output, dtype.
+ *   dY     (M,N) output for FL_ACT_GLU (may equal Y), NULL otherwise.
+ *   dbias  (N,) fp32 device buffer, or NULL for no bias gradient.  It is
+ *          overwritten: a fill kernel zeroes it on `stream`, then every
+ *          output tile adds its column sums with fp32 atomics, so its last
+ *          bits may differ from run to run (the order of the additions is
+ *          not fixed); dX and dY are deterministic.
+ *   dtype  FL_F16 or FL_BF16 (FL_F32 is FL_ERR_UNSUPPORTED).
+ *   opt    tile_cfg 0 (automatic: the 8-wave 256x256 kernel where the
+ *          forward choice is 256x256, 256x128 elsewhere), 2 or 5; others
+ *          are FL_ERR_UNSUPPORTED.  group_m, persistent and no_xcd_remap as
+ *          for fl_fused_linear_ex.
+ * Alignment, sizes and errors as fl_fused_linear_ex; M = 0 or N = 0 writes
+ * nothing but a zero dbias; K = 0 gives zeros.
+ */
+fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X,
+                              const void *Y, void *dX, void *dY,
+                              float *dbias, int64_t M, int64_t N, int64_t K,
+                              fl_act act, fl_dtype dtype, void *stream,
+                              const fl_options *opt);
+
 /* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
  * traffic": GEMM writes X, a bias pass reads and writes it, an activation
  * pass reads and writes it).  Each call is one launch and stores its result

@@ -228,3 +228,38 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _fp8(lib, **kwargs) == status
     assert msg in lib.fl_last_error().decode()
+
+
+# ------------------------------------------------------ backward epilogue
+
+X_P = 0x7000000    # saved pre-activation (M,N)
+DY_P = 0x7800000   # second output of the gate
+DB_P = 0x7F00000   # bias gradient (N,) fp32
+
+
+def _bwd(lib, G=A_P, W=B_P, X=X_P, Y=None, dX=OUT_P, dY=None, db=DB_P, dt=F16, M=64, N=64, K=64, act=RELU,
+         opt=None):
+    return lib.fl_fused_linear_bwd(G, W, X, Y, dX, dY, db, M, N, K, act, dt, None,
+                                   ctypes.byref(opt) if opt is not None else None)
+
+
+@pytest.mark.parametrize("kwargs,status,msg", [
+    (dict(dt=F32), UNSUPPORTED, "fp16 and bf16"),
+    (dict(X=None), INVALID, "X (the saved pre-activation) is NULL"),
+    (dict(act=GLU, Y=Y_P), INVALID, "the gate's backward needs dY"),
+    (dict(act=GLU), INVALID, "the gate needs Y"),
+    (dict(dY=DY_P), INVALID, "dY is only written for the gate"),
+    (dict(X=A_P + 128), INVALID, "X overlaps G or W"),
+    (dict(X=OUT_P + 2), INVALID, "R partially overlaps out"),
+    (dict(act=GLU, Y=Y_P, dY=X_P + 64), INVALID, "dY overlaps"),
+    (dict(act=GLU, Y=Y_P, dY=Y_P + 2), INVALID, "dY partially overlaps Y"),
+    (dict(db=X_P + 16), INVALID, "dbias overlaps"),
+    (dict(db=DB_P + 2), INVALID, "dbias is not 4-byte aligned"),
+    (dict(dX=A_P + 64), INVALID, "out overlaps A"),
+    (dict(opt=fl.Options(0, 0, 7, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
+    (dict(K=2 ** 22), UNSUPPORTED, "too large"),
+])
+def test_bwd_rejects_bad_arguments(lib, kwargs, status, msg):
+    assert _bwd(lib, **kwargs) == status
+    assert msg in lib.fl_last_error().decode()

@@ -551,3 +551,154 @@ def test_fp8_full_size_sampled_rows(name):
     ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act, out_dtype=w.dtype,
                                   rows=rows)
     _assert_close(out[rows], ref, w.dtype, name)
+
+
+# ------------------------------------------------------ backward epilogue
+# D = G @ W^T (W (N,K) read as its transpose), dX = D * act'(X), the gate's
+# dY = D * X, dbias = column sums of dX ("Optimizing GEMM + Activation on
+# CDNA4 with TLX", "Future Work").
+
+BWD_DTYPES = ["f16", "bf16"]
+
+
+def _run_bwd(d, act, dtype, with_dbias=True, **opts):
+    M, K = d["G"].shape
+    N = d["W"].shape[0]
+    G, W, X, Y = (to_dev(d[k], dtype) for k in ("G", "W", "X", "Y"))
+    dX, bufx = sentinel_out(M, N, dtype)
+    dY, bufy = sentinel_out(M, N, dtype) if act == "glu" else (None, None)
+    dbias = torch.full((N + 64,), float("nan"), dtype=torch.float32, device="cuda") if with_dbias else None
+    fl.fused_linear_bwd(G, W, X, Y, act=act, dX=dX, dY=dY, dbias=dbias[:N] if with_dbias else None, **opts)
+    torch.cuda.synchronize()
+    assert guard_intact(bufx, M, N), "write past the end of dX"
+    if dY is not None:
+        assert guard_intact(bufy, M, N), "write past the end of dY"
+    if with_dbias:
+        assert bool(torch.isnan(dbias[N:]).all().item()), "write past the end of dbias"
+    return (to_host(dX, dtype), None if dY is None else to_host(dY, dtype),
+            dbias[:N].cpu().numpy().astype(np.float64) if with_dbias else None)
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 17, 7), (67, 65, 8), (257, 264, 5), (513, 770, 3)])
+def test_bwd_integer_inputs_bit_exact(dtype, act, shape):
+    """Small integers: every value exact, so dX, dY and dbias must equal the
+    oracle's bits (dbias: exact integer sums in fp32)."""
+    M, N, K = shape
+    d = synth.draw_bwd_integer(M, N, K, dtype, act, seed=M + 3 * N + 7 * K)
+    say("bwd integer", dtype, act, shape)
+    dX, dY, db = _run_bwd(d, act, dtype)
+    rX, rY, rdb = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=act, dtype=dtype)
+    assert np.array_equal(dX.view(np.uint8), rX.view(np.uint8)), oracle.compare(dX, rX, dtype)
+    if act == "glu":
+        assert np.array_equal(dY.view(np.uint8), rY.view(np.uint8))
+    assert np.array_equal(db, rdb)
+
+
+def test_bwd_integer_longer_k_f16():
+    """K = 70 (a ragged last K stage) stays exact in fp16."""
+    M, N, K = 130, 200, 70
+    for act in ("relu", "glu"):
+        d = synth.draw_bwd_integer(M, N, K, "f16", act, seed=41)
+        say("bwd integer K=70", act)
+        dX, dY, db = _run_bwd(d, act, "f16")
+        rX, rY, rdb = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=act, dtype="f16")
+        assert np.array_equal(dX.view(np.uint8), rX.view(np.uint8))
+        assert np.array_equal(db, rdb)
+        if act == "glu":
+            assert np.array_equal(dY.view(np.uint8), rY.view(np.uint8))
+
+
+def _check_bwd(dX, dY, db, d, act, dtype, what):
+    M = d["G"].shape[0]
+    rX, rY, rdb, rdx = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=act, dtype=dtype, want_dx=True)
+    _assert_close(dX, rX, dtype, what + " dX")
+    if act == "glu":
+        _assert_close(dY, rY, dtype, what + " dY")
+    if db is not None:
+        res = oracle.compare_dbias(db, rdb, np.abs(rdx).sum(axis=0), M)
+        assert res["ok"], f"{what} dbias: {res}"
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("shape", [(127, 129, 96), (300, 260, 1000), (513, 264, 72), (256, 512, 33)])
+def test_bwd_random_within_tolerance(dtype, act, shape):
+    M, N, K = shape
+    d = synth.draw_bwd(M, N, K, dtype, act, seed=13)
+    say("bwd random", dtype, act, shape)
+    dX, dY, db = _run_bwd(d, act, dtype)
+    _check_bwd(dX, dY, db, d, act, dtype, f"bwd {dtype} {act} {shape}")
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["relu", "glu"])
+def test_bwd_variants_and_tile_orders_agree(dtype, act):
+    """The 8-wave 256x256 and the 256x128 kernels, and the tile orders, give
+    bit-identical dX and dY; dbias (fp32 atomics) agrees within tolerance."""
+    M, N, K = 600, 520, 300
+    d = synth.draw_bwd(M, N, K, dtype, act, seed=17)
+    outs = []
+    for opts in [dict(tile_cfg=5), dict(tile_cfg=2), dict(tile_cfg=5, group_m=1, persistent=1),
+                 dict(tile_cfg=2, no_xcd_remap=1)]:
+        say("bwd variant", dtype, act, opts)
+        outs.append(_run_bwd(d, act, dtype, **opts))
+        _check_bwd(*outs[-1], d, act, dtype, f"bwd {opts}")
+    for o in outs[1:]:
+        assert np.array_equal(o[0].view(np.uint8), outs[0][0].view(np.uint8))
+        if act == "glu":
+            assert np.array_equal(o[1].view(np.uint8), outs[0][1].view(np.uint8))
+
+
+def test_bwd_aliases_and_no_dbias():
+    """dX may overwrite X and dY may overwrite Y; dbias may be omitted."""
+    M, N, K = 300, 520, 64
+    d = synth.draw_bwd(M, N, K, "f16", "glu", seed=19)
+    G, W, X, Y = (to_dev(d[k], "f16") for k in ("G", "W", "X", "Y"))
+    say("bwd aliases")
+    dX, dY, db = fl.fused_linear_bwd(G, W, X, Y, act="glu", dX=X, dY=Y, dbias=None)
+    torch.cuda.synchronize()
+    assert db is None and dX.data_ptr() == X.data_ptr() and dY.data_ptr() == Y.data_ptr()
+    _check_bwd(to_host(X, "f16"), to_host(Y, "f16"), None, d, "glu", "f16", "aliased")
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+def test_bwd_degenerate_sizes(dtype):
+    """K = 0 gives zero gradients; M = 0 leaves a zeroed dbias."""
+    d = synth.draw_bwd(70, 90, 0, dtype, "relu", seed=23)
+    say("bwd K=0", dtype)
+    dX, _, db = _run_bwd(d, "relu", dtype)
+    assert not oracle.decode(dX, dtype).any() and not db.any()
+    G = torch.empty((0, 16), dtype=TORCH_DT[dtype], device="cuda")
+    W = torch.zeros((40, 16), dtype=TORCH_DT[dtype], device="cuda")
+    X = torch.empty((0, 40), dtype=TORCH_DT[dtype], device="cuda")
+    dbias = torch.full((40,), 7.0, dtype=torch.float32, device="cuda")
+    fl.fused_linear_bwd(G, W, X, act="relu", dbias=dbias)
+    torch.cuda.synchronize()
+    assert not dbias.any().item()
+
+
+@pytest.mark.parametrize("name", ["gelu_bwd_bf16_8192x14336x4096", "glu_bwd_f16_1024x21568x4096"])
+def test_bwd_full_size(name):
+    """The benchmarked launch: sampled rows of dX (and dY) against the oracle,
+    every output written, and dbias of sampled columns against the oracle's
+    exact column sums over all rows (a column subset of W, X and Y gives the
+    same columns of the full problem)."""
+    w = synth.WORKLOADS[name]
+    d = synth.draw_workload(w)
+    say("bwd full size", name)
+    dX, dY, db = _run_bwd(d, w.act, w.dtype)
+    assert not np.isnan(oracle.decode(dX, w.dtype)).any()
+    rows = sample_rows(w.M)
+    rX, rY, _ = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
+    _assert_close(dX[rows], rX, w.dtype, name + " dX")
+    if w.act == "glu":
+        _assert_close(dY[rows], rY, w.dtype, name + " dY")
+    cols = np.unique(np.concatenate([[0, w.N - 1], np.random.default_rng(1).integers(0, w.N, 14)]))
+    sub = {"G": d["G"], "W": np.ascontiguousarray(d["W"][cols]), "X": np.ascontiguousarray(d["X"][:, cols]),
+           "Y": None if d["Y"] is None else np.ascontiguousarray(d["Y"][:, cols])}
+    _, _, rdb, rdx = oracle.fused_linear_bwd(sub["G"], sub["W"], sub["X"], sub["Y"], act=w.act, dtype=w.dtype,
+                                             want_dx=True)
+    res = oracle.compare_dbias(db[cols], rdb, np.abs(rdx).sum(axis=0), w.M)
+    assert res["ok"], res
