@@ -16,6 +16,8 @@ Entry points (same names as the C ABI, without the ``fl_`` prefix):
                                           # FP8 E4M3 operands, 16-bit epilogue and output
   fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, **options)
                                           # backward epilogue: dX = (G @ W^T) * act'(X), gate dY, dbias
+  gemm_nt(A, Bt, D=None), activation_grad(D, X, Y=None, act=, dX=None, dY=None), column_sum(X, sums=None)
+                                          # the unfused backward chain
   gemm(A, B, X=None)                      # unfused step 1: X = A@B
   bias_add(X, bias)                       # unfused step 2: X += bias (in place)
   activation(X, Y=None, out=None, act=)   # unfused step 3: out = act(X[, Y])
@@ -32,7 +34,8 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
 EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
-           "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_gemm", "fl_bias_add", "fl_activation",
+           "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_gemm", "fl_gemm_nt", "fl_activation_grad",
+           "fl_column_sum", "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
 
@@ -77,6 +80,9 @@ def load_library():
     lib.fl_fused_linear_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
                                         ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
+    lib.fl_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
+    lib.fl_activation_grad.argtypes = [vp, vp, vp, vp, vp, i64, i64, c_int, c_int, vp]
+    lib.fl_column_sum.argtypes = [vp, vp, i64, i64, c_int, vp]
     lib.fl_bias_add.argtypes = [vp, vp, i64, i64, c_int, vp]
     lib.fl_activation.argtypes = [vp, vp, vp, i64, i64, c_int, c_int, vp]
     lib.fl_tile_grid.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(Options), P_i32, P_i32, P_i32, P_i32]
@@ -249,6 +255,48 @@ def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, 
         _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)), _dev_ptr(dbias, "dbias", torch.float32, (N,)),
         M, N, K, ACTS[act], _dtype_code(dt), _stream(G, stream), ctypes.byref(opt)))
     return dX, dY, dbias
+
+
+def gemm_nt(A, Bt, D=None, *, stream=None):
+    """Unfused backward step 1: D = A @ Bt^T with Bt (N,K) row-major."""
+    import torch
+    lib = load_library()
+    M, K = A.shape
+    N = Bt.shape[0]
+    dt = A.dtype
+    if D is None:
+        D = torch.empty((M, N), dtype=dt, device=A.device)
+    _check(lib.fl_gemm_nt(_dev_ptr(A, "A", dt), _dev_ptr(Bt, "Bt", dt, (N, K)), _dev_ptr(D, "D", dt, (M, N)),
+                          M, N, K, _dtype_code(dt), _stream(A, stream)))
+    return D
+
+
+def activation_grad(D, X, Y=None, act="relu", dX=None, dY=None, *, stream=None):
+    """Unfused backward step 2: dX = D * act'(X) (gate: also dY = D * X)."""
+    import torch
+    lib = load_library()
+    M, N = D.shape
+    dt = D.dtype
+    if dX is None:
+        dX = torch.empty_like(D)
+    if act == "glu" and dY is None:
+        dY = torch.empty_like(D)
+    _check(lib.fl_activation_grad(_dev_ptr(D, "D", dt), _dev_ptr(X, "X", dt, (M, N)), _dev_ptr(Y, "Y", dt, (M, N)),
+                                  _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)), M, N, ACTS[act],
+                                  _dtype_code(dt), _stream(D, stream)))
+    return dX, dY
+
+
+def column_sum(X, sums=None, *, stream=None):
+    """Unfused backward step 3: sums[j] = sum_i X[i, j] (fp32)."""
+    import torch
+    lib = load_library()
+    M, N = X.shape
+    if sums is None:
+        sums = torch.empty((N,), dtype=torch.float32, device=X.device)
+    _check(lib.fl_column_sum(_dev_ptr(X, "X", X.dtype), _dev_ptr(sums, "sums", torch.float32, (N,)), M, N,
+                             _dtype_code(X.dtype), _stream(X, stream)))
+    return sums
 
 
 def gemm(A, B, X=None, *, stream=None):

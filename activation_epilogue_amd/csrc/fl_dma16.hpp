@@ -637,10 +637,12 @@ struct Dma16 {
             make_rsrc(a.Y ? static_cast<const char *>(a.Y) + o_org * 2 : nullptr, a.Y ? o_bytes : 0);
         // R is the residual, or in the backward epilogue the saved X (same
         // shape, same loads)
+        // (a null X -- the plain transposed-B product -- reads as zeros)
         constexpr bool has_r = RES || BWD;
         const void *r_src = BWD ? a.Xs : a.R;
+        const bool r_live = has_r && r_src != nullptr;
         const __amdgpu_buffer_rsrc_t rR =
-            make_rsrc(has_r ? static_cast<const char *>(r_src) + o_org * 2 : nullptr, has_r ? o_bytes : 0);
+            make_rsrc(r_live ? static_cast<const char *>(r_src) + o_org * 2 : nullptr, r_live ? o_bytes : 0);
         const __amdgpu_buffer_rsrc_t rDY = make_rsrc(
             (BWD && ACT == FL_ACT_GLU) ? static_cast<char *>(a.dY) + o_org * 2 : nullptr,
             (BWD && ACT == FL_ACT_GLU) ? o_bytes : 0);
@@ -685,7 +687,9 @@ struct Dma16 {
         }
         if constexpr (RA && has_r) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) rq[0][g] = base::load4(rR, yoff(0, g), valid[g]);
+            for (int p = 0; p < RA; ++p)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) rq[p][g] = base::load4(rR, yoff(p, g), valid[g]);
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {

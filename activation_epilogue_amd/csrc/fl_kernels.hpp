@@ -617,6 +617,101 @@ __global__ void __launch_bounds__(kThreads) bias_add_kernel(void *Xv, const void
     }
 }
 
+// The unfused backward chain's second pass, elementwise: dX = D * act'(X)
+// and, for the gate, dY = D * X, each rounded once to the I/O dtype (D may be
+// dX and Y may be dY: each element is read before it is written, by the same
+// thread).  VECTOR: 16-byte aligned pointers; the tail that does not fill a
+// chunk is done element by element.
+template <int DT, int ACT, bool VECTOR>
+__global__ void __launch_bounds__(kThreads) activation_grad_kernel(const void *Dv, const void *Xv, const void *Yv,
+                                                                   void *dXv, void *dYv, int64_t total) {
+    using io = Io<DT>;
+    using raw = typename io::raw;
+    constexpr int VEC = 16 / io::size;
+    const raw *D = static_cast<const raw *>(Dv);
+    const raw *X = static_cast<const raw *>(Xv);
+    const raw *Y = static_cast<const raw *>(Yv);
+    raw *dX = static_cast<raw *>(dXv);
+    raw *dY = static_cast<raw *>(dYv);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    auto one = [&](raw d16, raw x16, raw y16, raw &dx16, raw &dy16) {
+        const float d = io::to_f32(d16), x = io::to_f32(x16);
+        float dx = d * activate_grad<ACT>(x, ACT == FL_ACT_GLU ? io::to_f32(y16) : 0.0f);
+        asm("" : "+v"(dx));
+        dx16 = io::from_f32(dx);
+        float dy = d * x;
+        asm("" : "+v"(dy));
+        dy16 = io::from_f32(dy);
+    };
+    int64_t done = 0;
+    if constexpr (VECTOR) {
+        const int64_t nchunks = total / VEC;
+        for (int64_t c = gid; c < nchunks; c += stride) {
+            const u32x4_t dv = *reinterpret_cast<const u32x4_t *>(D + c * VEC);
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(X + c * VEC);
+            u32x4_t yv = {0u, 0u, 0u, 0u};
+            if constexpr (ACT == FL_ACT_GLU) yv = *reinterpret_cast<const u32x4_t *>(Y + c * VEC);
+            raw ds[VEC], xs[VEC], ys[VEC], ox[VEC], oy[VEC];
+            __builtin_memcpy(ds, &dv, 16);
+            __builtin_memcpy(xs, &xv, 16);
+            __builtin_memcpy(ys, &yv, 16);
+#pragma unroll
+            for (int t = 0; t < VEC; ++t) one(ds[t], xs[t], ys[t], ox[t], oy[t]);
+            u32x4_t o;
+            __builtin_memcpy(&o, ox, 16);
+            *reinterpret_cast<u32x4_t *>(dX + c * VEC) = o;
+            if constexpr (ACT == FL_ACT_GLU) {
+                __builtin_memcpy(&o, oy, 16);
+                *reinterpret_cast<u32x4_t *>(dY + c * VEC) = o;
+            }
+        }
+        done = nchunks * VEC;
+    }
+    for (int64_t e = done + gid; e < total; e += stride) {
+        raw ox, oy;
+        one(D[e], X[e], ACT == FL_ACT_GLU ? Y[e] : raw(0), ox, oy);
+        dX[e] = ox;
+        if constexpr (ACT == FL_ACT_GLU) dY[e] = oy;
+    }
+}
+
+// The unfused backward chain's third pass: sums[j] += the fp32 sum of X[i, j]
+// over rows (sums zeroed first by the caller).  Block (bx, by) takes
+// kThreads column groups of CPT columns (one 16-byte load per row when
+// VECTOR) and the bands of kColRows rows by, by + gridDim.y, ...; one fp32
+// atomic per column and block, so the order of the additions is not fixed.
+constexpr int kColRows = 64;  // rows per band
+template <int DT, bool VECTOR>
+__global__ void __launch_bounds__(kThreads) column_sum_kernel(const void *Xv, float *sums, int64_t M, int64_t N) {
+    using io = Io<DT>;
+    using raw = typename io::raw;
+    constexpr int CPT = VECTOR ? 16 / io::size : 1;  // columns per thread
+    const raw *X = static_cast<const raw *>(Xv);
+    const int64_t j0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * CPT;
+    if (j0 >= N) return;
+    float acc[CPT];
+#pragma unroll
+    for (int t = 0; t < CPT; ++t) acc[t] = 0.0f;
+    for (int64_t band = blockIdx.y; band * kColRows < M; band += gridDim.y) {
+        const int64_t r0 = band * kColRows, r1 = r0 + kColRows < M ? r0 + kColRows : M;
+#pragma unroll 8
+        for (int64_t i = r0; i < r1; ++i) {
+            if constexpr (VECTOR) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + i * N + j0);
+                raw xs[CPT];
+                __builtin_memcpy(xs, &v, 16);
+#pragma unroll
+                for (int t = 0; t < CPT; ++t) acc[t] += io::to_f32(xs[t]);
+            } else {
+                acc[0] += io::to_f32(X[i * N + j0]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < CPT; ++t) unsafeAtomicAdd(sums + j0 + t, acc[t]);
+}
+
 // out = act(X[, Y]) elementwise.  VECTOR: 16-byte aligned pointers; the
 // tail that does not fill a chunk is done element by element.
 template <int DT, int ACT, bool VECTOR>

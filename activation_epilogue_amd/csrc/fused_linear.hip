@@ -201,9 +201,8 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
 fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
                       int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt,
                       int qfmt = -1, float scale = 1.0f, bool fp8_in = false, float ab_scale = 1.0f,
-                      const void *Xs = nullptr, void *dY = nullptr, float *dbias = nullptr) {
+                      const void *Xs = nullptr, void *dY = nullptr, float *dbias = nullptr, bool bwd = false) {
     if (M == 0 || N == 0) return FL_OK;
-    const bool bwd = Xs != nullptr;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
@@ -276,6 +275,55 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
 __global__ void zero_f32_kernel(float *p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0.0f;
+}
+
+// The tile choice of the transposed-B kernels: the 8-wave 256x256 kernel
+// where the forward choice is 256x256, else 256x128.
+fl_options bwd_tiles(int dtype, int64_t M, int64_t N, int64_t K) {
+    fl_options o{};
+    TileShape t;
+    tile_shape(dtype, M, N, K, &o, t);
+    o.tile_cfg = t.variant == fl::kDirect64x256W8 ? 5 : 2;
+    return o;
+}
+
+template <int DT, int ACT>
+void launch_ag(bool vec, int grid, hipStream_t st, const void *D, const void *X, const void *Y, void *dX, void *dY,
+               int64_t total) {
+    if (vec)
+        hipLaunchKernelGGL((fl::activation_grad_kernel<DT, ACT, true>), dim3(grid), dim3(fl::kThreads), 0, st, D, X, Y,
+                           dX, dY, total);
+    else
+        hipLaunchKernelGGL((fl::activation_grad_kernel<DT, ACT, false>), dim3(grid), dim3(fl::kThreads), 0, st, D, X, Y,
+                           dX, dY, total);
+}
+
+template <int DT>
+void launch_ag_act(int act, bool vec, int grid, hipStream_t st, const void *D, const void *X, const void *Y, void *dX,
+                   void *dY, int64_t total) {
+    switch (act) {
+    case FL_ACT_NONE: launch_ag<DT, FL_ACT_NONE>(vec, grid, st, D, X, Y, dX, dY, total); break;
+    case FL_ACT_RELU: launch_ag<DT, FL_ACT_RELU>(vec, grid, st, D, X, Y, dX, dY, total); break;
+    case FL_ACT_GELU_TANH: launch_ag<DT, FL_ACT_GELU_TANH>(vec, grid, st, D, X, Y, dX, dY, total); break;
+    default: launch_ag<DT, FL_ACT_GLU>(vec, grid, st, D, X, Y, dX, dY, total); break;
+    }
+}
+
+fl_status launch_activation_grad(int dtype, int act, bool vec, int grid, hipStream_t st, const void *D, const void *X,
+                                 const void *Y, void *dX, void *dY, int64_t total) {
+    if (dtype == FL_F16)
+        launch_ag_act<FL_F16>(act, vec, grid, st, D, X, Y, dX, dY, total);
+    else
+        launch_ag_act<FL_BF16>(act, vec, grid, st, D, X, Y, dX, dY, total);
+    return FL_OK;
+}
+
+template <int DT>
+void launch_column_sum(bool vec, dim3 grid, hipStream_t st, const void *X, float *sums, int64_t M, int64_t N) {
+    if (vec)
+        hipLaunchKernelGGL((fl::column_sum_kernel<DT, true>), grid, dim3(fl::kThreads), 0, st, X, sums, M, N);
+    else
+        hipLaunchKernelGGL((fl::column_sum_kernel<DT, false>), grid, dim3(fl::kThreads), 0, st, X, sums, M, N);
 }
 
 }  // namespace
@@ -419,7 +467,81 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     }
     if (M == 0 || N == 0) return FL_OK;
     return launch_gemm(G, W, nullptr, nullptr, Y, dX, M, N, K, act, dtype, stream, &o, -1, 1.0f, false, 1.0f, X, dY,
-                       dbias);
+                       dbias, true);
+}
+
+fl_status fl_gemm_nt(const void *A, const void *Bt, void *D, int64_t M, int64_t N, int64_t K, fl_dtype dtype,
+                     void *stream) {
+    clear_error();
+    if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the transposed-B product is built for fp16 and bf16");
+    fl_status s = validate_gemm(A, Bt, nullptr, nullptr, nullptr, D, M, N, K, FL_ACT_NONE, dtype, nullptr);
+    if (s != FL_OK) return s;
+    if (M == 0 || N == 0) return FL_OK;
+    const fl_options o = bwd_tiles(dtype, M, N, K);
+    return launch_gemm(A, Bt, nullptr, nullptr, nullptr, D, M, N, K, FL_ACT_NONE, dtype, stream, &o, -1, 1.0f, false,
+                       1.0f, nullptr, nullptr, nullptr, true);
+}
+
+fl_status fl_activation_grad(const void *D, const void *X, const void *Y, void *dX, void *dY, int64_t M, int64_t N,
+                             fl_act act, fl_dtype dtype, void *stream) {
+    clear_error();
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward passes are built for fp16 and bf16");
+    fl_status s = check_dims(M, N, 0);
+    if (s != FL_OK) return s;
+    const size_t es = elem_size(dtype), bytes = (size_t)M * N * es;
+    if (bytes == 0) return FL_OK;
+    if (!D || !X || !dX) return fail(FL_ERR_INVALID_ARG, "D, X and dX must not be NULL");
+    if (act == FL_ACT_GLU && (!Y || !dY)) return fail(FL_ERR_INVALID_ARG, "the gate's backward needs Y and dY");
+    if (act != FL_ACT_GLU && (Y || dY)) return fail(FL_ERR_INVALID_ARG, "Y and dY are only used by the gate");
+    const void *ptrs[5] = {D, X, Y, dX, dY};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, es)) return fail(FL_ERR_INVALID_ARG, "pointer %p is not aligned to the element size", p);
+    // dX may be D, dY may be Y; no other overlap among inputs and outputs
+    if (dX != D && overlaps(dX, bytes, D, bytes)) return fail(FL_ERR_INVALID_ARG, "dX partially overlaps D");
+    if (overlaps(dX, bytes, X, bytes) || (Y && overlaps(dX, bytes, Y, bytes)))
+        return fail(FL_ERR_INVALID_ARG, "dX overlaps X or Y");
+    if (dY) {
+        if (dY != Y && overlaps(dY, bytes, Y, bytes)) return fail(FL_ERR_INVALID_ARG, "dY partially overlaps Y");
+        if (overlaps(dY, bytes, D, bytes) || overlaps(dY, bytes, X, bytes) || overlaps(dY, bytes, dX, bytes))
+            return fail(FL_ERR_INVALID_ARG, "dY overlaps D, X or dX");
+    }
+    const bool vec = aligned(D, 16) && aligned(X, 16) && aligned(dX, 16) && (!Y || aligned(Y, 16)) &&
+                     (!dY || aligned(dY, 16));
+    const int64_t total = (int64_t)(bytes / es);
+    const int grid = grid_elementwise(vec ? total / (16 / (int64_t)es) + 1 : total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const fl_status ls = launch_activation_grad(dtype, act, vec, grid, st, D, X, Y, dX, dY, total);
+    if (ls != FL_OK) return ls;
+    return check_launch("activation_grad");
+}
+
+fl_status fl_column_sum(const void *X, float *sums, int64_t M, int64_t N, fl_dtype dtype, void *stream) {
+    clear_error();
+    if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward passes are built for fp16 and bf16");
+    fl_status s = check_dims(M, N, 0);
+    if (s != FL_OK) return s;
+    if (N == 0) return FL_OK;
+    const size_t es = elem_size(dtype), bytes = (size_t)M * N * es;
+    if (!sums) return fail(FL_ERR_INVALID_ARG, "sums is NULL");
+    if (!X && bytes) return fail(FL_ERR_INVALID_ARG, "X is NULL");
+    if (!aligned(sums, 4) || (X && !aligned(X, es))) return fail(FL_ERR_INVALID_ARG, "misaligned pointer");
+    if (overlaps(sums, (size_t)N * 4, X, bytes)) return fail(FL_ERR_INVALID_ARG, "sums overlaps X");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_elementwise(N)), dim3(fl::kThreads), 0, st, sums, (int64_t)N);
+    s = check_launch("column_sum (fill)");
+    if (s != FL_OK || M == 0) return s;
+    const bool vec = (N % 8 == 0) && aligned(X, 16);
+    const int64_t cpt = vec ? 8 : 1;
+    const int64_t bands = (M + fl::kColRows - 1) / fl::kColRows;
+    const dim3 grid((unsigned)((N / cpt + fl::kThreads - 1) / fl::kThreads), (unsigned)(bands < 4096 ? bands : 4096));
+    if (dtype == FL_F16)
+        launch_column_sum<FL_F16>(vec, grid, st, X, sums, M, N);
+    else
+        launch_column_sum<FL_BF16>(vec, grid, st, X, sums, M, N);
+    return check_launch("column_sum");
 }
 
 fl_status fl_gemm(const void *A, const void *B, void *X, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

@@ -336,8 +336,42 @@ def main():
         "device": device_info(),
     }
 
-    if w.residual or w.qfmt or w.in8 or w.bwd:
-        result["unfused"] = None  # the unfused chain has no residual, quantizing, FP8 or backward form
+    if w.bwd and not args.no_unfused:
+        # the unfused backward chain: the product stored, an elementwise
+        # derivative pass, a column-sum pass (each one launch, storing its result)
+        Dbuf = torch.empty_like(out)
+        dXu = torch.empty_like(out)
+        dYu = torch.empty_like(out) if w.act == "glu" else None
+        dbu = torch.empty_like(dbias)
+
+        def chain():
+            fl.gemm_nt(A, B, Dbuf)
+            fl.activation_grad(Dbuf, Xs, Y, act=w.act, dX=dXu, dY=dYu)
+            fl.column_sum(dXu, dbu)
+
+        ms_chain, _ = time_loop(chain, args.steps, args.warmup, stream)
+        ms_gemm, _ = time_loop(lambda: fl.gemm_nt(A, B, Dbuf), args.steps, args.warmup, stream)
+        ms_ag, _ = time_loop(lambda: fl.activation_grad(Dbuf, Xs, Y, act=w.act, dX=dXu, dY=dYu), args.steps,
+                             args.warmup, stream)
+        ms_cs, _ = time_loop(lambda: fl.column_sum(dXu, dbu), args.steps, args.warmup, stream)
+        mn = w.M * w.N
+        glu = w.act == "glu"
+        ag_bytes = (3 + 2 * glu) * mn * es  # D, X (+Y) read, dX (+dY) written
+        cs_bytes = mn * es + w.N * 4
+        result["unfused"] = {
+            "ms_per_step": round(ms_chain, 4),
+            "fused_speedup": round(ms_chain / ms_event, 3),
+            "gemm_nt_ms": round(ms_gemm, 4),
+            "activation_grad_pass": {"ms": round(ms_ag, 4), "GB/s": round(ag_bytes / ms_ag / 1e6, 1),
+                                     "frac_hbm": round(ag_bytes / ms_ag / 1e6 / PEAK_HBM_GBS, 3)},
+            "column_sum_pass": {"ms": round(ms_cs, 4), "GB/s": round(cs_bytes / ms_cs / 1e6, 1),
+                                "frac_hbm": round(cs_bytes / ms_cs / 1e6 / PEAK_HBM_GBS, 3)},
+            # bytes of the (M,N) arrays beyond the product's own operands: fused reads X (+Y) and
+            # writes dX (+dY); the chain also writes and re-reads D and re-reads dX
+            "epilogue_traffic_bytes": {"fused": (2 + 2 * glu) * mn * es, "unfused": (5 + 2 * glu) * mn * es},
+        }
+    elif w.residual or w.qfmt or w.in8 or w.bwd:
+        result["unfused"] = None  # the unfused chain has no residual, quantizing or FP8 form
     elif not args.no_unfused:
         X = torch.empty_like(out)
 

@@ -259,6 +259,31 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X,
                               fl_act act, fl_dtype dtype, void *stream,
                               const fl_options *opt);
 
+/* The unfused backward chain, for comparison with fl_fused_linear_bwd: one
+ * launch per step, each storing its result in dtype (so D and dX round-trip
+ * through memory), together round(round(D) * act'(X)) and the fp32 column
+ * sums of the stored dX. */
+
+/* D = A @ Bt^T: A (M,K), Bt (N,K) row-major (B given as its transpose), D
+ * (M,N), dtype FL_F16 or FL_BF16 (FL_F32 is FL_ERR_UNSUPPORTED); the
+ * backward kernel with no epilogue work.  Conventions as fl_gemm. */
+fl_status fl_gemm_nt(const void *A, const void *Bt, void *D, int64_t M,
+                     int64_t N, int64_t K, fl_dtype dtype, void *stream);
+
+/* dX = D * act'(X) elementwise, and for FL_ACT_GLU also dY = D * X (Y and
+ * dY NULL for the other activations).  All (M,N) in dtype (FL_F16 or
+ * FL_BF16); dX may equal D and dY may equal Y, no other overlap. */
+fl_status fl_activation_grad(const void *D, const void *X, const void *Y,
+                             void *dX, void *dY, int64_t M, int64_t N,
+                             fl_act act, fl_dtype dtype, void *stream);
+
+/* sums[j] = sum over i of X[i,j] in fp32: X (M,N) in dtype (FL_F16 or
+ * FL_BF16), sums (N,) fp32, overwritten (zeroed by a fill kernel, then
+ * added to with fp32 atomics, so its last bits may differ from run to
+ * run). */
+fl_status fl_column_sum(const void *X, float *sums, int64_t M, int64_t N,
+                        fl_dtype dtype, void *stream);
+
 /* The unfused chain ("Triton: Fused Matmul + Bias + ReLU", "The HBM
  * traffic": GEMM writes X, a bias pass reads and writes it, an activation
  * pass reads and writes it).  Each call is one launch and stores its result

@@ -89,6 +89,8 @@ def _load():
             lib.orc_gelu_tanh_grad.restype = ctypes.c_double
             lib.orc_fused_linear_bwd.argtypes = [c_int, c_int, p, p, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
             lib.orc_fused_linear_bwd.restype = c_int
+            lib.orc_unfused_bwd_chain.argtypes = [c_int, c_int, p, p, p, p, p, p, p, i64, i64, i64, p, i64, c_int, p]
+            lib.orc_unfused_bwd_chain.restype = c_int
             lib.orc_max_threads.restype = c_int
             _lib = lib
     return _lib
@@ -208,7 +210,14 @@ def gelu_tanh_grad(x):
     return _load().orc_gelu_tanh_grad(float(x))
 
 
-def fused_linear_bwd(G, W, X, Y=None, act="relu", dtype="f16", rows=None, threads=None, want_dx=False):
+def unfused_bwd_chain(G, W, X, Y=None, act="relu", dtype="f16", rows=None, threads=None, want_dx=False):
+    """As fused_linear_bwd for the three-pass chain: D stored in dtype before
+    the elementwise pass, dbias summed from the stored dX."""
+    return fused_linear_bwd(G, W, X, Y, act, dtype, rows, threads, want_dx, _fn="orc_unfused_bwd_chain")
+
+
+def fused_linear_bwd(G, W, X, Y=None, act="relu", dtype="f16", rows=None, threads=None, want_dx=False,
+                     _fn="orc_fused_linear_bwd"):
     """Backward epilogue: D = G @ W^T (G (M,K), W (N,K), FP64), then
     dX = round(D * act'(X)), for the gate also dY = round(D * X), and
     dbias = sum over rows of the unrounded dX (FP64; over the selected rows
@@ -230,10 +239,10 @@ def fused_linear_bwd(G, W, X, Y=None, act="relu", dtype="f16", rows=None, thread
     dY = np.empty((nrows, N), dtype=STORAGE[dtype]) if act == "glu" else None
     dbias = np.empty(N, dtype=np.float64)
     dx = np.empty((nrows, N), dtype=np.float64) if want_dx else None
-    st = lib.orc_fused_linear_bwd(DTYPES[dtype], ACTS[act], _ptr(G), _ptr(W), _ptr(X), _ptr(Y), _ptr(dX), _ptr(dY),
-                                  _ptr(dbias), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(dx))
+    st = getattr(lib, _fn)(DTYPES[dtype], ACTS[act], _ptr(G), _ptr(W), _ptr(X), _ptr(Y), _ptr(dX), _ptr(dY),
+                           _ptr(dbias), M, N, K, _ptr(rows_arr), nrows, int(threads or 0), _ptr(dx))
     if st != 0:
-        raise RuntimeError(f"orc_fused_linear_bwd failed with status {st}")
+        raise RuntimeError(f"{_fn} failed with status {st}")
     return (dX, dY, dbias, dx) if want_dx else (dX, dY, dbias)
 
 

@@ -486,11 +486,11 @@ static double act_grad(int act, double x, double y) {
  * in orc_fused_linear; dbias then sums the selected rows only.  dx_out, when
  * not NULL, receives the unrounded dX (nrows x N).
  */
-int orc_fused_linear_bwd(int dtype, int act, const void *G, const void *W,
-                         const void *X, const void *Y, void *dX, void *dY,
-                         double *dbias, int64_t M, int64_t N, int64_t K,
-                         const int64_t *rows, int64_t nrows, int nthreads,
-                         double *dx_out) {
+static int run_bwd(int dtype, int act, const void *G, const void *W,
+                   const void *X, const void *Y, void *dX, void *dY,
+                   double *dbias, int64_t M, int64_t N, int64_t K,
+                   const int64_t *rows, int64_t nrows, int nthreads,
+                   double *dx_out, int unfused) {
     if (dtype < 0 || dtype > 2 || act < 0 || act > 3) return 1;
     if (M < 0 || N < 0 || K < 0) return 1;
     if ((!G && M * K > 0) || (!W && N * K > 0) || (!X && M * N > 0) || (!dX && M * N > 0)) return 1;
@@ -530,11 +530,22 @@ int orc_fused_linear_bwd(int dtype, int act, const void *G, const void *W,
                     for (int64_t k = 0; k < K; ++k) d += grow[k] * w[k];
                     const double x = dec_one(dtype, X, i * N + j);
                     const double y = (act == ORC_GLU) ? dec_one(dtype, Y, i * N + j) : 0.0;
-                    const double dx = d * act_grad(act, x, y);
+                    if (unfused) {
+                        /* the chain stores D in dtype before the elementwise pass */
+                        double t[1] = {d};
+                        uint16_t h[2];
+                        float f[1];
+                        void *slot = (dtype == ORC_F32) ? (void *)f : (void *)h;
+                        orc_encode(dtype, t, 1, slot);
+                        orc_decode(dtype, slot, 1, t);
+                        d = t[0];
+                    }
+                    double dx = d * act_grad(act, x, y);
+                    if (act == ORC_GLU) enc_one(dtype, d * x, dY, r * N + j);
+                    enc_one(dtype, dx, dX, r * N + j);
+                    if (unfused) dx = dec_one(dtype, dX, r * N + j); /* the sums read the stored dX */
                     D[r * N + j] = dx;
                     if (dx_out) dx_out[r * N + j] = dx;
-                    enc_one(dtype, dx, dX, r * N + j);
-                    if (act == ORC_GLU) enc_one(dtype, d * x, dY, r * N + j);
                 }
             }
         }
@@ -548,6 +559,28 @@ int orc_fused_linear_bwd(int dtype, int act, const void *G, const void *W,
     free(W64);
     free(D);
     return status;
+}
+
+int orc_fused_linear_bwd(int dtype, int act, const void *G, const void *W,
+                         const void *X, const void *Y, void *dX, void *dY,
+                         double *dbias, int64_t M, int64_t N, int64_t K,
+                         const int64_t *rows, int64_t nrows, int nthreads,
+                         double *dx_out) {
+    return run_bwd(dtype, act, G, W, X, Y, dX, dY, dbias, M, N, K, rows, nrows, nthreads, dx_out, 0);
+}
+
+/*
+ * The unfused backward chain (a product, an elementwise pass, a column sum,
+ * each storing its result): D is rounded to dtype before the elementwise
+ * pass, dX = round(round(D) * act'(X)), dY = round(round(D) * X), and dbias
+ * sums the stored (rounded) dX.  dx_out receives the rounded dX as FP64.
+ */
+int orc_unfused_bwd_chain(int dtype, int act, const void *G, const void *W,
+                          const void *X, const void *Y, void *dX, void *dY,
+                          double *dbias, int64_t M, int64_t N, int64_t K,
+                          const int64_t *rows, int64_t nrows, int nthreads,
+                          double *dx_out) {
+    return run_bwd(dtype, act, G, W, X, Y, dX, dY, dbias, M, N, K, rows, nrows, nthreads, dx_out, 1);
 }
 
 /* --------------------------------------------------------------- tile map */

@@ -263,3 +263,25 @@ def _bwd(lib, G=A_P, W=B_P, X=X_P, Y=None, dX=OUT_P, dY=None, db=DB_P, dt=F16, M
 def test_bwd_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _bwd(lib, **kwargs) == status
     assert msg in lib.fl_last_error().decode()
+
+
+def test_unfused_bwd_chain_rejects_bad_arguments(lib):
+    D_P, X2_P, DX_P = 0x7000000, 0x7800000, OUT_P
+    assert lib.fl_gemm_nt(A_P, B_P, OUT_P, 64, 64, 64, F32, None) == UNSUPPORTED
+    assert lib.fl_gemm_nt(A_P, B_P, A_P + 64, 64, 64, 64, F16, None) == INVALID
+    assert "out overlaps A" in lib.fl_last_error().decode()
+    ag = lib.fl_activation_grad
+    assert ag(D_P, X2_P, None, DX_P, None, 64, 64, RELU, F32, None) == UNSUPPORTED
+    assert ag(D_P, X2_P, None, DX_P, None, 64, 64, GLU, F16, None) == INVALID
+    assert "needs Y and dY" in lib.fl_last_error().decode()
+    assert ag(D_P, X2_P, Y_P, DX_P, None, 64, 64, RELU, F16, None) == INVALID
+    assert ag(D_P, X2_P, None, D_P + 2, None, 64, 64, RELU, F16, None) == INVALID
+    assert "partially overlaps D" in lib.fl_last_error().decode()
+    assert ag(D_P, X2_P, None, X2_P, None, 64, 64, RELU, F16, None) == INVALID
+    assert ag(D_P + 1, X2_P, None, DX_P, None, 64, 64, RELU, F16, None) == INVALID
+    assert ag(D_P, X2_P, None, DX_P, None, 64, 64, 7, F16, None) == INVALID
+    cs = lib.fl_column_sum
+    assert cs(X2_P, None, 64, 64, F16, None) == INVALID
+    assert cs(X2_P, X2_P + 64, 64, 64, F16, None) == INVALID
+    assert "sums overlaps X" in lib.fl_last_error().decode()
+    assert cs(X2_P, DB_P, 64, 64, F32, None) == UNSUPPORTED

@@ -638,3 +638,40 @@ def test_bwd_checker_flags_planted_mistakes(mistake):
     good = D * ((1 + Y) if act == "glu" else relu_grad)
     assert oracle.compare(good.astype(np.float32), dX, "f32")["ok"]
     assert oracle.compare_dbias(good.sum(axis=0), dbias, np.abs(good).sum(axis=0), M)["ok"]
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+def test_bwd_unfused_chain_equals_fused_on_exact_inputs(act):
+    """With every value exact, storing D and dX in between changes nothing."""
+    s, _ = _bwd_integer(33, 21, 6, "bf16", act, seed=11)
+    fused = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="bf16")
+    chain = oracle.unfused_bwd_chain(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="bf16")
+    assert np.array_equal(fused[0], chain[0]) and np.array_equal(fused[2], chain[2])
+    if act == "glu":
+        assert np.array_equal(fused[1], chain[1])
+
+
+@pytest.mark.parametrize("act", ["relu", "glu"])
+def test_bwd_unfused_chain_rounds_after_each_stage(act):
+    """The chain is round(round(D) * g) with g = act'(X) exact here (0/1, or
+    1 + Y), round(D) from the product alone (act none), and its dbias the
+    FP64 sum of the stored dX."""
+    rng = np.random.default_rng(12)
+    M, N, K = 40, 36, 50
+    G, W = rng.standard_normal((M, K)), rng.standard_normal((N, K)) / np.sqrt(K)
+    X, Y = rng.standard_normal((M, N)), rng.integers(-2, 3, (M, N)).astype(np.float64)
+    s = {k: synth.to_storage(v, "f16") for k, v in dict(G=G, W=W, X=X, Y=Y).items()}
+    D16 = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], None, act="none", dtype="f16")[0]
+    Xd, Yd = oracle.decode(s["X"], "f16"), oracle.decode(s["Y"], "f16")
+    g = (Xd > 0).astype(np.float64) if act == "relu" else 1.0 + Yd
+    dX, dY, db = oracle.unfused_bwd_chain(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="f16")
+    want = oracle.encode(oracle.decode(D16, "f16") * g, "f16")
+    assert np.array_equal(dX, want)
+    assert np.array_equal(db, oracle.decode(dX, "f16").sum(axis=0))
+    if act == "glu":
+        assert np.array_equal(dY, oracle.encode(oracle.decode(D16, "f16") * Xd, "f16"))
+    # and, where the derivative is not 0 or 1 (the gate's 1 + Y = 3 here), it
+    # differs from the fused result, which rounds once
+    if act == "glu":
+        fused = oracle.fused_linear_bwd(s["G"], s["W"], s["X"], s["Y"], act=act, dtype="f16")[0]
+        assert not np.array_equal(fused, dX)

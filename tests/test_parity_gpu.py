@@ -702,3 +702,49 @@ def test_bwd_full_size(name):
                                              want_dx=True)
     res = oracle.compare_dbias(db[cols], rdb, np.abs(rdx).sum(axis=0), w.M)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("shape", [(200, 264, 136), (131, 77, 45)])
+def test_bwd_unfused_chain_matches_oracle_chain(dtype, act, shape):
+    """fl_gemm_nt, fl_activation_grad and fl_column_sum, each storing its
+    result, against the oracle's chain that rounds after every stage."""
+    M, N, K = shape
+    d = synth.draw_bwd(M, N, K, dtype, act, seed=29)
+    G, W, X, Y = (to_dev(d[k], dtype) for k in ("G", "W", "X", "Y"))
+    say("bwd unfused chain", dtype, act, shape)
+    D = fl.gemm_nt(G, W)
+    dX, dY = fl.activation_grad(D, X, Y, act=act)
+    db = fl.column_sum(dX)
+    torch.cuda.synchronize()
+    rX, rY, rdb, rdx = oracle.unfused_bwd_chain(d["G"], d["W"], d["X"], d["Y"], act=act, dtype=dtype, want_dx=True)
+    _assert_close(to_host(dX, dtype), rX, dtype, "chain dX")
+    if act == "glu":
+        _assert_close(to_host(dY, dtype), rY, dtype, "chain dY")
+    # the column sums are of the device's own stored dX: compare with the
+    # FP64 sums of those values (the reduction alone), and with the oracle
+    dev_dx = oracle.decode(to_host(dX, dtype), dtype)
+    res = oracle.compare_dbias(db.cpu().numpy(), dev_dx.sum(axis=0), np.abs(dev_dx).sum(axis=0), M)
+    assert res["ok"], res
+    res = oracle.compare_dbias(db.cpu().numpy(), rdb, np.abs(rdx).sum(axis=0) + np.abs(dev_dx).sum(axis=0), M)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+def test_bwd_unfused_chain_integer_equals_fused(dtype):
+    """Exact values: the chain and the fused kernel give the same bits, and
+    D may be overwritten in place by dX."""
+    M, N, K = 257, 264, 5
+    d = synth.draw_bwd_integer(M, N, K, dtype, "glu", seed=31)
+    G, W, X, Y = (to_dev(d[k], dtype) for k in ("G", "W", "X", "Y"))
+    say("bwd unfused integer", dtype)
+    D = fl.gemm_nt(G, W)
+    dX, dY = fl.activation_grad(D, X, Y, act="glu", dX=D)
+    db = fl.column_sum(dX)
+    fX, fY, fdb = fl.fused_linear_bwd(G, W, X, Y, act="glu")
+    torch.cuda.synchronize()
+    assert dX.data_ptr() == D.data_ptr()
+    assert np.array_equal(to_host(dX, dtype).view(np.uint8), to_host(fX, dtype).view(np.uint8))
+    assert np.array_equal(to_host(dY, dtype).view(np.uint8), to_host(fY, dtype).view(np.uint8))
+    assert np.array_equal(db.cpu().numpy(), fdb.cpu().numpy())
