@@ -608,6 +608,43 @@ struct Dma16 {
     static_assert(!BWD || (!SHARED_EPI && WN == 64 && 32 * DB_ROW <= EPI_WAVE),
                   "backward: own-area staging, one bias column per lane");
 
+    // Side input of the epilogue staged through LDS: SIDE 1 = Y (gate), 2 =
+    // R (residual, or the saved X of the backward epilogue), 0 = none (or
+    // one-byte output codes, whose staging rows are too narrow for it).
+    // When N % 8 == 0 (no 16-byte chunk of a row crosses N), the tile's side
+    // input is copied straight into the output staging area, at the place
+    // of each output element, with one direct-to-LDS load per 1 KB, all
+    // issued as the epilogue starts and waited for once.  A lane then reads
+    // its values there and overwrites them with its results.  Otherwise it
+    // is loaded into registers, one row block ahead.  The gate uses this
+    // path for Y, so a residual or saved X next to it stays in registers.
+    static constexpr int SIDE = QF >= 0 ? 0 : ACT == FL_ACT_GLU ? 1 : (RES || BWD) ? 2 : 0;
+
+    // This wave's part of the staging area: its own 128 x WN tile, or in
+    // the shared layout BM / WAVES whole rows of the tile.  Rows are EPI_ROW
+    // bytes: the data and one 16-byte pad chunk, which is filled with zeros
+    // (lanes given kOob).  Rows past M and columns past N read zeros.
+    __device__ __forceinline__ static void stage_side(const GemmArgs &a, const void *src, int m0, int n0, int wave,
+                                                      int wm, int wn, int lane, uint32_t lds_addr) {
+        constexpr int RC = EPI_ROW / 16;  // 16-byte chunks per staged row, the last one padding
+        constexpr int YR = SHARED_EPI ? BM / WAVES : 128;
+        constexpr int YW = SHARED_EPI ? BN : WN;
+        static_assert(EPI_ROW % 16 == 0 && RC == YW / 8 + 1 && (YR * RC) % 64 == 0, "whole copies of padded rows");
+        const int r0 = SHARED_EPI ? wave * YR : wm * 128, c0 = SHARED_EPI ? 0 : wn * WN;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(
+            lds_addr + (SHARED_EPI ? (uint32_t)(r0 * EPI_ROW) : (uint32_t)(wave * EPI_WAVE)));
+        const size_t o_org = (size_t)m0 * a.N + n0;
+        const i32x4_t rS = sgpr_rsrc(src ? static_cast<const char *>(src) + o_org * 2 : nullptr,
+                                     src ? ((size_t)a.M * a.N - o_org) * 2 : 0);
+#pragma unroll
+        for (int j = 0; j < YR * RC / 64; ++j) {
+            const int q = 64 * j + lane, row = q / RC, c = q - row * RC;
+            const int col = c0 + c * 8;
+            const bool ok = c < RC - 1 && m0 + r0 + row < a.M && n0 + col < a.N;
+            lds_copy16(rS, ok ? (uint32_t)((r0 + row) * a.N + col) * 2 : kOob, 0, base + j * 1024);
+        }
+    }
+
     // The elements e < cvalid of one 16-byte chunk bound for byte offset
     // off of out (nothing for off == kOob).
     __device__ __forceinline__ static void store_chunk_elems(const u32x4_t v, __amdgpu_buffer_rsrc_t rO, uint32_t off,
@@ -681,25 +718,37 @@ struct Dma16 {
         // phase 2, so out may alias Y or R.
         constexpr int RA = ACT == FL_ACT_GLU ? 0 : 1;  // residual row blocks loaded ahead
         quad_t yq[2][NG], rq[RA + 1][NG];
-        if constexpr (ACT == FL_ACT_GLU) {
+        // the side input through LDS (see stage_side)
+        const bool slds = SIDE != 0 && (a.N & 7) == 0;
+        const bool y_reg = ACT == FL_ACT_GLU && !(SIDE == 1 && slds);
+        const bool r_reg = has_r && !(SIDE == 2 && slds);
+        if constexpr (SIDE != 0) {
+            if (slds) {
+                stage_side(a, SIDE == 1 ? a.Y : r_live ? r_src : nullptr, m0, n0, wave, wm, wn, lane,
+                           (uint32_t)(uintptr_t)(FL_LDS void *)lds);
+                wait_vm<0>();
+                if constexpr (SHARED_EPI) __syncthreads();  // a lane's values were copied by other waves
+            }
+        }
+        if (y_reg) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) yq[0][g] = base::load4(rY, yoff(0, g), valid[g]);
         }
         if constexpr (RA && has_r) {
+            if (r_reg) {
 #pragma unroll
-            for (int p = 0; p < RA; ++p)
+                for (int p = 0; p < RA; ++p)
 #pragma unroll
-                for (int g = 0; g < NG; ++g) rq[p][g] = base::load4(rR, yoff(p, g), valid[g]);
+                    for (int g = 0; g < NG; ++g) rq[p][g] = base::load4(rR, yoff(p, g), valid[g]);
+            }
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            if constexpr (ACT == FL_ACT_GLU) {
-                if (mi + 1 < 4) {
+            if (y_reg && mi + 1 < 4) {
 #pragma unroll
-                    for (int g = 0; g < NG; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
-                }
+                for (int g = 0; g < NG; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
             }
-            if (has_r && mi + RA < 4) {
+            if (r_reg && mi + RA < 4) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     rq[(mi + RA) % (RA + 1)][g] = base::load4(rR, yoff(mi + RA, g), valid[g]);
@@ -707,6 +756,16 @@ struct Dma16 {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int ni = g >> 2, q = g & 3;
+                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's tile
+                if constexpr (SIDE != 0) {
+                    if (slds) {
+                        const quad_t s = *(const FL_LDS quad_t *)(wbuf + r * EPI_ROW + c * 2);
+                        if constexpr (SIDE == 1)
+                            yq[mi & 1][g] = s;
+                        else
+                            rq[mi % (RA + 1)][g] = s;
+                    }
+                }
                 float v[4];
                 if constexpr (BWD) {
                     // dX = D * act'(X), and for the gate dY = D * X (D: the
@@ -753,7 +812,6 @@ struct Dma16 {
                     if constexpr (has_r) x += base::elem_f32(rq[mi % (RA + 1)][g], e);
                     v[e] = activate<ACT>(x, y);
                 }
-                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's tile
                 if constexpr (QF < 0) {
                     u32x2_t w;
                     w[0] = io::from_f32(v[0]) | ((uint32_t)io::from_f32(v[1]) << 16);
