@@ -748,3 +748,58 @@ def test_bwd_unfused_chain_integer_equals_fused(dtype):
     assert np.array_equal(to_host(dX, dtype).view(np.uint8), to_host(fX, dtype).view(np.uint8))
     assert np.array_equal(to_host(dY, dtype).view(np.uint8), to_host(fY, dtype).view(np.uint8))
     assert np.array_equal(db.cpu().numpy(), fdb.cpu().numpy())
+
+
+# ------------------------------------------- epilogue side input: two paths
+# With N a multiple of 8 the epilogue's side input (the gate's Y, else the
+# residual or the saved X) is copied into LDS before the epilogue; otherwise
+# it is loaded into registers.  One extra column (N = 521 against 520) moves
+# the same problem onto the other path without changing the arithmetic of
+# the first 520 columns, so those must agree bit for bit.
+
+def _first_cols(d, n, keys_cols, keys_rows=()):
+    e = dict(d)
+    for k in keys_cols:
+        if e.get(k) is not None:
+            e[k] = np.ascontiguousarray(e[k][..., :n])
+    for k in keys_rows:
+        if e.get(k) is not None:
+            e[k] = np.ascontiguousarray(e[k][:n])
+    return e
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act,residual", [("glu", False), ("relu", True), ("gelu_tanh", True), ("glu", True)])
+@pytest.mark.parametrize("cfg", [0, 5, 6, 7])
+def test_side_input_paths_bit_identical(dtype, act, residual, cfg):
+    M, K = 300, 200
+    d = synth.draw(M, 521, K, dtype, act, seed=43)
+    if residual:
+        d = _with_residual(d, dtype, seed=44)
+    d520 = _first_cols(d, 520, ("B", "bias", "Y", "R"))
+    say("side input paths", dtype, act, residual, cfg)
+    wide = _run_fused(d, act, dtype, tile_cfg=cfg)
+    narrow = _run_fused(d520, act, dtype, tile_cfg=cfg)
+    ref = oracle.fused_linear(d520["A"], d520["B"], d520["bias"], d520["Y"], act=act, dtype=dtype, R=d520.get("R"))
+    _assert_close(narrow, ref, dtype, "N = 520")
+    assert np.array_equal(narrow.view(np.uint8), np.ascontiguousarray(wide[:, :520]).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
+@pytest.mark.parametrize("cfg", [5, 2])
+def test_bwd_side_input_paths_bit_identical(dtype, act, cfg):
+    M, K = 300, 200
+    d = synth.draw_bwd(M, 521, K, dtype, act, seed=47)
+    d520 = _first_cols(d, 520, ("X", "Y"), ("W",))
+    say("bwd side input paths", dtype, act, cfg)
+    wX, wY, wdb = _run_bwd(d, act, dtype, tile_cfg=cfg)
+    nX, nY, ndb = _run_bwd(d520, act, dtype, tile_cfg=cfg)
+    _check_bwd(nX, nY, ndb, d520, act, dtype, "N = 520")
+    assert np.array_equal(nX.view(np.uint8), np.ascontiguousarray(wX[:, :520]).view(np.uint8))
+    if act == "glu":
+        assert np.array_equal(nY.view(np.uint8), np.ascontiguousarray(wY[:, :520]).view(np.uint8))
+    _, _, rdb, rdx = oracle.fused_linear_bwd(d520["G"], d520["W"], d520["X"], d520["Y"], act=act, dtype=dtype,
+                                             want_dx=True)
+    res = oracle.compare_dbias(wdb[:520], rdb, np.abs(rdx).sum(axis=0), M)
+    assert res["ok"], res
