@@ -789,8 +789,8 @@ struct Dma16 {
                     if constexpr (ACT == FL_ACT_GLU) {
                         const uint32_t off = yoff(mi, g);
                         u32x2_t w;
-                        w[0] = io::from_f32(dy[0]) | ((uint32_t)io::from_f32(dy[1]) << 16);
-                        w[1] = io::from_f32(dy[2]) | ((uint32_t)io::from_f32(dy[3]) << 16);
+                        w[0] = io::pack2(dy[0], dy[1]);
+                        w[1] = io::pack2(dy[2], dy[3]);
                         if (valid[g] >= 4) {
                             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, w), rDY, off, 0, 0);
                         } else {
@@ -814,8 +814,8 @@ struct Dma16 {
                 }
                 if constexpr (QF < 0) {
                     u32x2_t w;
-                    w[0] = io::from_f32(v[0]) | ((uint32_t)io::from_f32(v[1]) << 16);
-                    w[1] = io::from_f32(v[2]) | ((uint32_t)io::from_f32(v[3]) << 16);
+                    w[0] = io::pack2(v[0], v[1]);
+                    w[1] = io::pack2(v[2], v[3]);
                     *(FL_LDS u32x2_t *)(wbuf + r * EPI_ROW + c * 2) = w;
                 } else {
                     *(FL_LDS uint32_t *)(wbuf + r * EPI_ROW + c) = quantize4<QF>(v, a.scale);

@@ -47,6 +47,9 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int v2u32_t __attribute__((ext_vector_type(2)));
@@ -71,12 +74,20 @@ template <> struct Io<FL_F16> {
     static constexpr int size = 2;
     __device__ static float to_f32(raw v) { return (float)__builtin_bit_cast(_Float16, v); }
     __device__ static raw from_f32(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+    // a in the low half, b in the high half: one v_cvt_pk_f16_f32 (round to
+    // nearest even, as the scalar conversion)
+    __device__ static uint32_t pack2(float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+    }
 };
 template <> struct Io<FL_BF16> {
     using raw = uint16_t;
     static constexpr int size = 2;
     __device__ static float to_f32(raw v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
     __device__ static raw from_f32(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+    __device__ static uint32_t pack2(float a, float b) {  // one v_cvt_pk_bf16_f32
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+    }
 };
 
 // ------------------------------------------------------------- epilogue ops

@@ -803,3 +803,46 @@ def test_bwd_side_input_paths_bit_identical(dtype, act, cfg):
                                              want_dx=True)
     res = oracle.compare_dbias(wdb[:520], rdb, np.abs(rdx).sum(axis=0), M)
     assert res["ok"], res
+
+
+# ------------------------------------------ the one rounding, bit for bit
+# At K = 1 the accumulator is the exact product a*b (two 16-bit values, 22
+# significant bits at most), so x = a*b + bias is one fp32 addition that
+# numpy's float32 arithmetic reproduces exactly, and the stored output must
+# be the round-to-nearest-even of act(x) in the output type: the paired
+# conversions of the direct kernels and the single ones of the
+# register-staged kernel alike.  Half the rows and columns are scaled down
+# so that fp16 results also fall among the subnormals.
+
+def _rne_bf16_bits(x32):
+    u = x32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu"])
+@pytest.mark.parametrize("N", [520, 521])
+@pytest.mark.parametrize("cfg", [0, 3, 5, 6, 7])
+def test_k1_output_rounding_bit_exact(dtype, act, N, cfg):
+    M = 300
+    rng = np.random.default_rng(N + 7 * cfg)
+    a = rng.standard_normal((M, 1)); a[M // 2:] *= 1e-2
+    b = rng.standard_normal((1, N)); b[:, N // 2:] *= 1e-2
+    bias = rng.standard_normal(N); bias[N // 2:] *= 1e-5
+    d = {"A": synth.to_storage(a, dtype), "B": synth.to_storage(b, dtype), "bias": synth.to_storage(bias, dtype),
+         "Y": None}
+    say("K=1 rounding", dtype, act, N, cfg)
+    out = _run_fused(d, act, dtype, tile_cfg=cfg)
+
+    def f32(raw):
+        return raw.astype(np.float32) if dtype == "f16" else (raw.astype(np.uint32) << 16).view(np.float32)
+    x = f32(d["A"]) * f32(d["B"]) + f32(d["bias"])[None, :]  # one fp32 multiply (exact) and one fp32 add
+    if act == "relu":
+        x = np.where(x > 0, x, np.float32(0.0))
+    ref = x.astype(np.float16).view(np.uint16) if dtype == "f16" else _rne_bf16_bits(x)
+    got = out.view(np.uint16)
+    nz = x != 0  # the sign of a zero result is not part of the contract
+    assert np.array_equal(got[nz], ref[nz]), f"{np.count_nonzero(got[nz] != ref[nz])} outputs differ"
+    if dtype == "f16":
+        sub = (np.abs(x) < 6.1e-5) & nz
+        assert sub.sum() > 1000, "the case must reach fp16 subnormals"
