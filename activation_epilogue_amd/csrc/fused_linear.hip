@@ -159,7 +159,7 @@ fl_status check_dims(int64_t M, int64_t N, int64_t K) {
 // Shared validation of the GEMM-shaped entry points.
 fl_status validate_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y,
                         const void *out, int64_t M, int64_t N, int64_t K, int act, int dtype,
-                        const fl_options *opt, bool out_optional = false) {
+                        const fl_options *opt, bool out_optional = false, bool b_kn = true) {
     if (!valid_dtype(dtype)) return fail(FL_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (!valid_act(act)) return fail(FL_ERR_INVALID_ARG, "unknown activation %d", act);
     fl_status s = check_dims(M, N, K);
@@ -178,6 +178,11 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
     // In-tile byte offsets are 32-bit: 256 rows of A, of Y and of out must span < 2^31 bytes.
     if ((size_t)K * es * 256 >= 0x80000000ull || (size_t)N * es * 256 >= 0x80000000ull)
         return fail(FL_ERR_UNSUPPORTED, "K or N too large (256 rows must span < 2 GiB)");
+    // B given as (K, N) is read through the whole K range from the tile's
+    // first column with 32-bit offsets (B as (N, K), the transposed operand,
+    // only through the tile's 256 rows).
+    if (b_kn && (size_t)K * N * es >= 0x80000000ull)
+        return fail(FL_ERR_UNSUPPORTED, "B too large (its K x N elements must span < 2 GiB)");
     const size_t a_bytes = (size_t)M * K * es, b_bytes = (size_t)K * N * es, o_bytes = (size_t)M * N * es;
     const size_t bias_bytes = bias ? (size_t)N * es : 0;
     if (!A && a_bytes) return fail(FL_ERR_INVALID_ARG, "A is NULL");
@@ -400,6 +405,7 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (!A8 && a_bytes) return fail(FL_ERR_INVALID_ARG, "A is NULL");
     if (!B8 && b_bytes) return fail(FL_ERR_INVALID_ARG, "B is NULL");
     if (K * 256 >= 0x80000000ll) return fail(FL_ERR_UNSUPPORTED, "K too large (256 rows must span < 2 GiB)");
+    if (b_bytes >= 0x80000000ull) return fail(FL_ERR_UNSUPPORTED, "B too large (its K x N bytes must span < 2 GiB)");
     if (overlaps(out, o_bytes, A8, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
     if (overlaps(out, o_bytes, B8, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
     // The two-per-CU and 256x192 variants have no FP8 build: where the
@@ -420,7 +426,7 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for fp16 and bf16");
     // G plays A (M,K) and W (N,K) has B's size; X is checked as a residual
     // would be (it may be dX itself), Y as the gate's operand.
-    fl_status s = validate_gemm(G, W, nullptr, X, Y, dX, M, N, K, act, dtype, opt);
+    fl_status s = validate_gemm(G, W, nullptr, X, Y, dX, M, N, K, act, dtype, opt, false, /*b_kn=*/false);
     if (s != FL_OK) return s;
     const size_t es = elem_size(dtype);
     const size_t g_bytes = (size_t)M * K * es, w_bytes = (size_t)N * K * es, o_bytes = (size_t)M * N * es;
@@ -474,7 +480,8 @@ fl_status fl_gemm_nt(const void *A, const void *Bt, void *D, int64_t M, int64_t 
                      void *stream) {
     clear_error();
     if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the transposed-B product is built for fp16 and bf16");
-    fl_status s = validate_gemm(A, Bt, nullptr, nullptr, nullptr, D, M, N, K, FL_ACT_NONE, dtype, nullptr);
+    fl_status s = validate_gemm(A, Bt, nullptr, nullptr, nullptr, D, M, N, K, FL_ACT_NONE, dtype, nullptr, false,
+                                /*b_kn=*/false);
     if (s != FL_OK) return s;
     if (M == 0 || N == 0) return FL_OK;
     const fl_options o = bwd_tiles(dtype, M, N, K);

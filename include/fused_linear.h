@@ -42,7 +42,11 @@
  *              overlap it.
  *   Shapes     M, N, K >= 0 and <= 2^31-1.  M == 0 or N == 0 returns FL_OK
  *              without launching.  K == 0 is valid: out = act(bias) on every
- *              row (bias NULL counts as zero).
+ *              row (bias NULL counts as zero).  Offsets inside a tile are
+ *              32-bit: 256 rows of A and of out (256*K and 256*N elements)
+ *              and the whole of B (K*N elements; not the transposed operand
+ *              of the backward entries) must each span less than 2 GiB, else
+ *              FL_ERR_UNSUPPORTED.
  *   Alignment  Pointers must be aligned to the element size.  16-byte aligned
  *              pointers with K and N multiples of 16 bytes / element size take
  *              the vector-load path; everything else takes the element path.

@@ -61,6 +61,7 @@ def _fused(lib, A=A_P, B=B_P, bias=BIAS_P, Y=None, out=OUT_P, M=64, N=64, K=64, 
     (dict(K=-5), INVALID, "negative size"),
     (dict(N=2 ** 31), UNSUPPORTED, "above 2^31-1"),
     (dict(K=2 ** 22), UNSUPPORTED, "too large"),
+    (dict(K=32768, N=32768), UNSUPPORTED, "B too large"),  # B of 2 GiB: 32-bit offsets
     (dict(act=7), INVALID, "unknown activation"),
     (dict(dt=9), INVALID, "unknown dtype"),
     (dict(A=A_P + 1), INVALID, "not aligned"),
@@ -92,6 +93,8 @@ def test_bad_options(lib):
 
 def test_unfused_entry_points_reject_bad_arguments(lib):
     assert lib.fl_gemm(None, B_P, OUT_P, 8, 8, 8, F32, None) == INVALID
+    assert lib.fl_gemm(A_P, B_P, OUT_P, 8, 32768, 32768, F16, None) == UNSUPPORTED
+    assert "B too large" in lib.fl_last_error().decode()
     assert lib.fl_bias_add(OUT_P, None, 8, 8, F32, None) == INVALID
     assert lib.fl_bias_add(OUT_P, OUT_P + 4, 8, 8, F32, None) == INVALID
     assert lib.fl_activation(OUT_P, None, OUT_P + 2, 8, 8, RELU, F16, None) == INVALID
@@ -224,6 +227,7 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
     (dict(act=GLU), INVALID, "the gate needs Y"),
     (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
     (dict(opt=fl.Options(0, 0, 9, 0, None)), UNSUPPORTED, "tile_cfg 9"),
+    (dict(K=65536, N=32768), UNSUPPORTED, "B too large"),
 ])
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _fp8(lib, **kwargs) == status
