@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
     p.add_argument("--tile-cfg", type=int, default=0, help="fl_options.tile_cfg (0 = automatic)")
+    p.add_argument("--operand-toggle", action="store_true",
+                   help="time the fused 4096^3 fp16 ReLU kernel on operands with fewer toggling bits instead "
+                        "(power diagnostic; one JSON line)")
     p.add_argument("--mfma-ceiling", action="store_true",
                    help="instead of the workload: the sustained MFMA rate of this GPU (register-only MFMA loop)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -197,10 +200,52 @@ def mfma_ceiling(args):
     print(json.dumps(res), flush=True)
 
 
+def operand_toggle(args):
+    """The 4096^3 fp16 ReLU fused kernel, unchanged, on operands whose bits
+    toggle less: the seeded N(0, 1/K) inputs, the same with only the top 3
+    of 10 mantissa bits kept, a constant (1/64), and zeros.  The work and
+    the memory traffic are the same in every case; only the power the
+    matrix units draw, and so the clock the chip holds, differs.  One JSON
+    line (event-timed average per launch)."""
+    import torch
+    import activation_epilogue_amd as fl
+    from activation_epilogue_amd import synth
+    w = synth.WORKLOADS["relu_f16_4096x4096x4096"]
+    d = synth.draw_workload(w)
+    A0 = torch.from_numpy(d["A"]).to("cuda")
+    B0 = torch.from_numpy(d["B"]).to("cuda")
+    bias = torch.from_numpy(d["bias"]).to("cuda")
+    out = torch.empty(w.M, w.N, device="cuda", dtype=torch.float16)
+    stream = torch.cuda.current_stream()
+
+    def trimmed(t):  # keep the sign, the exponent and the top 3 mantissa bits
+        return (t.view(torch.int16) & ~0x7F).view(torch.float16)
+    cases = {"random": (A0, B0), "random_3_mantissa_bits": (trimmed(A0), trimmed(B0)),
+             "constant_1_64": (torch.full_like(A0, 1 / 64), torch.full_like(B0, 1 / 64)),
+             "zeros": (torch.zeros_like(A0), torch.zeros_like(B0))}
+    res = {"kernel": "fused_linear_dma16_kernel (relu_f16_4096x4096x4096, automatic tile)",
+           "peak_datasheet_tflops": PEAK_TFLOPS["f16"]}
+    for name, (A, B) in cases.items():
+        def step():
+            fl.fused_linear(A, B, bias, act="relu", out=out)
+        t_end = time.perf_counter() + max(args.prewarm_s, 0.5)
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        ms, _ = time_loop(step, args.steps, args.warmup, stream)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        res[name] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["f16"], 4),
+                     "us_per_launch": round(ms * 1e3, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.mfma_ceiling:
         return mfma_ceiling(args)
+    if args.operand_toggle:
+        return operand_toggle(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
               "path (the layer shards by output columns or rows with no communication; see DESIGN.md).",
