@@ -289,3 +289,27 @@ def test_unfused_bwd_chain_rejects_bad_arguments(lib):
     assert cs(X2_P, X2_P + 64, 64, 64, F16, None) == INVALID
     assert "sums overlaps X" in lib.fl_last_error().decode()
     assert cs(X2_P, DB_P, 64, 64, F32, None) == UNSUPPORTED
+
+
+def test_error_message_is_per_thread(lib):
+    """Each host thread reads the message of its own last failed call
+    (validation errors only: nothing is launched)."""
+    import threading
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, kwargs):
+        barrier.wait()
+        for _ in range(200):
+            st = _fused(lib, **kwargs)
+            seen[name] = (st, lib.fl_last_error().decode())
+            assert seen[name][0] == INVALID
+
+    ta = threading.Thread(target=worker, args=("neg", dict(M=-1)))
+    tb = threading.Thread(target=worker, args=("null", dict(A=None)))
+    ta.start(); tb.start(); ta.join(); tb.join()
+    assert "negative size" in seen["neg"][1] and "A is NULL" not in seen["neg"][1]
+    assert "A is NULL" in seen["null"][1] and "negative size" not in seen["null"][1]
+    # a successful call clears this thread's message
+    assert _fused(lib, M=-1) == INVALID and lib.fl_last_error() != b""
+    assert _fused(lib, M=0) == OK and lib.fl_last_error() == b""
