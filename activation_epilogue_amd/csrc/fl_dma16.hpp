@@ -619,6 +619,12 @@ struct Dma16 {
     // is loaded into registers, one row block ahead.  The gate uses this
     // path for Y, so a residual or saved X next to it stays in registers.
     static constexpr int SIDE = QF >= 0 ? 0 : ACT == FL_ACT_GLU ? 1 : (RES || BWD) ? 2 : 0;
+    // The gate's backward has a second side input, the saved X: where a
+    // second staging area fits beside the first (own-area layout, one
+    // workgroup per CU), it is copied into that area in the same way.
+    static constexpr bool SIDE2 = BWD && ACT == FL_ACT_GLU && !SHARED_EPI && OCC == 1 && 2 * EPI_BYTES <= 163840;
+    static constexpr int SMEM_BYTES =
+        NBUF * BUF_BYTES > (SIDE2 ? 2 : 1) * EPI_BYTES ? NBUF * BUF_BYTES : (SIDE2 ? 2 : 1) * EPI_BYTES;
 
     // This wave's part of the staging area: its own 128 x WN tile, or in
     // the shared layout BM / WAVES whole rows of the tile.  Rows are EPI_ROW
@@ -721,11 +727,15 @@ struct Dma16 {
         // the side input through LDS (see stage_side)
         const bool slds = SIDE != 0 && (a.N & 7) == 0;
         const bool y_reg = ACT == FL_ACT_GLU && !(SIDE == 1 && slds);
-        const bool r_reg = has_r && !(SIDE == 2 && slds);
+        const bool r_reg = has_r && !((SIDE == 2 || SIDE2) && slds);
+        FL_LDS char *wbuf2 = lds + EPI_BYTES + wave * EPI_WAVE;  // SIDE2: the saved X
         if constexpr (SIDE != 0) {
             if (slds) {
                 stage_side(a, SIDE == 1 ? a.Y : r_live ? r_src : nullptr, m0, n0, wave, wm, wn, lane,
                            (uint32_t)(uintptr_t)(FL_LDS void *)lds);
+                if constexpr (SIDE2)
+                    stage_side(a, r_live ? r_src : nullptr, m0, n0, wave, wm, wn, lane,
+                               (uint32_t)(uintptr_t)(FL_LDS void *)(lds + EPI_BYTES));
                 wait_vm<0>();
                 if constexpr (SHARED_EPI) __syncthreads();  // a lane's values were copied by other waves
             }
@@ -764,6 +774,8 @@ struct Dma16 {
                             yq[mi & 1][g] = s;
                         else
                             rq[mi % (RA + 1)][g] = s;
+                        if constexpr (SIDE2)
+                            rq[mi % (RA + 1)][g] = *(const FL_LDS quad_t *)(wbuf2 + r * EPI_ROW + c * 2);
                     }
                 }
                 float v[4];
@@ -1020,7 +1032,7 @@ constexpr int kCopySpread = 2;
 template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF, int IN = DT>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
     using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF, IN>;
-    __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[T::SMEM_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.
     const int ntiles = a.tiles_m * a.tiles_n;
@@ -1040,7 +1052,7 @@ __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kern
 template <int DT, int ACT, int BK, int BN, int WAVES_N>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, 1) fused_linear_bwd_kernel(GemmArgs a) {
     using T = Dma16<DT, ACT, BK, BN, WAVES_N, kCopySpread, 1, false, -1, DT, true>;
-    __shared__ __attribute__((aligned(1024))) char smem[(T::NBUF * T::BUF_BYTES > T::EPI_BYTES) ? T::NBUF * T::BUF_BYTES : T::EPI_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[T::SMEM_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     const int G = gridDim.x;
     const int slot = a.xcd_remap ? xcd_logical(blockIdx.x, G) : (int)blockIdx.x;
