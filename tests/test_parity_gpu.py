@@ -846,3 +846,43 @@ def test_k1_output_rounding_bit_exact(dtype, act, N, cfg):
     if dtype == "f16":
         sub = (np.abs(x) < 6.1e-5) & nz
         assert sub.sum() > 1000, "the case must reach fp16 subnormals"
+
+
+def _shifted(t):
+    """A copy of t at an address one element past a 16-byte boundary."""
+    s = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)[1:].view(t.shape)
+    s.copy_(t)
+    return s
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_side_input_unaligned_bit_identical(dtype):
+    """Y, R, the saved X and the outputs one element off 16-byte alignment
+    (N = 520: the side input goes through LDS in 16-byte copies at those
+    addresses) give the aligned run's bits."""
+    M, N, K = 300, 520, 200
+    d = _with_residual(synth.draw(M, N, K, dtype, "glu", seed=91), dtype, seed=92)
+    A, B, bias, Y, R = (to_dev(d[k], dtype) for k in ("A", "B", "bias", "Y", "R"))
+    say("unaligned side inputs, forward", dtype)
+    for act, kw in (("glu", {}), ("relu", {"R": R}), ("glu", {"R": R})):
+        y = Y if act == "glu" else None
+        ref = fl.fused_linear(A, B, bias, y, act=act, **kw)
+        kw2 = {"R": _shifted(R)} if "R" in kw else {}
+        out2 = _shifted(torch.empty_like(ref))
+        got = fl.fused_linear(A, B, bias, _shifted(Y) if y is not None else None, act=act, out=out2, **kw2)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(got, dtype).view(np.uint16), to_host(ref, dtype).view(np.uint16)), act
+    b = synth.draw_bwd(M, N, K, dtype, "glu", seed=93)
+    G, W, X, Yb = (to_dev(b[k], dtype) for k in ("G", "W", "X", "Y"))
+    say("unaligned side inputs, backward", dtype)
+    for act in ("relu", "glu"):
+        y = Yb if act == "glu" else None
+        rX, rY, _ = fl.fused_linear_bwd(G, W, X, y, act=act, dbias=None)
+        dX2 = _shifted(torch.empty_like(rX))
+        dY2 = _shifted(torch.empty_like(rX)) if act == "glu" else None
+        gX, gY, _ = fl.fused_linear_bwd(G, W, _shifted(X), _shifted(y) if y is not None else None, act=act,
+                                        dX=dX2, dY=dY2, dbias=None)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(gX, dtype).view(np.uint16), to_host(rX, dtype).view(np.uint16)), act
+        if act == "glu":
+            assert np.array_equal(to_host(gY, dtype).view(np.uint16), to_host(rY, dtype).view(np.uint16))
