@@ -124,6 +124,13 @@ def launch_times(fn, n, stream, scrub=None):
     return {"n": n, "median_ms": round(ts[n // 2], 4), "min_ms": round(ts[0], 4), "max_ms": round(ts[-1], 4)}
 
 
+# The TLX page's own table ("Optimizing GEMM + Activation on CDNA4 with
+# TLX", the benchmark after Version 4): its best fused gate kernel on one
+# MI350X, fp16, M=1024, N=21568, TFLOP/s by K.  Another machine: context
+# for the same workloads, not a target.
+PAGES_GATE_MI350X = {256: 357.0, 512: 502.0, 1024: 619.0}
+
+
 def device_info():
     import torch
     p = torch.cuda.get_device_properties(0)
@@ -444,6 +451,11 @@ def main():
                                          "unfused": (5 + (1 if w.act == "glu" else 0)) * mn * es},
         }
 
+    if (w.act == "glu" and not w.bwd and not w.in8 and not w.residual and w.dtype == "f16"
+            and (w.M, w.N) == (1024, 21568) and w.K in PAGES_GATE_MI350X):
+        ref = PAGES_GATE_MI350X[w.K]
+        result["pages_context"] = {"value": ref, "unit": "TFLOP/s", "hardware": "1x MI350X",
+                                   "kernel": "the TLX page's Version 4", "ratio": round(tflops / ref, 3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
 
