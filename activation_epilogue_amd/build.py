@@ -3,10 +3,8 @@
 Ten translation units compiled in parallel: the host/ABI unit (with the
 elementwise kernels), one unit of fused GEMM kernels per dtype, one of
 quantized-output kernels per 16-bit dtype, one of FP8-input kernels per
-16-bit output dtype and one of backward-epilogue kernels per 16-bit dtype;
-then the
-separate MFMA-rate probe library used by the benchmark.  Every
-device compile carries -Xclang -target-feature -Xclang -packed-fp32-ops so
+16-bit output dtype and one of backward-epilogue kernels per 16-bit dtype.
+Every device compile carries -Xclang -target-feature -Xclang -packed-fp32-ops so
 that no packed fp32 instructions are generated.
 """
 from __future__ import annotations
@@ -21,7 +19,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfused_linear.so")
-PROBE_LIB = os.path.join(PKG, "libfl_mfma_probe.so")  # measurement aid, not part of the product path
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
@@ -67,11 +64,6 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     tmp = LIB + f".tmp{os.getpid()}"
     subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], check=True)
     os.replace(tmp, LIB)
-    # the sustained-MFMA-rate probe used by bench.py --mfma-ceiling
-    tmp = PROBE_LIB + f".tmp{os.getpid()}"
-    subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "mfma_probe.hip"), "-o", tmp], check=True,
-                   capture_output=True)
-    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -358,12 +358,14 @@ struct Dma16 {
     //  * a copy that runs past the end of A (or B) is range-checked per
     //    dword, so the dword that holds the buffer's last element can read as
     //    zero.  The lane whose chunk holds A[M-1][K-1] (B[K-1][N-1]) reloads
-    //    that element with a 2-byte load and writes it into LDS.
+    //    that element with a 2-byte load and writes it into LDS.  The reload
+    //    goes through the tile's own descriptor (based at row m0 of A, at
+    //    column n0 of B, or at row n0 of the transposed B), so its offset is
+    //    below 256 rows of the operand, which the host keeps under 2^31
+    //    bytes, however large the whole operand is.
     __device__ __forceinline__ static void fix_k_tail(const GemmArgs &a, const Lane &L, int m0, int n0, int kt,
                                                       int wave, int lane, FL_LDS char *buf) {
         const int k0 = kt * BK, kleft = a.K - k0;
-        const i32x4_t rA = sgpr_rsrc(a.A, (size_t)a.M * a.K * 2);
-        const i32x4_t rB = sgpr_rsrc(a.B, (size_t)a.K * a.N * 2);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int kb = L.a_k[i & 1];
@@ -379,7 +381,8 @@ struct Dma16 {
                 const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
                 if (row == a.M - 1) {
                     const uint32_t e = (uint32_t)(valid - 1);
-                    const uint32_t x = load_u16_now(rA, (uint32_t)((size_t)a.M * a.K - 1) * 2);
+                    const uint32_t x =
+                        load_u16_now(L.rA, (uint32_t)(((size_t)(a.M - 1 - m0) * a.K + (a.K - 1)) * 2));
                     v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
                 }
                 *(FL_LDS u32x4_t *)p = v;
@@ -387,7 +390,6 @@ struct Dma16 {
         }
         if constexpr (BT) {
             // B^T rows are K-contiguous like A's: the same two fixes
-            const i32x4_t rBt = sgpr_rsrc(a.B, (size_t)a.N * a.K * 2);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int kb = L.b_k[i & 1];
@@ -403,7 +405,8 @@ struct Dma16 {
                     const int row = n0 + B_ROWS_PER_COPY_T * (wave * NB + i) + lane / CA;
                     if (row == a.N - 1) {
                         const uint32_t e = (uint32_t)(valid - 1);
-                        const uint32_t x = load_u16_now(rBt, (uint32_t)((size_t)a.N * a.K - 1) * 2);
+                        const uint32_t x =
+                            load_u16_now(L.rB, (uint32_t)(((size_t)(a.N - 1 - n0) * a.K + (a.K - 1)) * 2));
                         v[e >> 1] =
                             (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
                     }
@@ -420,7 +423,7 @@ struct Dma16 {
                     const int e = a.N - 1 - col;
                     FL_LDS uint16_t *q =
                         (FL_LDS uint16_t *)(buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16 + 2 * e);
-                    *q = (uint16_t)load_u16_now(rB, (uint32_t)((size_t)a.K * a.N - 1) * 2);
+                    *q = (uint16_t)load_u16_now(L.rB, (uint32_t)(((size_t)(a.K - 1) * a.N + (a.N - 1 - n0)) * 2));
                 }
             }
         }

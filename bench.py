@@ -46,11 +46,6 @@ def parse():
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
     p.add_argument("--tile-cfg", type=int, default=0, help="fl_options.tile_cfg (0 = automatic)")
-    p.add_argument("--operand-toggle", action="store_true",
-                   help="time the fused 4096^3 fp16 ReLU kernel on operands with fewer toggling bits instead "
-                        "(power diagnostic; one JSON line)")
-    p.add_argument("--mfma-ceiling", action="store_true",
-                   help="instead of the workload: the sustained MFMA rate of this GPU (register-only MFMA loop)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -124,6 +119,40 @@ def launch_times(fn, n, stream, scrub=None):
     return {"n": n, "median_ms": round(ts[n // 2], 4), "min_ms": round(ts[0], 4), "max_ms": round(ts[-1], 4)}
 
 
+def algorithmic_bytes(M, N, K, es, act, residual=False, qfmt=None, in8=False, bwd=False):
+    """Bytes one launch must move at least: each input read once and each
+    output written once.  Forward: A (M,K) and B (K,N) (one byte per element
+    for FP8 operands), bias (N,), Y (gate) and R (residual) (M,N), and out
+    (M,N) in the I/O dtype, or one byte per element for a quantized output.
+    Backward epilogue: G (M,K), W (N,K), the saved X (M,N) (+ Y) read, dX (+
+    dY) written, and the fp32 bias gradient (N,) zeroed and added to."""
+    glu = act == "glu"
+    if bwd:
+        return (M * K + K * N + 2 * M * N * (2 if glu else 1)) * es + 2 * N * 4
+    mn_arrays = (0 if qfmt else 1) + glu + bool(residual)  # out, Y, R in the I/O dtype
+    return ((M * K + K * N) * (1 if in8 else es) + (N + M * N * mn_arrays) * es + (M * N if qfmt else 0))
+
+
+def activation_traffic_bytes(M, N, es, act, kernels=3):
+    """HBM bytes of the (M,N) activation arrays around the product ("Triton:
+    Fused Matmul + Bias + ReLU (Epilogue Fusion)", "The HBM traffic";
+    "Optimizing GEMM + Activation on CDNA4 with TLX", "The GLU Block").
+    Fused: the output written once, plus Y read by the gate.  Unfused, three
+    kernels (this library's chain): the product stores X; the bias pass reads
+    and writes it; the activation pass reads it (and Y) and writes the
+    output.  Unfused, two kernels (the bias folded into the product, as a
+    library GEMM does): X written, X (and Y) read, the output written."""
+    glu = 1 if act == "glu" else 0
+    mn = M * N * es
+    if kernels == 3:
+        unfused = (5 + glu) * mn
+    elif kernels == 2:
+        unfused = (3 + glu) * mn
+    else:
+        raise ValueError("kernels is 2 or 3")
+    return {"fused": (1 + glu) * mn, "unfused": unfused}
+
+
 # The TLX page's own table ("Optimizing GEMM + Activation on CDNA4 with
 # TLX", the benchmark after Version 4): its best fused gate kernel on one
 # MI350X, fp16, M=1024, N=21568, TFLOP/s by K.  Another machine: context
@@ -177,82 +206,8 @@ def cpu_baseline(w, d, target_s):
                       f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
 
 
-def mfma_ceiling(args):
-    """Sustained v_mfma_f32_32x32x16_f16 rate with register operands (no
-    memory traffic in the loop), for constant and for random operands: the
-    matrix unit's power, and so the clock the chip holds, depends on how
-    many operand bits toggle.  One JSON line."""
-    import ctypes
-    import torch
-    from activation_epilogue_amd import build as hip_build
-    lib = ctypes.CDLL(hip_build.PROBE_LIB)
-    lib.fl_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    lib.fl_probe_mfma.restype = ctypes.c_int
-    grid, iters = 256, 4096
-    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    flops = grid * 4 * 16 * iters * 32768
-    res = {"probe": "v_mfma_f32_32x32x16_f16, 256 workgroups x 4 waves, operands in registers",
-           "peak_datasheet_tflops": PEAK_TFLOPS["f16"]}
-    for random in (0, 1):
-        def step():
-            rc = lib.fl_probe_mfma(out.data_ptr(), grid, iters, random, ctypes.c_void_p(stream.cuda_stream))
-            if rc != 0:
-                raise RuntimeError(f"fl_probe_mfma failed: {rc}")
-        ms, _ = time_loop(step, 30, 20, stream)
-        tf = flops / (ms * 1e-3) / 1e12
-        key = "random_operands" if random else "constant_operands"
-        res[key] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["f16"], 4),
-                    "us_per_launch": round(ms * 1e3, 1)}
-    print(json.dumps(res), flush=True)
-
-
-def operand_toggle(args):
-    """The 4096^3 fp16 ReLU fused kernel, unchanged, on operands whose bits
-    toggle less: the seeded N(0, 1/K) inputs, the same with only the top 3
-    of 10 mantissa bits kept, a constant (1/64), and zeros.  The work and
-    the memory traffic are the same in every case; only the power the
-    matrix units draw, and so the clock the chip holds, differs.  One JSON
-    line (event-timed average per launch)."""
-    import torch
-    import activation_epilogue_amd as fl
-    from activation_epilogue_amd import synth
-    w = synth.WORKLOADS["relu_f16_4096x4096x4096"]
-    d = synth.draw_workload(w)
-    A0 = torch.from_numpy(d["A"]).to("cuda")
-    B0 = torch.from_numpy(d["B"]).to("cuda")
-    bias = torch.from_numpy(d["bias"]).to("cuda")
-    out = torch.empty(w.M, w.N, device="cuda", dtype=torch.float16)
-    stream = torch.cuda.current_stream()
-
-    def trimmed(t):  # keep the sign, the exponent and the top 3 mantissa bits
-        return (t.view(torch.int16) & ~0x7F).view(torch.float16)
-    cases = {"random": (A0, B0), "random_3_mantissa_bits": (trimmed(A0), trimmed(B0)),
-             "constant_1_64": (torch.full_like(A0, 1 / 64), torch.full_like(B0, 1 / 64)),
-             "zeros": (torch.zeros_like(A0), torch.zeros_like(B0))}
-    res = {"kernel": "fused_linear_dma16_kernel (relu_f16_4096x4096x4096, automatic tile)",
-           "peak_datasheet_tflops": PEAK_TFLOPS["f16"]}
-    for name, (A, B) in cases.items():
-        def step():
-            fl.fused_linear(A, B, bias, act="relu", out=out)
-        t_end = time.perf_counter() + max(args.prewarm_s, 0.5)
-        while time.perf_counter() < t_end:
-            for _ in range(20):
-                step()
-            torch.cuda.synchronize()
-        ms, _ = time_loop(step, args.steps, args.warmup, stream)
-        tf = w.flops / (ms * 1e-3) / 1e12
-        res[name] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["f16"], 4),
-                     "us_per_launch": round(ms * 1e3, 2)}
-    print(json.dumps(res), flush=True)
-
-
 def main():
     args = parse()
-    if args.mfma_ceiling:
-        return mfma_ceiling(args)
-    if args.operand_toggle:
-        return operand_toggle(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X and has no multi-GPU "
               "path (the layer shards by output columns or rows with no communication; see DESIGN.md).",
@@ -346,12 +301,7 @@ def main():
     achieved = flops / (ms_event * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp8" if w.in8 else w.dtype]
     es = ES[w.dtype]
-    mn_arrays = (0 if w.qfmt else 1) + (w.act == "glu") + w.residual  # out, Y, R in the I/O dtype
-    alg_bytes = ((w.M * w.K + w.K * w.N) * (1 if w.in8 else es) + (w.N + w.M * w.N * mn_arrays) * es
-                 + (w.M * w.N if w.qfmt else 0))
-    if w.bwd:
-        # G, W, X (+Y) read, dX (+dY) written once, dbias (fp32) zeroed and added to
-        alg_bytes = (w.M * w.K + w.K * w.N + 2 * w.M * w.N * (2 if w.act == "glu" else 1)) * es + 2 * w.N * 4
+    alg_bytes = algorithmic_bytes(w.M, w.N, w.K, es, w.act, residual=w.residual, qfmt=w.qfmt, in8=w.in8, bwd=w.bwd)
 
     result = {
         "metric": METRIC,
@@ -447,8 +397,8 @@ def main():
                           "frac_hbm": round(bias_bytes / ms_bias / 1e6 / PEAK_HBM_GBS, 3)},
             "act_pass": {"ms": round(ms_act, 4), "GB/s": round(act_bytes / ms_act / 1e6, 1),
                          "frac_hbm": round(act_bytes / ms_act / 1e6 / PEAK_HBM_GBS, 3)},
-            "activation_traffic_bytes": {"fused": (2 if w.act == "glu" else 1) * mn * es,
-                                         "unfused": (5 + (1 if w.act == "glu" else 0)) * mn * es},
+            "activation_traffic_bytes": activation_traffic_bytes(w.M, w.N, es, w.act),
+            "activation_traffic_bytes_two_kernels": activation_traffic_bytes(w.M, w.N, es, w.act, kernels=2),
         }
 
     if (w.act == "glu" and not w.bwd and not w.in8 and not w.residual and w.dtype == "f16"

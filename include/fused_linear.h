@@ -202,7 +202,7 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
 
 /*
  * out = act(ab_scale * (A8 @ B8) + bias): the fused linear layer with FP8
- * operands ("Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next":
+ * operands ("Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work":
  * the projection in FP8, which CDNA4's matrix cores run at twice the 16-bit
  * rate and which halves the operand traffic).  A8 (M,K) and B8 (K,N) are OCP
  * FP8 E4M3 codes, row-major; the products are summed in fp32 by

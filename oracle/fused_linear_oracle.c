@@ -34,7 +34,7 @@
  *     epilogue value times a scale, limited to the target range and
  *     converted to int8 or FP8 codes as it is stored (see
  *     orc_fused_linear_quant).
- *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next" (FP8
+ *   - "Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work" (FP8
  *     precision): the projection itself in FP8, i.e. A and B as OCP E4M3
  *     codes with a per-tensor scale, fp32 accumulation, and the same
  *     epilogue in the 16-bit output dtype (see orc_fused_linear_fp8).

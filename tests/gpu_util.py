@@ -1,6 +1,6 @@
-"""Helpers shared by the GPU tests: host<->device transfer of raw storage,
-sentinel-filled outputs with a guard band, and row sampling.  No method
-arithmetic lives here."""
+"""Helpers shared by the GPU tests: host<->device transfer of raw storage and
+sentinel-filled outputs with a guard band.  No method arithmetic lives
+here."""
 import sys
 
 import numpy as np
@@ -40,13 +40,3 @@ def sentinel_out(M, N, dtype):
 
 def guard_intact(buf, M, N):
     return bool(torch.isnan(buf[M * N:]).all().item())
-
-
-def sample_rows(M, tile=256, extra=16, seed=0):
-    """Rows at every tile edge plus a few random ones, sorted and unique."""
-    rows = {0, M - 1}
-    for m0 in range(0, M, tile):
-        rows.update({m0, min(m0 + tile - 1, M - 1), min(m0 + 31, M - 1), min(m0 + 32, M - 1)})
-    rng = np.random.default_rng(seed)
-    rows.update(int(r) for r in rng.integers(0, M, extra))
-    return np.array(sorted(r for r in rows if 0 <= r < M), dtype=np.int64)

@@ -96,6 +96,66 @@ def test_k1_k3_agree_with_unfused_chain(dtype, K):
     assert oracle.compare(chain, fused, dtype)["ok"]
 
 
+def _round_to(x64, dtype):
+    """RNE rounding to the dtype by routines other than the oracle's own:
+    numpy's float64 -> float32 / float16 conversions, and torch's float32 ->
+    bfloat16 cast (used only where the float32 step is exact)."""
+    if dtype == "f32":
+        return x64.astype(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return x64.astype(np.float16).astype(np.float64)
+    f32 = x64.astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), x64), "bf16 reference needs float32-exact values"
+    return torch.from_numpy(f32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("act", ["relu", "glu"])
+def test_unfused_chain_rounds_after_each_stage(dtype, act):
+    """The unfused chain stores X = A@B, then X + bias, then the activation,
+    each in the dtype ("Epilogue concept", "Things that break"; "I3. Fuse a
+    GEMM epilogue and change tile scheduling", "Why the baseline uses
+    FP32"): round(act(round(round(A@B) + bias))).  With integer operands the
+    product is exact in int64; the bias has a fraction and the products are
+    large enough that the intermediate roundings move values, so the chain
+    without the rounding of the product, or the fused once-rounded result,
+    differs.  The rounding after the bias pass is visible with the gate only:
+    ReLU commutes with rounding (max(0, round(v)) = round(max(0, v))), so with
+    ReLU that rounding and the final one coincide; the gate's v + v*Y with
+    Y = 0.5 does not."""
+    rng = np.random.default_rng(21)
+    M, N, K = 48, 40, 8
+    amax = {"f32": 8000, "f16": 60, "bf16": 60}[dtype]
+    A = rng.integers(-amax, amax + 1, (M, K)).astype(np.float64)
+    B = rng.integers(-amax, amax + 1, (K, N)).astype(np.float64)
+    if dtype == "bf16":  # 8 significant bits
+        bias = rng.integers(-127, 128, N) * rng.choice([1.0, 0.25], N)
+    else:
+        bias = rng.integers(-500, 501, N) + rng.choice([0.0, 0.25, 0.5, 0.75], N)
+    Y = rng.choice([-1.0, 0.0, 0.5, 1.0], (M, N)) if act == "glu" else None
+    for v in (A, B, bias, Y):
+        if v is not None:
+            assert np.array_equal(_round_to(v, dtype), v), "inputs exact in the dtype"
+    raw = {k: None if v is None else synth.to_storage(v, dtype) for k, v in dict(A=A, B=B, bias=bias, Y=Y).items()}
+    X = (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64)
+
+    def act_fn(v):
+        return np.maximum(v, 0.0) if act == "relu" else v + v * Y
+
+    want = _round_to(act_fn(_round_to(_round_to(X, dtype) + bias[None, :], dtype)), dtype)
+    got = oracle.decode(oracle.unfused_chain(raw["A"], raw["B"], raw["bias"], raw["Y"], act=act, dtype=dtype), dtype)
+    assert np.array_equal(got, want)
+    no_first = _round_to(act_fn(_round_to(X + bias[None, :], dtype)), dtype)
+    no_second = _round_to(act_fn(_round_to(X, dtype) + bias[None, :]), dtype)
+    once = _round_to(act_fn(X + bias[None, :]), dtype)
+    for wrong in (no_first, once) + ((no_second,) if act == "glu" else ()):
+        assert not np.array_equal(wrong, want)
+    if act == "relu":
+        assert np.array_equal(no_second, want)
+    fused = oracle.decode(oracle.fused_linear(raw["A"], raw["B"], raw["bias"], raw["Y"], act=act, dtype=dtype), dtype)
+    assert np.array_equal(fused, once)
+
+
 # ------------------------------------------------ exact integers, brute force
 
 def _int_reference(A, B, bias, Y, act):
@@ -478,7 +538,7 @@ def test_compare_quant_flags_off_by_one_codes_away_from_boundaries():
 
 
 # ---------------------------------------------------------------- FP8 inputs
-# "Optimizing GEMM + Activation on CDNA4 with TLX", "What's Next": the
+# "Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work": the
 # projection in FP8 (A and B as OCP E4M3 codes, per-tensor scale, fp32
 # accumulation, 16-bit epilogue and output).
 
