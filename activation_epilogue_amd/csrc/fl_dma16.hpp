@@ -105,16 +105,21 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
 // stay in DT).  BWD: the backward epilogue (see epilogue_lds), with B given
 // as (N, K) row-major (the weight read as its transpose): its tile is
 // staged and read exactly like A's, and a lane's 16-byte read of a row is
-// already the MFMA's B fragment (8 consecutive k of one column).
+// already the MFMA's B fragment (8 consecutive k of one column).  M16:
+// the product runs as 16x16 output blocks 32 deep (v_mfma_f32_16x16x32_
+// {f16,bf16}) instead of 32x32 blocks 16 deep; same flops per operand read
+// from LDS for the wave's tile, but on random data the matrix cores hold a
+// higher clock under the 16x16 form (measured with operands in registers:
+// 1838 against 1645 TFLOP/s, 2.29 against 2.01 GHz, 8 waves per CU).
 template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false,
-          int QF = -1, int IN = DT, bool BWD = false>
+          int QF = -1, int IN = DT, bool BWD = false, bool M16 = false>
 struct Dma16 {
     using base = FusedTile<DT, ACT, true>;  // shares the epilogue
     static constexpr bool F8 = IN == kInFp8;
     static constexpr bool BT = BWD;  // B is (N, K) row-major, K contiguous
     static constexpr int IES = F8 ? 1 : 2;           // bytes per A/B element
     static constexpr int EPCH = 16 / IES;            // A/B elements per 16-byte chunk
-    static constexpr int KPM = F8 ? 64 : 16;         // K per MFMA (32x32x64 fp8, 32x32x16 fp16/bf16)
+    static constexpr int KPM = F8 ? 64 : M16 ? 32 : 16;  // K per MFMA (32x32x64 fp8, 16x16x32 / 32x32x16 16-bit)
     static constexpr int BM = 256, BN = BN_, BK = BK_;
     static_assert(BK * IES == 64 || BK * IES == 128, "stage depth: 64- or 128-byte A rows");
     static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
@@ -123,14 +128,19 @@ struct Dma16 {
     static_assert(BN != 192 || !F8, "the 192-wide swizzle is for 16-bit B");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
-    static constexpr int NI = WN / 32;               // 32-wide MFMA blocks per wave along N
+    static_assert(!M16 || (!F8 && !BWD), "16x16x32 blocks: 16-bit forward kernels");
+    static constexpr int RBH = M16 ? 16 : 32;        // output rows of an accumulator block
+    static constexpr int NRB = 128 / RBH;            // accumulator blocks per wave along M
+    static constexpr int NI = WN / RBH;              // MFMA blocks per wave along N (square blocks)
+    static constexpr int AV = M16 ? 4 : 16;          // accumulator floats per lane and block
+    typedef float acc_t __attribute__((ext_vector_type(AV)));
     static constexpr int KK = BK / KPM;              // MFMA blocks per stage
     static constexpr int CA = BK * IES / 16;         // 16-byte chunks per A row
     static constexpr int CB = BN * IES / 16;         // 16-byte chunks per B row
     static constexpr int A_BYTES = BM * BK * IES;    // rows of BK*IES bytes
     static constexpr int B_BYTES = BK * BN * IES;    // rows of BN*IES bytes
     static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_RING = OCC == 2 ? 73728 : BN == 256 ? 131072 : BN == 128 ? 147456 : 163840;
+    static constexpr int LDS_RING = OCC == 2 ? 73728 : M16 ? 163840 : BN == 256 ? 131072 : BN == 128 ? 147456 : 163840;
     static constexpr int NBUF = LDS_RING / BUF_BYTES;  // LDS ring
     static constexpr int A_ROWS_PER_COPY = 64 / CA;  // A rows per 1 KB copy
     static constexpr int NA = BM / (A_ROWS_PER_COPY * WAVES);  // A copies per wave per stage
@@ -139,18 +149,21 @@ struct Dma16 {
     // divisor of 1 KB).  The lane -> (row offset, chunk) pattern and the
     // swizzle repeat every PB copies, which span B_ROWS_PER_PERIOD rows (a
     // multiple of the swizzle's period in rows, FBP).
+    // With 16x16 blocks the swizzle also depends on bit 3 of the row (period
+    // 16 rows), which the copies of one wave need not repeat: each of them
+    // keeps its own offset (PB = NB).
     static constexpr int FBP = F8 ? 8 : 4;
     static constexpr int pb_of(int p) { return ((64 * p) % CB == 0 && ((64 * p) / CB) % FBP == 0) ? p : pb_of(p + 1); }
-    static constexpr int PB = pb_of(2);  // 2 for every power-of-two width
-    static constexpr int B_ROWS_PER_PERIOD = 64 * PB / CB;
     static constexpr int NB = BK * CB / (64 * WAVES);  // B copies per wave per stage
+    static constexpr int PB = M16 ? NB : pb_of(2);     // 2 for every power-of-two width
+    static constexpr int B_ROWS_PER_PERIOD = 64 * PB / CB;
     static constexpr int B_ROWS_PER_COPY_T = 64 / CA;  // K-contiguous B: its rows per 1 KB copy
     static constexpr int DMA_PER_WAVE = NA + NB;
-    static constexpr int SLOTS = 4 * NI;             // MFMAs per block
+    static constexpr int SLOTS = NRB * NI;           // MFMAs per block
     static constexpr int RPA = F8 ? 2 : 1;           // LDS reads per A operand (16 bytes each)
     static constexpr int RPB = F8 ? 4 : BT ? 1 : 2;  // reads per B operand (transposed 8-byte, or one 16-byte)
     static constexpr int BPARTS = F8 ? 4 : 2;        // 8-byte parts of a B operand
-    static constexpr int READS = 4 * RPA + NI * RPB; // operand reads per block
+    static constexpr int READS = NRB * RPA + NI * RPB;  // operand reads per block
     static_assert(NA * WAVES * A_ROWS_PER_COPY == BM, "A copies cover the tile");
     static_assert(NB * WAVES * 64 == BK * CB, "B copies cover the stage");
     static_assert(NB % PB == 0, "each wave's first B copy starts a swizzle period");
@@ -160,9 +173,16 @@ struct Dma16 {
     // index (Lane below keeps two offsets and a stride), so each wave's
     // first copy must have an even index: an even number of copies per wave.
     static_assert(NA % 2 == 0, "A copies per wave");
-    static_assert(SPREAD >= 1 && SPREAD <= KK, "copies spread over the blocks of one stage at most");
+    // The copies of a stage are spread over SPR blocks (at most the blocks of
+    // one stage).  With 16x16 blocks a stage has only two blocks (64 deep) or
+    // one (32 deep), and all its copies go out in the block after the
+    // barrier that frees their buffer: the copies of the second half would
+    // otherwise have half a stage less to land (measured 1219 -> 1279
+    // TFLOP/s at 4096^3 together with the read placement below).
+    static constexpr int SPR = M16 ? 1 : SPREAD < KK ? SPREAD : KK;
+    static_assert(SPREAD >= 1, "copies spread over one block at least");
     // Copies [part_lo(p), part_lo(p+1)) of a stage form part p.
-    static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPREAD; }
+    static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPR; }
     static_assert(NBUF >= 2, "double buffering at least");
     static_assert(OCC == 1 || (OCC == 2 && WAVES == 4), "two resident workgroups of 4 waves");
 
@@ -175,6 +195,19 @@ struct Dma16 {
         else
             return ((r >> 1) ^ ((r & 1) << 2)) & 7;
     }
+    // 16x16 blocks with 32-deep stages (64-byte A rows): each 16-row block
+    // of the A stage is stored chunk-major, chunk c of row r at c*256 + r*16,
+    // so that the operand read of a block (lane l: row l%16, chunk l/16) is
+    // one linear 1 KB read, which the LDS serves without conflicts; 64-byte
+    // rows read row-major cost twice the cycles whatever the chunk XOR
+    // (measured).  A copy of 1 KB fills one such block: lane l fetches row
+    // l%16, chunk l/16.
+    static constexpr bool A_CM = M16 && CA == 4;
+    __device__ __forceinline__ static int a_row_in_copy(int lane) { return A_CM ? (lane & 15) : lane / CA; }
+    __device__ __forceinline__ static int a_chunk_in_copy(int lane, int r) {
+        return A_CM ? (lane >> 4) : (lane % CA) ^ fa(r);
+    }
+
     // B swizzle: chunk c of k-row r sits at c ^ fb(r).  16-bit B: fb in
     // {0,6,12,10} by r % 4 (rows are 256 or 512 bytes, a multiple of the bank
     // width); conflict-free for the transposed 8-byte reads (4 rows x 2 or 4
@@ -187,13 +220,19 @@ struct Dma16 {
     // four by two chunks, which again leaves the 4 rows x 2 chunks of a
     // transposed read in 8 different bank groups.  An XOR below 8 keeps
     // every chunk inside its row of 24.
+    //
+    // 16x16 blocks: the four 16-lane groups of a transposed read take k-rows
+    // 8 apart (rows g*8 + 0..3 of the same 16 columns), and two of them are
+    // served in the same cycle; the XOR term from bit 3 of the row moves
+    // rows 8..15 of every 16 by 2 chunks (4 for 192-wide rows), into the
+    // bank groups rows 0..7 leave free.
     __device__ __forceinline__ static int fb(int r) {
         if constexpr (F8)
             return r & 7;
         else if constexpr (BN == 192)
-            return r & 2;
+            return (r & 2) ^ (M16 ? ((r >> 1) & 4) : 0);
         else
-            return (0xAC60 >> (4 * (r & 3))) & 0xF;
+            return ((0xAC60 >> (4 * (r & 3))) & 0xF) ^ (M16 ? ((r >> 2) & 2) : 0);
     }
 
     // Per-lane copy offsets and operand-read addresses, fixed for a tile.
@@ -230,8 +269,8 @@ struct Dma16 {
 #pragma unroll
         for (int i = 0; i < (PB > 2 ? PB : 2); ++i) {
             if (i < 2) {
-                const int ra = A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
-                const int ca = (lane % CA) ^ fa(ra);
+                const int ra = A_ROWS_PER_COPY * (wave * NA + i) + a_row_in_copy(lane);
+                const int ca = a_chunk_in_copy(lane, ra);
                 L.a_off[i] = (uint32_t)(ra * a.K + ca * EPCH) * IES;
                 L.a_k[i] = ca * EPCH;
             }
@@ -264,6 +303,24 @@ struct Dma16 {
             for (int kk = 0; kk < KK; ++kk) {
                 L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
                 L.b_frag[kk] = A_BYTES + rn * (BK * 2) + (((kk * 2 + lg) ^ fa(rn)) * 16);
+            }
+        } else if constexpr (M16) {
+            // A: lane (row r16, group g16) takes k = g16*8 .. g16*8+7 of each
+            // 32-deep block: chunk kk*4 + g16; fa depends on the row modulo
+            // 16 only, so blocks mi > 0 add 16 rows to this address.
+            const int r16 = wm * 128 + i16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                L.a_frag[kk] = A_CM ? wm * 128 * (BK * 2) + g16 * 256 + i16 * 16
+                                    : r16 * (BK * 2) + (((kk * 4 + g16) ^ fa(r16)) * 16);
+            // B: 16-lane group g16 covers k-rows g16*8 .. g16*8+7 of the block
+            // in two transposed reads (h adds 4 rows); lane i16 points at k-row
+            // i16/4 of the four and at columns 4*(i16%4) .. +3 of the 16.
+            const int rk = g16 * 8 + (i16 >> 2);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = wn * WN + ni * 16 + 4 * (i16 & 3);
+                L.b_frag[ni] = A_BYTES + rk * (BN * 2) + (((n >> 3) ^ fb(rk)) * 16) + ((n >> 2) & 1) * 8;
             }
         } else if constexpr (!F8) {
 #pragma unroll
@@ -378,7 +435,7 @@ struct Dma16 {
                     const uint32_t keep = (2 * d + 1 < valid) ? 0xffffffffu : (2 * d < valid) ? 0x0000ffffu : 0u;
                     v[d] &= keep;
                 }
-                const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + lane / CA;
+                const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + a_row_in_copy(lane);
                 if (row == a.M - 1) {
                     const uint32_t e = (uint32_t)(valid - 1);
                     const uint32_t x =
@@ -430,7 +487,7 @@ struct Dma16 {
     }
 
     struct Frags {
-        u32x4_t a[4][RPA];     // A operand per mi (16 bytes per read)
+        u32x4_t a[NRB][RPA];   // A operand per mi (16 bytes per read)
         i32x2_t b[NI][BPARTS]; // B operand per ni (8 bytes per transposed read, or halves of one 16-byte read)
     };
 
@@ -449,7 +506,7 @@ struct Dma16 {
                 f.b[ni][1] = i32x2_t{(int)v[2], (int)v[3]};
             } else if constexpr (!F8)
                 f.b[ni][h] = __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                             (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * 16 * (BN * 2) +
+                                                             (FL_LDS s16x4_t *)(buf + L.b_frag[ni] + kk * KPM * (BN * 2) +
                                                                                 h * 4 * (BN * 2))));
             else
                 f.b[ni][h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -457,7 +514,7 @@ struct Dma16 {
         } else {
             constexpr int Q = P - RPA - NI * RPB;
             constexpr int mi = 1 + Q / RPA, h = Q % RPA;
-            f.a[mi][h] = *(const FL_LDS u32x4_t *)(buf + ((L.a_frag[kk] + mi * 32 * BK * IES) ^ (h * 16)));
+            f.a[mi][h] = *(const FL_LDS u32x4_t *)(buf + ((L.a_frag[kk] + mi * RBH * BK * IES) ^ (h * 16)));
         }
     }
 
@@ -476,9 +533,13 @@ struct Dma16 {
         }
     }
 
+    // MFMA I of a block.  16x16 blocks run the rows of blocks in snake
+    // order (odd rows right to left), so that consecutive MFMAs always share
+    // one operand: fewer operand bits toggle, which lowers the matrix cores'
+    // power and lets the chip hold a higher clock (+1-2% measured).
     template <int I>
-    __device__ __forceinline__ static void mma_one(const Frags &f, f32x16_t (&acc)[4][NI]) {
-        constexpr int mi = I / NI, ni = I % NI;
+    __device__ __forceinline__ static void mma_one(const Frags &f, acc_t (&acc)[NRB][NI]) {
+        constexpr int mi = I / NI, ni = (M16 && (mi & 1)) ? NI - 1 - I % NI : I % NI;
         if constexpr (F8) {
             const i32x4_t b01 = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3);
             const i32x4_t b23 = __builtin_shufflevector(f.b[ni][2], f.b[ni][3], 0, 1, 2, 3);
@@ -491,14 +552,24 @@ struct Dma16 {
         }
         const s16x8_t bv = __builtin_bit_cast(
             s16x8_t, __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3));
-        if constexpr (DT == FL_F16)
+        if constexpr (M16) {
+            if constexpr (DT == FL_F16)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, bv),
+                                                                     __builtin_bit_cast(f16x8_t, f.a[mi][0]),
+                                                                     acc[mi][ni], 0, 0, 0);
+            else
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bv),
+                                                                      __builtin_bit_cast(bf16x8_t, f.a[mi][0]),
+                                                                      acc[mi][ni], 0, 0, 0);
+        } else if constexpr (DT == FL_F16) {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bv),
                                                                  __builtin_bit_cast(f16x8_t, f.a[mi][0]), acc[mi][ni],
                                                                  0, 0, 0);
-        else
+        } else {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv),
                                                                   __builtin_bit_cast(bf16x8_t, f.a[mi][0]),
                                                                   acc[mi][ni], 0, 0, 0);
+        }
     }
 
     // Copies [C0, C1) of a look-ahead stage.
@@ -513,15 +584,19 @@ struct Dma16 {
     // One block: the SLOTS MFMAs on `use`, with the READS operand reads of
     // block kk_next of buffer `src` (into `fill`) in the last READS slots
     // and copies [C0, C1) of the look-ahead stage `s` spread over all slots.
-    // Without copies the reads follow the first MFMAs.
+    // Without copies the reads follow the first MFMAs.  16x16 blocks spread
+    // the reads evenly over the block instead: a wave's next operands are
+    // then all requested well before the block ends.
     template <int I, int C0, int C1>
     __device__ __forceinline__ static void block(const Lane &L, const FL_LDS char *src, int kk_next, const Stage &s,
-                                                 const Frags &use, Frags &fill, f32x16_t (&acc)[4][NI]) {
+                                                 const Frags &use, Frags &fill, acc_t (&acc)[NRB][NI]) {
         if constexpr (I < SLOTS) {
             constexpr int NC = C1 - C0;
             mma_one<I>(use, acc);
             copy_range<C0 + (I * NC + SLOTS - 1) / SLOTS, C0 + ((I + 1) * NC + SLOTS - 1) / SLOTS>(L, s);
-            if constexpr (READS <= SLOTS) {
+            if constexpr (M16) {
+                read_range<I * READS / SLOTS, (I + 1) * READS / SLOTS>(L, src, kk_next, fill);
+            } else if constexpr (READS <= SLOTS) {
                 constexpr int R = NC > 0 ? I - (SLOTS - READS) : I;
                 if constexpr (R >= 0 && R < READS) read_piece<R>(L, src, kk_next, fill);
             } else {
@@ -554,16 +629,18 @@ struct Dma16 {
     // every wave and buffer `buf` has been read by all of them, so the last
     // block starts refilling it with stage kt+NBUF while reading stage
     // kt+1's first operands.
-    template <int J = 0>
+    // P: the operand buffer stage kt starts from (f[P]); with an odd number
+    // of blocks per stage it alternates from one stage to the next.
+    template <int J = 0, int P = 0>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                  uint32_t lds_addr, int m0, int n0, int kt, int nk, int buf,
-                                                 int wave, Stage &pend, Frags (&f)[2], f32x16_t (&acc)[4][NI]) {
+                                                 int wave, Stage &pend, Frags (&f)[2], acc_t (&acc)[NRB][NI]) {
         const FL_LDS char *cur = lds + buf * BUF_BYTES;
         if constexpr (J < KK - 1) {
-            constexpr int p = J + 1 < SPREAD ? J + 1 : SPREAD;  // part SPREAD is empty
-            block<0, part_lo(p), part_lo(p < SPREAD ? p + 1 : p)>(L, cur, J + 1, pend, f[J & 1], f[(J + 1) & 1],
-                                                                    acc);
-            stage<J + 1>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+            constexpr int p = J + 1 < SPR ? J + 1 : SPR;  // part SPR is empty
+            block<0, part_lo(p), part_lo(p < SPR ? p + 1 : p)>(L, cur, J + 1, pend, f[(J + P) & 1],
+                                                                f[(J + P + 1) & 1], acc);
+            stage<J + 1, P>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
         } else {
             const int nbuf = buf + 1 == NBUF ? 0 : buf + 1;
             const FL_LDS char *nxt = lds + nbuf * BUF_BYTES;
@@ -573,7 +650,7 @@ struct Dma16 {
                     fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
             __syncthreads();
             pend = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
-            block<0, 0, part_lo(1)>(L, nxt, 0, pend, f[J & 1], f[(J + 1) & 1], acc);
+            block<0, 0, part_lo(1)>(L, nxt, 0, pend, f[(J + P) & 1], f[(J + P + 1) & 1], acc);
         }
     }
 
@@ -604,7 +681,24 @@ struct Dma16 {
     static constexpr int EPI_WAVE = 128 * EPI_ROW;  // one wave's area (own-area layout)
     static constexpr int EPI_BYTES = SHARED_EPI ? BM * EPI_ROW : WAVES * EPI_WAVE;
     static_assert(EPI_BYTES <= (OCC == 2 ? 73728 : 163840), "epilogue staging fits in the workgroup's LDS");
-    static constexpr int NG = 4 * NI;  // 4-column groups per lane and row block
+    // A lane's accumulators form groups of 4 consecutive output columns of
+    // one row: per accumulator row block (RBH rows), NG groups.  32x32
+    // blocks: lane l holds row l%32 and, in block ni, columns ni*32 + q*8 +
+    // (l/32)*4 + e (q, e = 0..3; group g = ni*4 + q).  16x16 blocks: lane l
+    // holds row l%16 and columns ni*16 + (l/16)*4 + e (group g = ni).
+    static constexpr int NG = M16 ? NI : 4 * NI;
+    __device__ __forceinline__ static int gcol(int g, int lane) {  // column of group g within the wave's tile
+        if constexpr (M16)
+            return g * 16 + (lane >> 4) * 4;
+        else
+            return (g >> 2) * 32 + (g & 3) * 8 + (lane >> 5) * 4;
+    }
+    __device__ __forceinline__ static float accv(const acc_t (&acc)[NRB][NI], int mi, int g, int e) {
+        if constexpr (M16)
+            return acc[mi][g][e];
+        else
+            return acc[mi][g >> 2][(g & 3) * 4 + e];
+    }
     // Backward: the lanes' fp32 column sums of dX meet in the wave's own LDS
     // area as 32 rows (one per lane row) of WN floats, padded like EPI_ROW.
     static constexpr int DB_ROW = WN * 4 + 16;
@@ -672,7 +766,7 @@ struct Dma16 {
     }
 
     __device__ __forceinline__ static void epilogue_lds(const GemmArgs &a, int m0, int n0, int wave, int wm, int wn,
-                                                        int lane, const f32x16_t (&acc)[4][NI], FL_LDS char *lds) {
+                                                        int lane, const acc_t (&acc)[NRB][NI], FL_LDS char *lds) {
         using io = Io<DT>;
         using quad_t = u32x2_t;
         const size_t o_org = (size_t)m0 * a.N + n0;
@@ -696,11 +790,11 @@ struct Dma16 {
             make_rsrc(a.bias ? static_cast<const char *>(a.bias) + (size_t)n0 * 2 : nullptr,
                       a.bias ? (size_t)(a.N - n0) * 2 : 0);
         FL_LDS char *wbuf = SHARED_EPI ? lds + (wm * 128) * EPI_ROW + wn * WN * OES : lds + wave * EPI_WAVE;
-        const int lrow = lane & 31, lg = lane >> 5;
+        const int lrow = lane & (RBH - 1);
         int col[NG], valid[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            col[g] = wn * WN + (g >> 2) * 32 + (g & 3) * 8 + lg * 4;  // g = ni*4 + q
+            col[g] = wn * WN + gcol(g, lane);
             valid[g] = a.N - n0 - col[g];
         }
         float dsum[BWD ? NG : 1][4];  // backward: this lane's column sums of dX
@@ -717,7 +811,7 @@ struct Dma16 {
             if (a.bias) bq[g] = base::load4(rBias, valid[g] > 0 ? (uint32_t)col[g] * 2 : kOob, valid[g]);
         }
         auto yoff = [&](int mi, int g) -> uint32_t {
-            const int row = wm * 128 + mi * 32 + lrow;
+            const int row = wm * 128 + mi * RBH + lrow;
             return (m0 + row < a.M && valid[g] > 0) ? (uint32_t)(row * a.N + col[g]) * 2 : kOob;
         };
         // Y (gate) of row block mi+1 is loaded before row block mi is
@@ -756,20 +850,19 @@ struct Dma16 {
             }
         }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (y_reg && mi + 1 < 4) {
+        for (int mi = 0; mi < NRB; ++mi) {
+            if (y_reg && mi + 1 < NRB) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g) yq[(mi + 1) & 1][g] = base::load4(rY, yoff(mi + 1, g), valid[g]);
             }
-            if (r_reg && mi + RA < 4) {
+            if (r_reg && mi + RA < NRB) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     rq[(mi + RA) % (RA + 1)][g] = base::load4(rR, yoff(mi + RA, g), valid[g]);
             }
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const int ni = g >> 2, q = g & 3;
-                const int r = mi * 32 + lrow, c = ni * 32 + q * 8 + lg * 4;  // within the wave's tile
+                const int r = mi * RBH + lrow, c = gcol(g, lane);  // within the wave's tile
                 if constexpr (SIDE != 0) {
                     if (slds) {
                         const quad_t s = *(const FL_LDS quad_t *)(wbuf + r * EPI_ROW + c * 2);
@@ -789,7 +882,7 @@ struct Dma16 {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
-                        const float d = acc[mi][ni][q * 4 + e];
+                        const float d = accv(acc, mi, g, e);
                         const float xs = base::elem_f32(rq[mi % (RA + 1)][g], e);
                         float dx = d * activate_grad<ACT>(xs, y);
                         asm("" : "+v"(dx));
@@ -821,9 +914,9 @@ struct Dma16 {
                     const float y = (ACT == FL_ACT_GLU) ? base::elem_f32(yq[mi & 1][g], e) : 0.0f;
                     float x;
                     if constexpr (F8)
-                        x = __builtin_fmaf(acc[mi][ni][q * 4 + e], a.ab_scale, base::elem_f32(bq[g], e));
+                        x = __builtin_fmaf(accv(acc, mi, g, e), a.ab_scale, base::elem_f32(bq[g], e));
                     else
-                        x = acc[mi][ni][q * 4 + e] + base::elem_f32(bq[g], e);
+                        x = accv(acc, mi, g, e) + base::elem_f32(bq[g], e);
                     if constexpr (has_r) x += base::elem_f32(rq[mi % (RA + 1)][g], e);
                     v[e] = activate<ACT>(x, y);
                 }
@@ -958,7 +1051,7 @@ struct Dma16 {
             // there).
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const int c = (g >> 2) * 32 + (g & 3) * 8 + lg * 4;
+                const int c = gcol(g, lane);
                 const f32x4_t t = {dsum[g][0], dsum[g][1], dsum[g][2], dsum[g][3]};
                 *(FL_LDS f32x4_t *)(wbuf + lrow * DB_ROW + c * 4) = t;
             }
@@ -966,7 +1059,7 @@ struct Dma16 {
             asm volatile("" ::: "memory");
             float sum = 0.0f;
 #pragma unroll 8
-            for (int r = 0; r < 32; ++r) sum += *(const FL_LDS float *)(wbuf + r * DB_ROW + lane * 4);
+            for (int r = 0; r < RBH; ++r) sum += *(const FL_LDS float *)(wbuf + r * DB_ROW + lane * 4);
             const int col = n0 + wn * WN + lane;
             if (col < a.N) unsafeAtomicAdd(a.dbias + col, sum);
         }
@@ -982,13 +1075,13 @@ struct Dma16 {
         const FL_LDS char *lds = (const FL_LDS char *)smem;
         const uint32_t lds_addr = (uint32_t)(uintptr_t)(FL_LDS void *)smem;
 
-        f32x16_t acc[4][NI];
+        acc_t acc[NRB][NI];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < NRB; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
+                for (int e = 0; e < AV; ++e) acc[mi][ni][e] = 0.0f;
 
         const int nk = (a.K + BK - 1) / BK;
         if (nk > 0) {
@@ -1006,12 +1099,25 @@ struct Dma16 {
             __syncthreads();
             Frags f[2];
             read_all(L, lds, 0, f[0]);
-            static_assert(KK % 2 == 0, "operand double buffer f[] must line up across stages");
             int buf = 0;
+            if constexpr (KK % 2 == 0) {
 #pragma unroll 1
-            for (int kt = 0; kt < nk; ++kt) {
-                stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
-                buf = buf + 1 == NBUF ? 0 : buf + 1;
+                for (int kt = 0; kt < nk; ++kt) {
+                    stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                }
+            } else {
+                // an odd number of blocks per stage: two stages per pass, the
+                // second starting from the other operand buffer
+#pragma unroll 1
+                for (int kt = 0; kt < nk; kt += 2) {
+                    stage<0, 0>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    if (kt + 1 < nk) {
+                        stage<0, 1>(a, L, lds, lds_addr, m0, n0, kt + 1, nk, buf, wave, pend, f, acc);
+                        buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    }
+                }
             }
             // The look-ahead copies (past the end of K) must land before this
             // workgroup's LDS is reused.
@@ -1032,9 +1138,10 @@ struct Dma16 {
 // 4096^3 fp16, 8192x14336x4096 bf16 and 1024x21568x4096 fp16 shapes.
 constexpr int kCopySpread = 2;
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF, int IN = DT>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int SPREAD, int OCC, bool RES, int QF, int IN = DT,
+          bool M16 = false>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF, IN>;
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, SPREAD, OCC, RES, QF, IN, false, M16>;
     __shared__ __attribute__((aligned(1024))) char smem[T::SMEM_BYTES];
     // One strided loop for both launch modes (one program per tile runs one
     // iteration), so the tile body is inlined once.

@@ -17,27 +17,27 @@ void launch(const GemmArgs &a, int grid, hipStream_t s) {
 
 }  // namespace
 
-template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, bool RES>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, bool RES, bool M16>
 void launch_dma(const GemmArgs &a, int grid, hipStream_t s) {
     if constexpr (DT != FL_F32)
-        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES, -1>), dim3(grid),
-                           dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
+        hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES, -1, DT, M16>),
+                           dim3(grid), dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
 }
 
-template <int DT, int BK, int BN, int WAVES_N, int OCC, bool RES>
+template <int DT, int BK, int BN, int WAVES_N, int OCC, bool RES, bool M16>
 fused_launcher pick_dma_res(int act) {
     switch (act) {
-    case FL_ACT_NONE: return launch_dma<DT, FL_ACT_NONE, BK, BN, WAVES_N, OCC, RES>;
-    case FL_ACT_RELU: return launch_dma<DT, FL_ACT_RELU, BK, BN, WAVES_N, OCC, RES>;
-    case FL_ACT_GELU_TANH: return launch_dma<DT, FL_ACT_GELU_TANH, BK, BN, WAVES_N, OCC, RES>;
-    default: return launch_dma<DT, FL_ACT_GLU, BK, BN, WAVES_N, OCC, RES>;
+    case FL_ACT_NONE: return launch_dma<DT, FL_ACT_NONE, BK, BN, WAVES_N, OCC, RES, M16>;
+    case FL_ACT_RELU: return launch_dma<DT, FL_ACT_RELU, BK, BN, WAVES_N, OCC, RES, M16>;
+    case FL_ACT_GELU_TANH: return launch_dma<DT, FL_ACT_GELU_TANH, BK, BN, WAVES_N, OCC, RES, M16>;
+    default: return launch_dma<DT, FL_ACT_GLU, BK, BN, WAVES_N, OCC, RES, M16>;
     }
 }
 
-template <int DT, int BK, int BN, int WAVES_N = 2, int OCC = 1>
+template <int DT, int BK, int BN, int WAVES_N = 2, int OCC = 1, bool M16 = false>
 fused_launcher pick_dma(int act, bool residual) {
-    return residual ? pick_dma_res<DT, BK, BN, WAVES_N, OCC, true>(act)
-                    : pick_dma_res<DT, BK, BN, WAVES_N, OCC, false>(act);
+    return residual ? pick_dma_res<DT, BK, BN, WAVES_N, OCC, true, M16>(act)
+                    : pick_dma_res<DT, BK, BN, WAVES_N, OCC, false, M16>(act);
 }
 
 template <>
@@ -52,6 +52,12 @@ fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant, boo
         case kDirect32x128Occ2: return pick_dma<DT, 32, 128, 2, 2>(act, residual);
         case kDirect64x192: return pick_dma<DT, 64, 192>(act, residual);
         case kDirect32x192: return pick_dma<DT, 32, 192>(act, residual);
+        case kDirect64x256M16: return pick_dma<DT, 64, 256, 2, 1, true>(act, residual);
+        case kDirect64x256W8M16: return pick_dma<DT, 64, 256, 4, 1, true>(act, residual);
+        case kDirect64x192M16: return pick_dma<DT, 64, 192, 2, 1, true>(act, residual);
+        case kDirect64x128M16: return pick_dma<DT, 64, 128, 2, 1, true>(act, residual);
+        case kDirect32x256M16: return pick_dma<DT, 32, 256, 2, 1, true>(act, residual);
+        case kDirect32x256W8M16: return pick_dma<DT, 32, 256, 4, 1, true>(act, residual);
         default: break;
         }
     }

@@ -775,6 +775,12 @@ enum Variant {
     kDirect32x128Occ2 = 6,  // Dma16 BK 32, 256x128, two workgroups per CU
     kDirect64x192 = 7,  // Dma16 BK 64, 256x192 (a width that is not a power of two), 4 waves
     kDirect32x192 = 8,  // Dma16 BK 32, 256x192, 4 waves
+    kDirect64x256M16 = 9,     // Dma16 BK 64, 256x256, 4 waves, 16x16x32 MFMA blocks
+    kDirect64x256W8M16 = 10,  // Dma16 BK 64, 256x256, 8 waves, 16x16x32 MFMA blocks
+    kDirect64x192M16 = 11,    // Dma16 BK 64, 256x192, 4 waves, 16x16x32 MFMA blocks
+    kDirect64x128M16 = 12,    // Dma16 BK 64, 256x128, 4 waves, 16x16x32 MFMA blocks
+    kDirect32x256M16 = 13,    // Dma16 BK 32 (five-stage ring), 256x256, 4 waves, 16x16x32 MFMA blocks
+    kDirect32x256W8M16 = 14,  // Dma16 BK 32 (five-stage ring), 256x256, 8 waves, 16x16x32 MFMA blocks
 };
 
 // Returns the launcher of the fused kernel for (DT, act, variant, residual);

@@ -97,10 +97,11 @@ constexpr int64_t kOcc2MaxK192 = 2048;
 
 fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 8) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 14) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
         if (cfg == 2 || cfg == 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
         if (cfg == 7 || cfg == 8) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x192) is fp16/bf16 only", cfg);
+        if (cfg >= 9) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (16x16x32 blocks) is fp16/bf16 only", cfg);
         t = {256, 256, fl::kRegStaged};
         return FL_OK;
     }
@@ -113,6 +114,12 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     case 6: t = {256, 128, fl::kDirect32x128Occ2}; return FL_OK;
     case 7: t = {256, 192, fl::kDirect64x192}; return FL_OK;
     case 8: t = {256, 192, fl::kDirect32x192}; return FL_OK;
+    case 9: t = {256, 256, fl::kDirect64x256M16}; return FL_OK;
+    case 10: t = {256, 256, fl::kDirect64x256W8M16}; return FL_OK;
+    case 11: t = {256, 192, fl::kDirect64x192M16}; return FL_OK;
+    case 12: t = {256, 128, fl::kDirect64x128M16}; return FL_OK;
+    case 13: t = {256, 256, fl::kDirect32x256M16}; return FL_OK;
+    case 14: t = {256, 256, fl::kDirect32x256W8M16}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
@@ -125,12 +132,28 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     if (fills_two && K <= (bn == 256 ? 512 : bn == 192 ? kOcc2MaxK192 : 3072))
         t = {256, 128, fl::kDirect32x128Occ2};
     else if (bn == 128)
-        t = {256, 128, fl::kDirect64x128};
+        t = {256, 128, fl::kDirect64x128M16};
     else if (bn == 192)
-        t = {256, 192, fl::kDirect64x192};
+        t = {256, 192, fl::kDirect64x192M16};
     else
-        t = {256, 256, fl::kDirect64x256W8};
+        t = {256, 256, fl::kDirect64x256W8M16};
     return FL_OK;
+}
+
+// The sibling with 32x32 MFMA blocks of a kernel variant (same tile, same
+// copies).  The quantized-output, FP8-operand and backward kernels are built
+// with 32x32 blocks only: where the automatic choice names a 16x16 kernel,
+// they run its sibling.
+int family32(int v) {
+    switch (v) {
+    case fl::kDirect64x256M16: return fl::kDirect64x256;
+    case fl::kDirect64x256W8M16: return fl::kDirect64x256W8;
+    case fl::kDirect32x256M16: return fl::kDirect32x256;
+    case fl::kDirect32x256W8M16: return fl::kDirect64x256W8;
+    case fl::kDirect64x192M16: return fl::kDirect64x192;
+    case fl::kDirect64x128M16: return fl::kDirect64x128;
+    default: return v;
+    }
 }
 
 int grid_elementwise(int64_t work_items) {
@@ -211,6 +234,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
+    if ((qfmt >= 0 || fp8_in || bwd) && !(opt && opt->tile_cfg)) t.variant = family32(t.variant);
     const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
     const int es = (int)elem_size(dtype);
@@ -288,7 +312,7 @@ fl_options bwd_tiles(int dtype, int64_t M, int64_t N, int64_t K) {
     fl_options o{};
     TileShape t;
     tile_shape(dtype, M, N, K, &o, t);
-    o.tile_cfg = t.variant == fl::kDirect64x256W8 ? 5 : 2;
+    o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 5 : 2;
     return o;
 }
 
@@ -414,7 +438,8 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(FL_F16, M, N, K, &o, t);
-        if (t.variant == fl::kDirect32x128Occ2 || t.variant == fl::kDirect64x192) o.tile_cfg = 2;
+        const int v = family32(t.variant);
+        if (v == fl::kDirect32x128Occ2 || v == fl::kDirect64x192) o.tile_cfg = 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }
@@ -458,7 +483,7 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(dtype, M, N, K, &o, t);
-        o.tile_cfg = t.variant == fl::kDirect64x256W8 ? 5 : 2;
+        o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 5 : 2;
     } else if (o.tile_cfg != 2 && o.tile_cfg != 5) {
         return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2 and 5 only");
     }

@@ -100,27 +100,39 @@ typedef struct {
                            to the GPU whose workgroups loop over tiles. */
     int32_t tile_cfg;   /* Kernel and tile.  0 = automatic: fp32 runs the
                            register-staged 256x256 kernel; fp16/bf16 run the
-                           direct-to-LDS kernel with 256x256 tiles (8 waves,
-                           as 5), 256x192 (as 7) or 256x128 (4 waves, as 2),
-                           whichever takes the fewest waves x relative wave
-                           time on this GPU's compute units; short
-                           reductions (K <= 3072 for a 256x128 choice, K <=
-                           2048 for 256x192, K <= 512 for 256x256) whose
-                           256x128 grid fills two workgroups per compute unit
-                           run as 6.  1 = 256x256 direct, 4 waves
-                           (fp16/bf16; fp32 as 0); 2 = 256x128 direct
-                           (fp16/bf16 only); 3 = register-staged 256x256 for
-                           any dtype; 4 = 256x256 direct with 32-deep K
-                           stages; 5 = 256x256 direct with 8 waves (two per
-                           SIMD, 128x64 each; fp16/bf16; fp32 as 0);
-                           6 = 256x128 direct with 32-deep K stages and two
-                           workgroups per compute unit (fp16/bf16 only);
-                           7 and 8 = 256x192 direct (a tile width that is not
-                           a power of two, 4 waves of 128x96) with 64- and
-                           32-deep K stages (fp16/bf16 only).  Every
-                           variant gives bit-identical results.  Any other
-                           value, or a variant the problem does not allow,
-                           is FL_ERR_UNSUPPORTED. */
+                           direct-to-LDS kernel with 16x16x32 MFMA blocks and
+                           256x256 tiles (8 waves, as 10), 256x192 (as 11) or
+                           256x128 (as 12), whichever takes the fewest waves
+                           x relative wave time on this GPU's compute units;
+                           short reductions (K <= 3072 for a 256x128 choice,
+                           K <= 2048 for 256x192, K <= 512 for 256x256)
+                           whose 256x128 grid fills two workgroups per
+                           compute unit run as 6.  The quantized-output,
+                           FP8-operand and backward entry points, which are
+                           built with 32x32 blocks only, run the 32x32
+                           sibling of that choice (5, 7 or 2).
+                           Variants with 32x32x16 MFMA blocks: 1 = 256x256
+                           direct, 4 waves (fp16/bf16; fp32 as 0); 2 =
+                           256x128 direct (fp16/bf16 only); 3 =
+                           register-staged 256x256 for any dtype; 4 =
+                           256x256 direct with 32-deep K stages; 5 = 256x256
+                           direct with 8 waves (two per SIMD, 128x64 each;
+                           fp16/bf16; fp32 as 0); 6 = 256x128 direct with
+                           32-deep K stages and two workgroups per compute
+                           unit (fp16/bf16 only); 7 and 8 = 256x192 direct
+                           (a tile width that is not a power of two, 4 waves
+                           of 128x96) with 64- and 32-deep K stages
+                           (fp16/bf16 only).  Variants with 16x16x32 MFMA
+                           blocks (fp16/bf16 only): 9 = 256x256, 4 waves;
+                           10 = 256x256, 8 waves; 11 = 256x192; 12 =
+                           256x128; 13 and 14 = 256x256 with 4 and 8 waves
+                           and 32-deep K stages in a five-stage ring.  All
+                           variants of one MFMA shape give bit-identical
+                           results; the two shapes sum each output in a
+                           different order (both within the stated
+                           tolerance, and equal wherever the arithmetic is
+                           exact).  Any other value, or a variant the
+                           problem does not allow, is FL_ERR_UNSUPPORTED. */
     int32_t no_xcd_remap; /* 0 = place neighbouring tiles on one XCD; 1 = off */
     uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
                            counters (see fl_tile_grid); each output tile adds

@@ -133,8 +133,18 @@ def test_tile_grid(lib):
     for cfg in (7, 8):
         with pytest.raises(fl.FusedLinearError):
             fl.tile_grid(64, 64, 64, F32, tile_cfg=cfg)
+    # 16x16x32 MFMA blocks: 256x256 with 4 or 8 waves, 256x192, 256x128
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=9) == (256, 256, 16, 16)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=10) == (256, 256, 16, 16)
+    assert fl.tile_grid(1024, 21568, 4096, F16, tile_cfg=11) == (256, 192, 4, 113)
+    assert fl.tile_grid(4097, 3071, 1537, BF16, tile_cfg=12) == (256, 128, 17, 24)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=13) == (256, 256, 16, 16)
+    assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=14) == (256, 256, 16, 16)
+    for cfg in (9, 10, 11, 12, 13, 14):
+        with pytest.raises(fl.FusedLinearError):
+            fl.tile_grid(64, 64, 64, F32, tile_cfg=cfg)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=9)
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=15)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
@@ -226,7 +236,8 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
     (dict(out=A_P + 64), INVALID, "out overlaps A"),
     (dict(act=GLU), INVALID, "the gate needs Y"),
     (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
-    (dict(opt=fl.Options(0, 0, 9, 0, None)), UNSUPPORTED, "tile_cfg 9"),
+    (dict(opt=fl.Options(0, 0, 15, 0, None)), UNSUPPORTED, "tile_cfg 15"),
+    (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
     (dict(K=65536, N=32768), UNSUPPORTED, "B too large"),
 ])
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):

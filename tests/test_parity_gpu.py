@@ -306,28 +306,61 @@ def test_y_may_alias_out():
 
 # ------------------------------------------------------------ kernel variants
 
+# Variants that sum each output in the same order, in 32x32 blocks 16 deep
+# (v_mfma_f32_32x32x16) or in 16x16 blocks 32 deep (v_mfma_f32_16x16x32):
+# bit-identical within a family.
+FAMILY_32 = [1, 2, 3, 4, 5, 6, 7, 8]
+FAMILY_16 = [9, 10, 11, 12, 13, 14]
+
+
+def _same_family_bits(outs):
+    """Within each family every variant gives the same bits; the automatic
+    choice (cfg 0) gives the bits of one of the families."""
+    bases = {}
+    for fam in (FAMILY_32, FAMILY_16):
+        got = [c for c in fam if c in outs]
+        if got:
+            bases[got[0]] = outs[got[0]].view(np.uint8)
+            for c in got:
+                assert np.array_equal(outs[c].view(np.uint8), bases[got[0]]), f"tile_cfg {c} differs from {got[0]}"
+    if 0 in outs:
+        assert any(np.array_equal(outs[0].view(np.uint8), b) for b in bases.values()), "tile_cfg 0"
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["relu", "glu"])
 @pytest.mark.parametrize("shape", [(127, 129, 96), (300, 520, 1000), (513, 264, 72), (1024, 2048, 1024)])
 def test_kernel_variants_bit_identical_and_within_tolerance(dtype, act, shape):
     """Every fp16/bf16 kernel variant (256x256, 256x192 or 256x128 tiles,
     64- or 32-deep K stages, 4 or 8 waves, one or two workgroups per CU,
-    direct or register-staged loads) sums each output in the same k order,
-    so results are bit-identical; each also passes the oracle check.  The
-    shapes leave ragged last tiles for every width (N = 129, 520, 264 and
-    2048 are not multiples of 192)."""
+    direct or register-staged loads) of one MFMA family sums each output in
+    the same k order, so results are bit-identical within the family; each
+    also passes the oracle check.  The shapes leave ragged last tiles for
+    every width (N = 129, 520, 264 and 2048 are not multiples of 192)."""
     M, N, K = shape
     d = synth.draw(M, N, K, dtype, act, seed=21)
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
     outs = {}
-    cfgs = [0, 1, 2, 3, 4, 5, 6, 7, 8]
-    for cfg in cfgs:
+    for cfg in [0] + FAMILY_32 + FAMILY_16:
         say("variant", cfg, dtype, act, shape)
         outs[cfg] = _run_fused(d, act, dtype, tile_cfg=cfg)
         _assert_close(outs[cfg], ref, dtype, f"tile_cfg {cfg}")
-    base = outs[1].view(np.uint8)
-    for cfg, o in outs.items():
-        assert np.array_equal(o.view(np.uint8), base), f"tile_cfg {cfg} differs from tile_cfg 1"
+    _same_family_bits(outs)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["none", "relu", "glu"])
+@pytest.mark.parametrize("shape", [(67, 65, 70), (257, 264, 40), (300, 520, 24), (513, 770, 33), (129, 1024, 16)])
+def test_integer_inputs_bit_exact_every_variant(dtype, act, shape):
+    """Exact small-integer data: every variant, whatever its MFMA shape and
+    summation order, must give the oracle's bits on ragged shapes."""
+    M, N, K = shape
+    d = synth.draw_integer(M, N, K, dtype, act, seed=M + 5 * N + 11 * K, amax=1, bias_max=3)
+    ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype)
+    for cfg in FAMILY_32 + FAMILY_16:
+        say("integer variant", cfg, dtype, act, shape)
+        out = _run_fused(d, act, dtype, tile_cfg=cfg)
+        assert np.array_equal(out.view(np.uint8), ref.view(np.uint8)), (cfg, oracle.compare(out, ref, dtype))
 
 
 
@@ -376,12 +409,11 @@ def test_residual_kernel_variants_bit_identical(dtype, act):
     d = _with_residual(synth.draw(M, N, K, dtype, act, seed=22), dtype, seed=23)
     ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=d["R"])
     outs = {}
-    for cfg in range(9):
+    for cfg in [0] + FAMILY_32 + FAMILY_16:
         say("residual variant", cfg, dtype, act)
         outs[cfg] = _run_fused(d, act, dtype, tile_cfg=cfg)
         _assert_close(outs[cfg], ref, dtype, f"tile_cfg {cfg}")
-    for cfg, o in outs.items():
-        assert np.array_equal(o.view(np.uint8), outs[1].view(np.uint8)), f"tile_cfg {cfg}"
+    _same_family_bits(outs)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -762,7 +794,7 @@ def _first_cols(d, n, keys_cols, keys_rows=()):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act,residual", [("glu", False), ("relu", True), ("gelu_tanh", True), ("glu", True)])
-@pytest.mark.parametrize("cfg", [0, 5, 6, 7])
+@pytest.mark.parametrize("cfg", [0, 5, 6, 7, 10, 11, 13, 14])
 def test_side_input_paths_bit_identical(dtype, act, residual, cfg):
     M, K = 300, 200
     d = synth.draw(M, 521, K, dtype, act, seed=43)
@@ -814,7 +846,7 @@ def _rne_bf16_bits(x32):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["none", "relu"])
 @pytest.mark.parametrize("N", [520, 521])
-@pytest.mark.parametrize("cfg", [0, 3, 5, 6, 7])
+@pytest.mark.parametrize("cfg", [0, 3, 5, 6, 7, 9, 10, 11, 12, 13, 14])
 def test_k1_output_rounding_bit_exact(dtype, act, N, cfg):
     M = 300
     rng = np.random.default_rng(N + 7 * cfg)
