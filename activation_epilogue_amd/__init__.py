@@ -52,7 +52,8 @@ class FusedLinearError(RuntimeError):
 class Options(ctypes.Structure):
     """Mirror of fl_options."""
     _fields_ = [("group_m", ctypes.c_int32), ("persistent", ctypes.c_int32), ("tile_cfg", ctypes.c_int32),
-                ("no_xcd_remap", ctypes.c_int32), ("debug_tile_count", ctypes.c_void_p)]
+                ("no_xcd_remap", ctypes.c_int32), ("debug_tile_count", ctypes.c_void_p),
+                ("debug_sync", ctypes.c_int32)]
 
 
 _lib = None
@@ -131,14 +132,14 @@ def _stream(t, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _options(group_m=0, persistent=0, tile_cfg=0, no_xcd_remap=0, debug_tile_count=None):
+def _options(group_m=0, persistent=0, tile_cfg=0, no_xcd_remap=0, debug_tile_count=None, debug_sync=0):
     ptr = None
     if debug_tile_count is not None:
         import torch
         if debug_tile_count.dtype != torch.int32 or not debug_tile_count.is_cuda:
             raise TypeError("debug_tile_count must be an int32 device tensor")
         ptr = debug_tile_count.data_ptr()
-    return Options(int(group_m), int(persistent), int(tile_cfg), int(no_xcd_remap), ptr)
+    return Options(int(group_m), int(persistent), int(tile_cfg), int(no_xcd_remap), ptr, int(debug_sync))
 
 
 def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, R=None, stream=None, **options):
@@ -146,7 +147,7 @@ def fused_linear(A, B, bias=None, Y=None, act="relu", out=None, *, R=None, strea
     Y (M,N) for act="glu" (out = X + X*Y), R (M,N) an optional residual added
     before the activation (fl_fused_linear_residual).  Returns out (allocated
     with torch if not given).  Keyword options map to fl_options (group_m,
-    persistent, tile_cfg, no_xcd_remap, debug_tile_count)."""
+    persistent, tile_cfg, no_xcd_remap, debug_tile_count, debug_sync)."""
     import torch
     lib = load_library()
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:

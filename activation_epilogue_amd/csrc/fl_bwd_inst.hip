@@ -13,19 +13,19 @@
 namespace fl {
 namespace {
 
-template <int DT, int ACT, int BN, int WAVES_N>
+template <int DT, int ACT, int BN, int WAVES_N, bool M16>
 void launch_bwd(const GemmArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((fused_linear_bwd_kernel<DT, ACT, 64, BN, WAVES_N>), dim3(grid),
+    hipLaunchKernelGGL((fused_linear_bwd_kernel<DT, ACT, 64, BN, WAVES_N, M16>), dim3(grid),
                        dim3(Dma16<DT, ACT, 64, BN, WAVES_N>::THREADS), 0, s, a);
 }
 
-template <int DT, int BN, int WAVES_N>
+template <int DT, int BN, int WAVES_N, bool M16 = false>
 fused_launcher pick_bwd_act(int act) {
     switch (act) {
-    case FL_ACT_NONE: return launch_bwd<DT, FL_ACT_NONE, BN, WAVES_N>;
-    case FL_ACT_RELU: return launch_bwd<DT, FL_ACT_RELU, BN, WAVES_N>;
-    case FL_ACT_GELU_TANH: return launch_bwd<DT, FL_ACT_GELU_TANH, BN, WAVES_N>;
-    default: return launch_bwd<DT, FL_ACT_GLU, BN, WAVES_N>;
+    case FL_ACT_NONE: return launch_bwd<DT, FL_ACT_NONE, BN, WAVES_N, M16>;
+    case FL_ACT_RELU: return launch_bwd<DT, FL_ACT_RELU, BN, WAVES_N, M16>;
+    case FL_ACT_GELU_TANH: return launch_bwd<DT, FL_ACT_GELU_TANH, BN, WAVES_N, M16>;
+    default: return launch_bwd<DT, FL_ACT_GLU, BN, WAVES_N, M16>;
     }
 }
 
@@ -38,6 +38,8 @@ fused_launcher pick_bwd_for<FL_INST_DTYPE>(int act, int variant) {
     switch (variant) {
     case kDirect64x256W8: return pick_bwd_act<DT, 256, 4>(act);
     case kDirect64x128: return pick_bwd_act<DT, 128, 2>(act);
+    case kDirect64x256W8M16: return pick_bwd_act<DT, 256, 4, true>(act);
+    case kDirect64x128M16: return pick_bwd_act<DT, 128, 2, true>(act);
     default: return nullptr;
     }
 }

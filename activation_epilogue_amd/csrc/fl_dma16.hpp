@@ -128,7 +128,7 @@ struct Dma16 {
     static_assert(BN != 192 || !F8, "the 192-wide swizzle is for 16-bit B");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
-    static_assert(!M16 || (!F8 && !BWD), "16x16x32 blocks: 16-bit forward kernels");
+    static_assert(!M16 || !F8, "16x16x32 blocks: 16-bit operands");
     static constexpr int RBH = M16 ? 16 : 32;        // output rows of an accumulator block
     static constexpr int NRB = 128 / RBH;            // accumulator blocks per wave along M
     static constexpr int NI = WN / RBH;              // MFMA blocks per wave along N (square blocks)
@@ -297,12 +297,16 @@ struct Dma16 {
         const int g16 = lane >> 4, i16 = lane & 15;
         if constexpr (BT) {
             // rows of the B^T tile are output columns; fa depends on the row
-            // modulo 16 only, so one address per kk serves every ni (+32 rows)
-            const int rn = wn * WN + lrow;
+            // modulo 16 only, so one address per kk serves every ni (+32 rows,
+            // or +16 with 16x16 blocks, whose lanes take chunk kk*4 + g16 of
+            // rows i16 as the A operand does)
+            const int rA = M16 ? wm * 128 + i16 : r;
+            const int rn = wn * WN + (M16 ? i16 : lrow);
+            const int ck = M16 ? g16 : lg, kst = M16 ? 4 : 2;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                L.a_frag[kk] = r * (BK * 2) + (((kk * 2 + lg) ^ fa(r)) * 16);
-                L.b_frag[kk] = A_BYTES + rn * (BK * 2) + (((kk * 2 + lg) ^ fa(rn)) * 16);
+                L.a_frag[kk] = rA * (BK * 2) + (((kk * kst + ck) ^ fa(rA)) * 16);
+                L.b_frag[kk] = A_BYTES + rn * (BK * 2) + (((kk * kst + ck) ^ fa(rn)) * 16);
             }
         } else if constexpr (M16) {
             // A: lane (row r16, group g16) takes k = g16*8 .. g16*8+7 of each
@@ -501,7 +505,7 @@ struct Dma16 {
         } else if constexpr (P < RPA + NI * RPB) {
             constexpr int ni = (P - RPA) / RPB, h = (P - RPA) % RPB;
             if constexpr (BT) {
-                const u32x4_t v = *(const FL_LDS u32x4_t *)(buf + L.b_frag[kk] + ni * 32 * (BK * 2));
+                const u32x4_t v = *(const FL_LDS u32x4_t *)(buf + L.b_frag[kk] + ni * RBH * (BK * 2));
                 f.b[ni][0] = i32x2_t{(int)v[0], (int)v[1]};
                 f.b[ni][1] = i32x2_t{(int)v[2], (int)v[3]};
             } else if constexpr (!F8)
@@ -651,6 +655,12 @@ struct Dma16 {
             __syncthreads();
             pend = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
             block<0, 0, part_lo(1)>(L, nxt, 0, pend, f[(J + P) & 1], f[(J + P + 1) & 1], acc);
+            if (a.debug_sync) {
+                // the debugging schedule: every copy of this wave landed and
+                // every wave here before the next stage begins
+                wait_vm<0>();
+                __syncthreads();
+            }
         }
     }
 
@@ -1159,9 +1169,9 @@ __global__ void __launch_bounds__(64 * 2 * WAVES_N, OCC) fused_linear_dma16_kern
 // B^T with B given as (N, K) row-major, then dX = D * act'(Xs), the gate's
 // dY = D * Xs, and dbias += column sums of dX.  Same tile body and launch
 // loop as the forward kernel.
-template <int DT, int ACT, int BK, int BN, int WAVES_N>
+template <int DT, int ACT, int BK, int BN, int WAVES_N, bool M16 = false>
 __global__ void __launch_bounds__(64 * 2 * WAVES_N, 1) fused_linear_bwd_kernel(GemmArgs a) {
-    using T = Dma16<DT, ACT, BK, BN, WAVES_N, kCopySpread, 1, false, -1, DT, true>;
+    using T = Dma16<DT, ACT, BK, BN, WAVES_N, kCopySpread, 1, false, -1, DT, true, M16>;
     __shared__ __attribute__((aligned(1024))) char smem[T::SMEM_BYTES];
     const int ntiles = a.tiles_m * a.tiles_n;
     const int G = gridDim.x;

@@ -255,6 +255,7 @@ struct GemmArgs {
     int xcd_remap;
     int persistent;   // nonzero: loop over tiles with stride gridDim.x
     uint32_t *tile_count;
+    int debug_sync;   // nonzero: an extra full wait and barrier in every K stage (same results)
 };
 
 template <int DT, int ACT, bool VECTOR>
@@ -567,6 +568,7 @@ struct FusedTile {
                 compute_stage(cur, wm, wn, lane, acc);
                 if (more) store_stage(nxt, tid, ra, rb);
                 __syncthreads();
+                if (a.debug_sync) __syncthreads();
             }
         }
         epilogue(a, m0, n0, wm, wn, lane, acc);

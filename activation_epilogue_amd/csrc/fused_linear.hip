@@ -193,6 +193,8 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
             return fail(FL_ERR_INVALID_ARG, "persistent must be 0 or 1");
         if (opt->no_xcd_remap != 0 && opt->no_xcd_remap != 1)
             return fail(FL_ERR_INVALID_ARG, "no_xcd_remap must be 0 or 1");
+        if (opt->debug_sync != 0 && opt->debug_sync != 1)
+            return fail(FL_ERR_INVALID_ARG, "debug_sync must be 0 or 1");
         TileShape t;
         s = tile_shape(dtype, M, N, K, opt, t);
         if (s != FL_OK) return s;
@@ -234,7 +236,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
-    if ((qfmt >= 0 || fp8_in || bwd) && !(opt && opt->tile_cfg)) t.variant = family32(t.variant);
+    if (fp8_in && !(opt && opt->tile_cfg)) t.variant = family32(t.variant);
     const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
     const int es = (int)elem_size(dtype);
@@ -267,6 +269,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     a.xcd_remap = (opt && opt->no_xcd_remap) ? 0 : 1;
     a.persistent = (opt && opt->persistent) ? 1 : 0;
     a.tile_count = opt ? opt->debug_tile_count : nullptr;
+    a.debug_sync = (opt && opt->debug_sync) ? 1 : 0;
     const int ntiles = (int)(tiles_m * tiles_n);
     int grid = ntiles;
     if (a.persistent) {
@@ -276,7 +279,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (bwd) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_bwd_for<FL_F16>(act, t.variant)
                                                      : fl::pick_bwd_for<FL_BF16>(act, t.variant);
-        if (!f) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2 and 5 only");
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2, 5, 10 and 12 only");
         f(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_bwd");
     }
@@ -290,7 +293,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (qfmt >= 0) {
         const fl::fused_launcher q = dtype == FL_F16 ? fl::pick_quant_for<FL_F16>(act, t.variant, qfmt)
                                                      : fl::pick_quant_for<FL_BF16>(act, t.variant, qfmt);
-        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5, 6 and 7 only");
+        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12 only");
         q(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_quant");
     }
@@ -312,7 +315,7 @@ fl_options bwd_tiles(int dtype, int64_t M, int64_t N, int64_t K) {
     fl_options o{};
     TileShape t;
     tile_shape(dtype, M, N, K, &o, t);
-    o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 5 : 2;
+    o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 12;
     return o;
 }
 
@@ -483,9 +486,9 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(dtype, M, N, K, &o, t);
-        o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 5 : 2;
-    } else if (o.tile_cfg != 2 && o.tile_cfg != 5) {
-        return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2 and 5 only");
+        o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 12;
+    } else if (o.tile_cfg != 2 && o.tile_cfg != 5 && o.tile_cfg != 10 && o.tile_cfg != 12) {
+        return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2, 5, 10 and 12 only");
     }
     // dbias is a sum over every tile row: zero it first (a fill kernel on
     // the same stream), then the tiles add into it.

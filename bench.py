@@ -167,18 +167,47 @@ def device_info():
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family / model /
+    stepping numbers and the logical CPUs visible to this process."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                info[k] = v.strip()
     except OSError:
         pass
-    return None
+    info["logical_cpus"] = os.cpu_count()
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return info
+
+
+def _oracle_rows(w, d, rows, threads=None):
+    """The oracle's output for the given rows of the workload (FP64 inside,
+    rounded once to the output type), as its own storage arrays."""
+    import oracle
+    if w.bwd:
+        return oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=w.act, dtype=w.dtype, rows=rows,
+                                       threads=threads)
+    if w.in8:
+        return oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act,
+                                       out_dtype=w.dtype, rows=rows, threads=threads)
+    if w.qfmt:
+        return oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, qfmt=w.qfmt,
+                                         scale=w.scale, rows=rows, threads=threads, want_u=True)
+    return oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, R=d["R"],
+                               threads=threads)
 
 
 def cpu_baseline(w, d, target_s):
     """Time the FP64 oracle (as it is) on a bounded sample of output rows,
-    growing the sample until one call takes at least half of target_s."""
+    growing the sample until one call takes at least half of target_s.
+    Returns the baseline record and the rows and oracle output of the sample
+    (for the parity statistics)."""
     import numpy as np
     import oracle
     threads = oracle.max_threads()
@@ -186,24 +215,62 @@ def cpu_baseline(w, d, target_s):
     while True:
         rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        if w.bwd:
-            oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=w.act, dtype=w.dtype, rows=rows)
-        elif w.in8:
-            oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=w.act,
-                                    out_dtype=w.dtype, rows=rows)
-        elif w.qfmt:
-            oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, qfmt=w.qfmt,
-                                      scale=w.scale, rows=rows)
-        else:
-            oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, R=d["R"])
+        ref = _oracle_rows(w, d, rows)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or nrows >= w.M:
             break
         nrows = int(min(w.M, nrows * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
     flops = 2.0 * nrows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
-            "sample": f"{nrows} of {w.M} output rows of {w.name}, FP64, evenly spaced; "
-                      f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "cpu": cpu_model(),
+           "sample": f"{nrows} of {w.M} output rows of {w.name}, FP64, evenly spaced; "
+                     f"{flops / 2:.3g} multiply-adds in {dt:.1f} s (B decoded once per call)"}
+    return rec, rows, ref
+
+
+def per_core_rate():
+    """The oracle on one thread: the whole 127x129x96 fp32 ReLU workload
+    (repeated for at least 0.5 s) and 16 evenly spaced rows of the ragged
+    4097x3071x1537 bf16 one, in GFLOP/s of the GEMM (2*M*N*K)."""
+    import numpy as np
+    import oracle
+    from activation_epilogue_amd import synth
+    out = {}
+    for name, nrows in (("relu_f32_127x129x96", None), ("relu_bf16_4097x3071x1537", 16)):
+        w = synth.WORKLOADS[name]
+        d = synth.draw_workload(w)
+        rows = None if nrows is None else np.linspace(0, w.M - 1, nrows).astype(np.int64)
+        n_out = w.M if rows is None else nrows
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=w.act, dtype=w.dtype, rows=rows, threads=1)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 0.5:
+                break
+        out[name] = {"GFLOP/s": round(2.0 * n_out * w.N * w.K * reps / dt / 1e9, 3), "threads": 1,
+                     "rows": "all" if rows is None else f"{nrows} of {w.M}", "calls": reps}
+    return out
+
+
+def parity_stats(w, host_out, ref):
+    """Element-wise comparison of the benchmarked output rows with the
+    oracle's: max |dev - ref|, max relative error and the number of elements
+    outside the stated tolerance (or, for one-byte codes, outside the
+    boundary band)."""
+    import oracle
+    if w.qfmt:
+        codes, u = ref
+        r = oracle.compare_quant(host_out, codes, u, w.qfmt)
+        return {"elements": int(host_out.size), "violations": r["mismatches"],
+                "accepted_near_boundary": r["accepted_near_boundary"], "ok": bool(r["ok"]),
+                "tolerance": "code equal, or neighbouring code within the binary32 boundary band"}
+    if w.bwd:
+        ref = ref[0]  # dX
+    atol, rtol = oracle.TOLERANCE[w.dtype]
+    r = oracle.compare(host_out, ref, w.dtype)
+    return {"elements": int(host_out.size), "max_abs": r["max_abs"], "max_rel": r["max_rel"],
+            "violations": r["violations"], "ok": r["ok"], "tolerance": {"atol": atol, "rtol": rtol}}
 
 
 def main():
@@ -407,7 +474,21 @@ def main():
         result["pages_context"] = {"value": ref, "unit": "TFLOP/s", "hardware": "1x MI350X",
                                    "kernel": "the TLX page's Version 4", "ratio": round(tflops / ref, 3)}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+        import numpy as np
+        result["cpu_baseline"], rows, ref = cpu_baseline(w, d, args.cpu_seconds)
+        result["cpu_baseline"]["per_core"] = per_core_rate()
+        # the output the timed steps wrote, on the sampled rows, against the oracle
+        step()
+        torch.cuda.synchronize()
+        host = out.detach().to("cpu")
+        if w.qfmt:
+            host = host.numpy()
+        elif w.dtype == "bf16":
+            host = host.view(torch.int16).numpy().view(np.uint16)
+        else:
+            host = host.numpy()
+        result["parity"] = dict(parity_stats(w, np.ascontiguousarray(host[rows]), ref),
+                                rows=f"{len(rows)} of {w.M} (the CPU baseline's sample)")
 
     print(json.dumps(result), flush=True)
 

@@ -137,6 +137,11 @@ typedef struct {
     uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
                            counters (see fl_tile_grid); each output tile adds
                            one when it is written.  Caller zeroes it. */
+    int32_t debug_sync; /* 0 = normal; 1 = a debugging schedule: every K
+                           stage also waits for all of its wave's copies and
+                           meets the other waves at an extra barrier.  It
+                           changes timing only, so the results are the same
+                           bits as with 0 (a test checks this); slower. */
 } fl_options;
 
 /*
@@ -200,7 +205,7 @@ fl_status fl_fused_linear_residual(const void *A, const void *B,
  *          A, B, bias or Y.
  *   scale  finite fp32 (a per-tensor output scale).
  *   dtype  FL_F16 or FL_BF16 (FL_F32 inputs are FL_ERR_UNSUPPORTED).
- *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5, 6 or 7 (the
+ *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5, 6, 7, 10, 11 or 12 (the
  *          kernels the automatic choice uses); other values are
  *          FL_ERR_UNSUPPORTED.
  * Errors as fl_fused_linear_ex; an unknown qfmt or a non-finite scale is
@@ -262,10 +267,11 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
  *          bits may differ from run to run (the order of the additions is
  *          not fixed); dX and dY are deterministic.
  *   dtype  FL_F16 or FL_BF16 (FL_F32 is FL_ERR_UNSUPPORTED).
- *   opt    tile_cfg 0 (automatic: the 8-wave 256x256 kernel where the
- *          forward choice is 256x256, 256x128 elsewhere), 2 or 5; others
- *          are FL_ERR_UNSUPPORTED.  group_m, persistent and no_xcd_remap as
- *          for fl_fused_linear_ex.
+ *   opt    tile_cfg 0 (automatic: the 8-wave 256x256 kernel with 16x16x32
+ *          MFMA blocks where the forward choice is 256 wide, its 256x128
+ *          sibling elsewhere), 10 and 12 (those two), or 5 and 2 (the same
+ *          tiles with 32x32x16 blocks); others are FL_ERR_UNSUPPORTED.
+ *          group_m, persistent and no_xcd_remap as for fl_fused_linear_ex.
  * Alignment, sizes and errors as fl_fused_linear_ex; M = 0 or N = 0 writes
  * nothing but a zero dbias; K = 0 gives zeros.
  */

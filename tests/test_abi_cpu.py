@@ -89,6 +89,8 @@ def test_bad_options(lib):
     assert _fused(lib, opt=fl.Options(0, 2, 0, 0, None)) == INVALID
     assert _fused(lib, opt=fl.Options(0, 0, 99, 0, None)) == UNSUPPORTED
     assert "tile_cfg" in lib.fl_last_error().decode()
+    assert _fused(lib, opt=fl.Options(0, 0, 0, 0, None, 2)) == INVALID
+    assert b"debug_sync" in lib.fl_last_error()
 
 
 def test_unfused_entry_points_reject_bad_arguments(lib):
@@ -208,8 +210,8 @@ def _quant(lib, out=OUT_P, scale=1.0, q=0, dt=F16, act=RELU, Y=None, opt=None, M
     (dict(out=None), INVALID, "out is NULL"),
     (dict(out=A_P + 100), INVALID, "out overlaps A"),
     (dict(act=GLU, Y=Y_P, out=Y_P + 8191), INVALID, "out overlaps Y"),
-    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6 and 7"),
-    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6 and 7"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12"),
+    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12"),
 ])
 def test_quant_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _quant(lib, **kwargs) == status
@@ -271,8 +273,8 @@ def _bwd(lib, G=A_P, W=B_P, X=X_P, Y=None, dX=OUT_P, dY=None, db=DB_P, dt=F16, M
     (dict(db=X_P + 16), INVALID, "dbias overlaps"),
     (dict(db=DB_P + 2), INVALID, "dbias is not 4-byte aligned"),
     (dict(dX=A_P + 64), INVALID, "out overlaps A"),
-    (dict(opt=fl.Options(0, 0, 7, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
-    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 7, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 10 and 12"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 10 and 12"),
     (dict(K=2 ** 22), UNSUPPORTED, "too large"),
 ])
 def test_bwd_rejects_bad_arguments(lib, kwargs, status, msg):

@@ -91,3 +91,25 @@ def test_algorithmic_bytes_variants():
     # backward: G, W, X read, dX written, dbias zeroed and added to (fp32)
     assert bench.algorithmic_bytes(M, N, K, 2, "relu", bwd=True) == (M * K + K * N + 2 * M * N) * 2 + 2 * N * 4
     assert bench.algorithmic_bytes(M, N, K, 2, "glu", bwd=True) == (M * K + K * N + 4 * M * N) * 2 + 2 * N * 4
+
+
+def test_parity_stats_report_errors_and_violations():
+    """The bench line's parity statistics: max abs / rel error and the
+    violation count of a device output against the oracle's rows."""
+    import numpy as np
+    import oracle
+    w = synth.WORKLOADS["relu_f32_127x129x96"]
+    d = synth.draw_workload(w)
+    rows = np.array([0, 5, 126])
+    ref = bench._oracle_rows(w, d, rows)
+    good = bench.parity_stats(w, ref.copy(), ref)
+    assert good["ok"] and good["violations"] == 0 and good["max_abs"] == 0.0
+    bad = ref.copy()
+    bad[1, 3] += np.float32(1.0)
+    r = bench.parity_stats(w, bad, ref)
+    assert not r["ok"] and r["violations"] == 1 and abs(r["max_abs"] - 1.0) < 1e-6
+
+
+def test_cpu_model_names_the_host():
+    info = bench.cpu_model()
+    assert info["logical_cpus"] >= 1

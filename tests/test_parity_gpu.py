@@ -283,6 +283,38 @@ def test_npot_tiles_full_gate_shape(cfg):
     _assert_close(h, ref, w.dtype, f"{w.name} tile_cfg {cfg}")
 
 
+@pytest.mark.parametrize("cfg", [0, 2, 3, 5, 6, 7, 9, 10, 11, 12, 14])
+@pytest.mark.parametrize("dtype,act,shape", [("f16", "relu", (1024, 2048, 1024)), ("bf16", "glu", (513, 770, 1537)),
+                                             ("f32", "relu", (300, 260, 200))])
+def test_debug_sync_gives_the_same_bits(cfg, dtype, act, shape):
+    """The debugging schedule (an extra full wait for the copies and an extra
+    barrier in every K stage) only changes timing: a race between the copies,
+    the operand reads and the barriers would show as different bits."""
+    if dtype == "f32" and cfg not in (0, 3):
+        pytest.skip("fp32 runs the register-staged kernel only")
+    M, N, K = shape
+    d = synth.draw(M, N, K, dtype, act, seed=61)
+    say("debug sync", cfg, dtype, act, shape)
+    fast = _run_fused(d, act, dtype, tile_cfg=cfg)
+    slow = _run_fused(d, act, dtype, tile_cfg=cfg, debug_sync=1)
+    assert np.array_equal(fast.view(np.uint8), slow.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["gelu_bwd_bf16_8192x14336x4096", "glu_bwd_f16_1024x21568x4096"])
+def test_debug_sync_gives_the_same_bits_backward(name):
+    """The backward epilogue under the debugging schedule: dX and dY keep
+    their bits (dbias is summed with atomics, so only its value is checked)."""
+    w = synth.WORKLOADS[name]
+    d = synth.draw_bwd(1024, 1536, 1024, w.dtype, w.act, seed=62)
+    say("debug sync bwd", name)
+    fX, fY, fdb = _run_bwd(d, w.act, w.dtype)
+    sX, sY, sdb = _run_bwd(d, w.act, w.dtype, debug_sync=1)
+    assert np.array_equal(fX.view(np.uint8), sX.view(np.uint8))
+    if fY is not None:
+        assert np.array_equal(fY.view(np.uint8), sY.view(np.uint8))
+    assert np.allclose(fdb, sdb, rtol=1e-5, atol=1e-5)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = synth.WORKLOADS["relu_f16_4096x4096x4096"]
     d = synth.draw_workload(w)
@@ -487,12 +519,19 @@ def test_quant_random_inputs(dtype, act, qfmt, scale):
 def test_quant_kernel_variants_identical(dtype, qfmt):
     M, N, K = 513, 770, 600
     d = synth.draw(M, N, K, dtype, "relu", seed=19)
+    ref, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], None, act="relu", dtype=dtype, qfmt=qfmt,
+                                       scale=50.0, want_u=True)
     outs = {}
-    for cfg in (0, 2, 5, 6, 7):
+    for cfg in (0, 2, 5, 6, 7, 10, 11, 12):
         say("quant variant", cfg, dtype, qfmt)
         outs[cfg] = _run_quant(d, "relu", dtype, qfmt, 50.0, tile_cfg=cfg)
-    for cfg, o in outs.items():
-        assert np.array_equal(o, outs[2]), cfg
+        res = oracle.compare_quant(outs[cfg], ref, u, qfmt)
+        assert res["ok"], (cfg, res)
+    for cfg in (5, 6, 7):  # 32x32 blocks
+        assert np.array_equal(outs[cfg], outs[2]), cfg
+    for cfg in (11, 12):  # 16x16 blocks
+        assert np.array_equal(outs[cfg], outs[10]), cfg
+    assert np.array_equal(outs[0], outs[10]) or np.array_equal(outs[0], outs[2])
 
 
 def test_quant_full_size_whole_output():
@@ -665,20 +704,23 @@ def test_bwd_random_within_tolerance(dtype, act, shape):
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
 @pytest.mark.parametrize("act", ["relu", "glu"])
 def test_bwd_variants_and_tile_orders_agree(dtype, act):
-    """The 8-wave 256x256 and the 256x128 kernels, and the tile orders, give
-    bit-identical dX and dY; dbias (fp32 atomics) agrees within tolerance."""
+    """The 8-wave 256x256 and the 256x128 kernels of one MFMA shape (32x32 or
+    16x16 blocks), and the tile orders, give bit-identical dX and dY; dbias
+    (fp32 atomics) agrees within tolerance; every variant passes the oracle
+    check."""
     M, N, K = 600, 520, 300
     d = synth.draw_bwd(M, N, K, dtype, act, seed=17)
-    outs = []
-    for opts in [dict(tile_cfg=5), dict(tile_cfg=2), dict(tile_cfg=5, group_m=1, persistent=1),
-                 dict(tile_cfg=2, no_xcd_remap=1)]:
-        say("bwd variant", dtype, act, opts)
-        outs.append(_run_bwd(d, act, dtype, **opts))
-        _check_bwd(*outs[-1], d, act, dtype, f"bwd {opts}")
-    for o in outs[1:]:
-        assert np.array_equal(o[0].view(np.uint8), outs[0][0].view(np.uint8))
-        if act == "glu":
-            assert np.array_equal(o[1].view(np.uint8), outs[0][1].view(np.uint8))
+    for fam in ((5, 2), (10, 12)):
+        outs = []
+        for opts in [dict(tile_cfg=fam[0]), dict(tile_cfg=fam[1]), dict(tile_cfg=fam[0], group_m=1, persistent=1),
+                     dict(tile_cfg=fam[1], no_xcd_remap=1)]:
+            say("bwd variant", dtype, act, opts)
+            outs.append(_run_bwd(d, act, dtype, **opts))
+            _check_bwd(*outs[-1], d, act, dtype, f"bwd {opts}")
+        for o in outs[1:]:
+            assert np.array_equal(o[0].view(np.uint8), outs[0][0].view(np.uint8))
+            if act == "glu":
+                assert np.array_equal(o[1].view(np.uint8), outs[0][1].view(np.uint8))
 
 
 def test_bwd_aliases_and_no_dbias():
@@ -811,7 +853,7 @@ def test_side_input_paths_bit_identical(dtype, act, residual, cfg):
 
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
 @pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
-@pytest.mark.parametrize("cfg", [5, 2])
+@pytest.mark.parametrize("cfg", [5, 2, 10, 12])
 def test_bwd_side_input_paths_bit_identical(dtype, act, cfg):
     M, K = 300, 200
     d = synth.draw_bwd(M, 521, K, dtype, act, seed=47)
