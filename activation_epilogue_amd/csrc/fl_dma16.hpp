@@ -3,10 +3,10 @@
 // Same contract and epilogue as FusedTile (fl_kernels.hpp); this variant
 // serves every fp16/bf16 problem.  Pointers need only element alignment:
 // 16-byte buffer loads and the 8-byte epilogue accesses may be unaligned on
-// gfx950.  With N % 8 != 0 a B chunk that crosses N brings in the next row's
-// first values, which only reach output columns >= N (never stored); with
-// K % 8 != 0 the straddling A chunk is zeroed in LDS (fix_k_tail) and B's
-// rows >= K are read as zeros.  Differences from the register-staged kernel:
+// gfx950.  With N % 8 != 0 (16 for FP8 codes) a B chunk that crosses N
+// brings in the next row's first values, which only reach output columns
+// >= N (never stored); with K % 8 != 0 (16) the straddling A chunk is zeroed
+// in LDS (fix_k_tail) and B's rows >= K are read as zeros.  Differences from the register-staged kernel:
 //
 //   * Global -> LDS copies use buffer_load_dwordx4 with the LDS bit: each
 //     instruction moves 64 x 16 bytes straight into 1 KB of LDS at
@@ -69,7 +69,7 @@ __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t voffset, uint3
                  "s"(soffset), "s"(lds_addr)
                  : "memory", "m0");
 }
-// One 16-bit load and its wait in a single asm block.  A load into a VGPR
+// One 16-bit (or 8-bit) load and its wait in a single asm block.  A load into a VGPR
 // that the compiler sees, issued on a branch inside the K loop, makes its
 // wait-count pass assume the register may still be pending on every later
 // pass through the loop, and it then drains all outstanding copies
@@ -84,6 +84,14 @@ __device__ __forceinline__ uint32_t load_u16_now(i32x4_t rsrc, uint32_t voffset)
                  : "v"(voffset), "s"(rsrc)
                  : "memory");
     return v & 0xffffu;
+}
+__device__ __forceinline__ uint32_t load_u8_now(i32x4_t rsrc, uint32_t voffset) {
+    uint32_t v;
+    asm volatile("buffer_load_ubyte %0, %1, %2, 0 offen\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(v)
+                 : "v"(voffset), "s"(rsrc)
+                 : "memory");
+    return v & 0xffu;
 }
 #pragma clang diagnostic pop
 
@@ -119,7 +127,8 @@ struct Dma16 {
     static constexpr bool BT = BWD;  // B is (N, K) row-major, K contiguous
     static constexpr int IES = F8 ? 1 : 2;           // bytes per A/B element
     static constexpr int EPCH = 16 / IES;            // A/B elements per 16-byte chunk
-    static constexpr int KPM = F8 ? 64 : M16 ? 32 : 16;  // K per MFMA (32x32x64 fp8, 16x16x32 / 32x32x16 16-bit)
+    static constexpr int KPM = F8 ? (M16 ? 128 : 64) : M16 ? 32 : 16;  // K per MFMA: 16x16x128 / 32x32x64 fp8,
+                                                                        // 16x16x32 / 32x32x16 16-bit
     static constexpr int BM = 256, BN = BN_, BK = BK_;
     static_assert(BK * IES == 64 || BK * IES == 128, "stage depth: 64- or 128-byte A rows");
     static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
@@ -128,7 +137,6 @@ struct Dma16 {
     static_assert(BN != 192 || !F8, "the 192-wide swizzle is for 16-bit B");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
-    static_assert(!M16 || !F8, "16x16x32 blocks: 16-bit operands");
     static constexpr int RBH = M16 ? 16 : 32;        // output rows of an accumulator block
     static constexpr int NRB = 128 / RBH;            // accumulator blocks per wave along M
     static constexpr int NI = WN / RBH;              // MFMA blocks per wave along N (square blocks)
@@ -211,9 +219,18 @@ struct Dma16 {
     // B swizzle: chunk c of k-row r sits at c ^ fb(r).  16-bit B: fb in
     // {0,6,12,10} by r % 4 (rows are 256 or 512 bytes, a multiple of the bank
     // width); conflict-free for the transposed 8-byte reads (4 rows x 2 or 4
-    // chunks per 16 or 32 lanes).  FP8 B: fb = r % 8, so the 8 k-rows a
-    // 16-lane transposed read touches (one 16-byte chunk each) fall in 8
-    // different chunks.
+    // chunks per 16 or 32 lanes).
+    //
+    // FP8 B: a transposed 8-byte read serves 32 lanes per cycle, which touch
+    // 8 k-rows in two 16-byte chunks each (32x32x64 blocks: chunks c and c+1,
+    // c even) or in one chunk of 16 k-rows (16x16x128 blocks: rows 0..7 and
+    // 32..39 of a 64-row group).  256-byte rows (BN = 256) span the 64 banks,
+    // so the 16 (row, chunk) pairs need 16 different chunks: fb = 2*(r % 8)
+    // puts chunk c of rows 0..7 on the 8 chunks of c's parity, and the XOR
+    // of 1 by bit 5 of the row moves rows 32..63 to the other parity.
+    // 128-byte rows (BN = 128) alternate between the two halves of the banks,
+    // so fb = r % 8 (with the same bit-5 term) suffices: 4 rows of each half
+    // x 2 chunks, or 8 rows of each half x 1 chunk, on 8 different chunks.
     //
     // 16-bit B, BN = 192: rows of 384 bytes, so odd rows already start half
     // a bank width (128 bytes) over; fb = r & 2 moves rows 2 and 3 of every
@@ -228,7 +245,7 @@ struct Dma16 {
     // bank groups rows 0..7 leave free.
     __device__ __forceinline__ static int fb(int r) {
         if constexpr (F8)
-            return r & 7;
+            return (BN == 256 ? (r & 7) << 1 : (r & 7)) ^ (M16 ? ((r >> 5) & 1) : 0);
         else if constexpr (BN == 192)
             return (r & 2) ^ (M16 ? ((r >> 1) & 4) : 0);
         else
@@ -307,6 +324,22 @@ struct Dma16 {
             for (int kk = 0; kk < KK; ++kk) {
                 L.a_frag[kk] = rA * (BK * 2) + (((kk * kst + ck) ^ fa(rA)) * 16);
                 L.b_frag[kk] = A_BYTES + rn * (BK * 2) + (((kk * kst + ck) ^ fa(rn)) * 16);
+            }
+        } else if constexpr (F8 && M16) {
+            // FP8 in 16x16 blocks 128 deep (v_mfma_scale_f32_16x16x128):
+            // A: lane (row i16, group g16) takes k = g16*32 .. g16*32+31 of
+            // the block, chunks kk*8 + g16*2 and the next one (address bit 4).
+            const int r16 = wm * 128 + i16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) L.a_frag[kk] = r16 * (BK * IES) + (((kk * 8 + g16 * 2) ^ fa(r16)) * 16);
+            // B: lane L of group g16 points at k-row g16*32 + L/2 (+8 per
+            // transposed read), 8 columns at 8*(L%2) of the 16-column block:
+            // it then holds 8 k-values of column i16 per read.
+            const int rk = g16 * 32 + (i16 >> 1);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = wn * WN + ni * 16 + 8 * (i16 & 1);
+                L.b_frag[ni] = A_BYTES + rk * BN + (((n >> 4) ^ fb(rk)) * 16) + (n & 15);
             }
         } else if constexpr (M16) {
             // A: lane (row r16, group g16) takes k = g16*8 .. g16*8+7 of each
@@ -411,19 +444,73 @@ struct Dma16 {
     }
 
     // Fix-up of the last K stage (origin kt*BK) when K or N is not a
-    // multiple of 8, run by each wave on the chunks it copied, after its
-    // copies have landed and before the barrier that publishes them:
+    // multiple of EPCH (the elements of a 16-byte chunk), run by each wave on
+    // the chunks it copied, after its copies have landed and before the
+    // barrier that publishes them:
     //  * an A chunk that straddles K also holds the first values of the next
     //    row; the values at or past K are zeroed so that only k < K reaches
-    //    the accumulators;
+    //    the accumulators (B's rows at or past K read as zeros);
     //  * a copy that runs past the end of A (or B) is range-checked per
-    //    dword, so the dword that holds the buffer's last element can read as
-    //    zero.  The lane whose chunk holds A[M-1][K-1] (B[K-1][N-1]) reloads
-    //    that element with a 2-byte load and writes it into LDS.  The reload
-    //    goes through the tile's own descriptor (based at row m0 of A, at
-    //    column n0 of B, or at row n0 of the transposed B), so its offset is
-    //    below 256 rows of the operand, which the host keeps under 2^31
-    //    bytes, however large the whole operand is.
+    //    dword, so a dword that holds the buffer's last bytes and runs past
+    //    it reads as zero: with 2-byte elements the last element, with FP8
+    //    codes up to the last three.  A lane whose chunk holds one of those
+    //    elements (one that belongs to its own row, below K, or below N for
+    //    B) reloads it with a 1- or 2-byte load and writes it into LDS.  The
+    //    reload goes through the tile's own descriptor (based at row m0 of A,
+    //    at column n0 of B, or at row n0 of the transposed B), so its offset
+    //    is below 256 rows of the operand, which the host keeps under 2^31
+    //    bytes, however large the whole operand is.  The elements a partial
+    //    dword can hold lie in the last row of B (the host asks for N >= 3
+    //    with FP8 codes), so the last stage has them.
+    static constexpr int EPD = 4 / IES;  // elements per dword
+
+    __device__ __forceinline__ static uint32_t keep_mask(int valid, int d) {
+        const int vb = valid * IES - 4 * d;  // bytes of dword d below the end of the row
+        return vb >= 4 ? 0xffffffffu : vb <= 0 ? 0u : (1u << (8 * vb)) - 1u;
+    }
+
+    __device__ __forceinline__ static uint32_t load_elem_now(i32x4_t rsrc, uint32_t voffset) {
+        if constexpr (F8)
+            return load_u8_now(rsrc, voffset);
+        else
+            return load_u16_now(rsrc, voffset);
+    }
+
+    // Reload the elements of a chunk that a partial last dword may have
+    // zeroed: elements e = first .. valid-1 (at most EPD-1 of them), element
+    // e at byte offset (rel + e) * IES of the descriptor.  All in 32 bits:
+    // the offsets stay below 256 rows (A, B^T) or below the whole operand
+    // (B), which the host keeps under 2^31 bytes.
+    __device__ __forceinline__ static void reload_one(i32x4_t rsrc, uint32_t rel, int e, u32x4_t &v) {
+        const uint32_t x = load_elem_now(rsrc, (rel + e) * IES);
+        const int sh = 8 * ((e * IES) & 3);
+        const uint32_t m = (F8 ? 0xffu : 0xffffu) << sh;
+        v[(e * IES) >> 2] = (v[(e * IES) >> 2] & ~m) | (x << sh);
+    }
+    __device__ __forceinline__ static void reload_tail(i32x4_t rsrc, uint32_t rel, int first, int valid, u32x4_t &v) {
+        if constexpr (EPD == 2) {
+            // 2-byte elements: the one element `first` (>= 0 where called)
+            if (first < valid) reload_one(rsrc, rel, first, v);
+        } else {
+            for (int e = first > 0 ? first : 0; e < valid; ++e) reload_one(rsrc, rel, e, v);
+        }
+    }
+
+    // The K-contiguous operand (A, or B^T): chunk of row `row` (of `rows`,
+    // the descriptor based at row `r0`) starting at k = kc, `valid` values
+    // below K.  Only the last EPD-1 rows can hold an element of the
+    // buffer's last dword.
+    __device__ __forceinline__ static void fix_kc_chunk(i32x4_t rsrc, int row, int rows, int r0, int K, int kc,
+                                                        int valid, FL_LDS char *p) {
+        u32x4_t v = *(FL_LDS u32x4_t *)p;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] &= keep_mask(valid, d);
+        const int dr = rows - row;  // 1 for the last row
+        if (dr > 0 && dr < EPD)
+            reload_tail(rsrc, (uint32_t)((row - r0) * K + kc), dr * K - (EPD - 1) - kc, valid, v);
+        *(FL_LDS u32x4_t *)p = v;
+    }
+
     __device__ __forceinline__ static void fix_k_tail(const GemmArgs &a, const Lane &L, int m0, int n0, int kt,
                                                       int wave, int lane, FL_LDS char *buf) {
         const int k0 = kt * BK, kleft = a.K - k0;
@@ -431,23 +518,9 @@ struct Dma16 {
         for (int i = 0; i < NA; ++i) {
             const int kb = L.a_k[i & 1];
             const int valid = kleft - kb;  // values of this chunk below K
-            if (valid > 0 && valid < 8) {
-                FL_LDS char *p = buf + (wave * NA + i) * 1024 + lane * 16;
-                u32x4_t v = *(FL_LDS u32x4_t *)p;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t keep = (2 * d + 1 < valid) ? 0xffffffffu : (2 * d < valid) ? 0x0000ffffu : 0u;
-                    v[d] &= keep;
-                }
-                const int row = m0 + A_ROWS_PER_COPY * (wave * NA + i) + a_row_in_copy(lane);
-                if (row == a.M - 1) {
-                    const uint32_t e = (uint32_t)(valid - 1);
-                    const uint32_t x =
-                        load_u16_now(L.rA, (uint32_t)(((size_t)(a.M - 1 - m0) * a.K + (a.K - 1)) * 2));
-                    v[e >> 1] = (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
-                }
-                *(FL_LDS u32x4_t *)p = v;
-            }
+            if (valid > 0 && valid < EPCH)
+                fix_kc_chunk(L.rA, m0 + A_ROWS_PER_COPY * (wave * NA + i) + a_row_in_copy(lane), a.M, m0, a.K,
+                             k0 + kb, valid, buf + (wave * NA + i) * 1024 + lane * 16);
         }
         if constexpr (BT) {
             // B^T rows are K-contiguous like A's: the same two fixes
@@ -455,36 +528,25 @@ struct Dma16 {
             for (int i = 0; i < NB; ++i) {
                 const int kb = L.b_k[i & 1];
                 const int valid = kleft - kb;
-                if (valid > 0 && valid < 8) {
-                    FL_LDS char *p = buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16;
-                    u32x4_t v = *(FL_LDS u32x4_t *)p;
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint32_t keep = (2 * d + 1 < valid) ? 0xffffffffu : (2 * d < valid) ? 0x0000ffffu : 0u;
-                        v[d] &= keep;
-                    }
-                    const int row = n0 + B_ROWS_PER_COPY_T * (wave * NB + i) + lane / CA;
-                    if (row == a.N - 1) {
-                        const uint32_t e = (uint32_t)(valid - 1);
-                        const uint32_t x =
-                            load_u16_now(L.rB, (uint32_t)(((size_t)(a.N - 1 - n0) * a.K + (a.K - 1)) * 2));
-                        v[e >> 1] =
-                            (e & 1) ? ((v[e >> 1] & 0x0000ffffu) | (x << 16)) : ((v[e >> 1] & 0xffff0000u) | x);
-                    }
-                    *(FL_LDS u32x4_t *)p = v;
-                }
+                if (valid > 0 && valid < EPCH)
+                    fix_kc_chunk(L.rB, n0 + B_ROWS_PER_COPY_T * (wave * NB + i) + lane / CA, a.N, n0, a.K, k0 + kb,
+                                 valid, buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16);
             }
-        } else if (a.N & 7) {
+        } else if (a.N % EPCH) {
+            // columns at or past N are never stored, so only the reload, of
+            // elements of B's last row (N >= EPD-1 where FP8 codes are read)
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int rb = b_row(L, i);  // K row within the stage
                 const int cb = ((64 % CB == 0) ? lane % CB : (64 * (wave * NB + i) + lane) % CB) ^ fb(rb);
-                const int col = n0 + cb * 8;
-                if (rb == kleft - 1 && col <= a.N - 1 && a.N - 1 < col + 8) {
-                    const int e = a.N - 1 - col;
-                    FL_LDS uint16_t *q =
-                        (FL_LDS uint16_t *)(buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16 + 2 * e);
-                    *q = (uint16_t)load_u16_now(L.rB, (uint32_t)(((size_t)(a.K - 1) * a.N + (a.N - 1 - n0)) * 2));
+                const int col = n0 + cb * EPCH;
+                const int vn = a.N - col < EPCH ? a.N - col : EPCH;  // values of this chunk below N
+                const int first = a.N - (EPD - 1) - col;              // chunk element of the first reload
+                if (rb == kleft - 1 && vn > 0 && first < vn) {
+                    FL_LDS char *p = buf + A_BYTES + (wave * NB + i) * 1024 + lane * 16;
+                    u32x4_t v = *(FL_LDS u32x4_t *)p;
+                    reload_tail(L.rB, (uint32_t)((a.K - 1) * a.N + (col - n0)), first, vn, v);
+                    *(FL_LDS u32x4_t *)p = v;
                 }
             }
         }
@@ -514,7 +576,7 @@ struct Dma16 {
                                                                                 h * 4 * (BN * 2))));
             else
                 f.b[ni][h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (FL_LDS i32x2_t *)(buf + L.b_frag[ni] + kk * 64 * BN + h * 8 * BN));
+                    (FL_LDS i32x2_t *)(buf + L.b_frag[ni] + kk * KPM * BN + h * 8 * BN));
         } else {
             constexpr int Q = P - RPA - NI * RPB;
             constexpr int mi = 1 + Q / RPA, h = Q % RPA;
@@ -551,7 +613,10 @@ struct Dma16 {
             const i32x8_t av = __builtin_shufflevector(__builtin_bit_cast(i32x4_t, f.a[mi][0]),
                                                        __builtin_bit_cast(i32x4_t, f.a[mi][1]), 0, 1, 2, 3, 4, 5, 6, 7);
             // format codes 0, 0: both operands FP8 E4M3; no block scales
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+            if constexpr (M16)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+            else
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[mi][ni], 0, 0, 0, 0, 0, 0);
             return;
         }
         const s16x8_t bv = __builtin_bit_cast(
@@ -635,7 +700,15 @@ struct Dma16 {
     // kt+1's first operands.
     // P: the operand buffer stage kt starts from (f[P]); with an odd number
     // of blocks per stage it alternates from one stage to the next.
-    template <int J = 0, int P = 0>
+    // TAIL: the stage may be the one before the last, which fixes up the
+    // last stage's chunks (fix_k_tail).  With SPLIT_TAIL the K loop runs its
+    // other stages from a copy without that code (the 8-wave loop of 64
+    // MFMAs shrinks from about 500 instructions to 175).  The 4-wave kernels
+    // with 16x16 blocks keep one loop: split, the compiler's allocation of
+    // their 192 (or 128) accumulator registers rotates them through copies
+    // (about 250 accumulator moves per pass), which the single loop avoids.
+    static constexpr bool SPLIT_TAIL = !(M16 && WAVES == 4);
+    template <int J = 0, int P = 0, bool TAIL = false>
     __device__ __forceinline__ static void stage(const GemmArgs &a, const Lane &L, const FL_LDS char *lds,
                                                  uint32_t lds_addr, int m0, int n0, int kt, int nk, int buf,
                                                  int wave, Stage &pend, Frags (&f)[2], acc_t (&acc)[NRB][NI]) {
@@ -644,13 +717,13 @@ struct Dma16 {
             constexpr int p = J + 1 < SPR ? J + 1 : SPR;  // part SPR is empty
             block<0, part_lo(p), part_lo(p < SPR ? p + 1 : p)>(L, cur, J + 1, pend, f[(J + P) & 1],
                                                                 f[(J + P + 1) & 1], acc);
-            stage<J + 1, P>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+            stage<J + 1, P, TAIL>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
         } else {
             const int nbuf = buf + 1 == NBUF ? 0 : buf + 1;
             const FL_LDS char *nxt = lds + nbuf * BUF_BYTES;
             wait_vm<(NBUF - 2) * DMA_PER_WAVE>();
-            if constexpr (!F8)
-                if (((a.K | a.N) & 7) && kt + 2 == nk)
+            if constexpr (TAIL)
+                if (((a.K | a.N) % EPCH) && kt + 2 == nk)
                     fix_k_tail(a, L, m0, n0, kt + 1, wave, threadIdx.x & 63, (FL_LDS char *)nxt);
             __syncthreads();
             pend = stage_of(a, kt + NBUF, wave, lds_addr + buf * BUF_BYTES);
@@ -1104,30 +1177,62 @@ struct Dma16 {
             Stage pend = stage_of(a, NBUF - 1, wave, lds_addr + (NBUF - 1) * BUF_BYTES);
             copy_range<0, part_lo(1)>(L, pend);
             wait_vm<(NBUF - 2) * DMA_PER_WAVE + part_lo(1)>();
-            if constexpr (!F8)
-                if (((a.K | a.N) & 7) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
+            if (((a.K | a.N) % EPCH) && nk == 1) fix_k_tail(a, L, m0, n0, 0, wave, lane, (FL_LDS char *)lds);
             __syncthreads();
             Frags f[2];
             read_all(L, lds, 0, f[0]);
             int buf = 0;
-            if constexpr (KK % 2 == 0) {
+            // With SPLIT_TAIL the stages up to nk-3 run without the tail
+            // fix-up and the last two from a copy that has it (stage nk-2
+            // fixes stage nk-1); otherwise every stage runs the one copy.
+            int kt = 0;
+            if constexpr (KK % 2 == 0 && !SPLIT_TAIL) {
 #pragma unroll 1
-                for (int kt = 0; kt < nk; ++kt) {
+                for (; kt < nk; ++kt) {
+                    stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                }
+            } else if constexpr (KK % 2 == 0) {
+#pragma unroll 1
+                for (; kt + 2 < nk; ++kt) {
                     stage(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
                     buf = buf + 1 == NBUF ? 0 : buf + 1;
                 }
-            } else {
+                if (kt < nk) {
+                    stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    ++kt;
+                }
+                if (kt < nk) stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+            } else if constexpr (!SPLIT_TAIL) {
                 // an odd number of blocks per stage: two stages per pass, the
-                // second starting from the other operand buffer
+                // second starting from the other operand buffer; an odd last
+                // stage after the loop (no branch inside the loop body)
 #pragma unroll 1
-                for (int kt = 0; kt < nk; kt += 2) {
+                for (; kt + 1 < nk; kt += 2) {
+                    stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    stage<0, 1, true>(a, L, lds, lds_addr, m0, n0, kt + 1, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                }
+                if (kt < nk) stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+            } else {
+                // the same, with the last two or three stages after the loop
+#pragma unroll 1
+                for (; kt + 3 < nk; kt += 2) {
                     stage<0, 0>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
                     buf = buf + 1 == NBUF ? 0 : buf + 1;
-                    if (kt + 1 < nk) {
-                        stage<0, 1>(a, L, lds, lds_addr, m0, n0, kt + 1, nk, buf, wave, pend, f, acc);
-                        buf = buf + 1 == NBUF ? 0 : buf + 1;
-                    }
+                    stage<0, 1>(a, L, lds, lds_addr, m0, n0, kt + 1, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
                 }
+                if (kt + 1 < nk) {
+                    stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    stage<0, 1, true>(a, L, lds, lds_addr, m0, n0, kt + 1, nk, buf, wave, pend, f, acc);
+                    buf = buf + 1 == NBUF ? 0 : buf + 1;
+                    kt += 2;
+                }
+                if (kt < nk) stage<0, 0, true>(a, L, lds, lds_addr, m0, n0, kt, nk, buf, wave, pend, f, acc);
             }
             // The look-ahead copies (past the end of K) must land before this
             // workgroup's LDS is reused.

@@ -12,19 +12,19 @@
 namespace fl {
 namespace {
 
-template <int DT, int ACT, int BN, int WAVES_N>
+template <int DT, int ACT, int BN, int WAVES_N, bool M16>
 void launch_f8(const GemmArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, 128, BN, WAVES_N, kCopySpread, 1, false, -1, kInFp8>),
+    hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, 128, BN, WAVES_N, kCopySpread, 1, false, -1, kInFp8, M16>),
                        dim3(grid), dim3(Dma16<DT, ACT, 128, BN, WAVES_N, 1, 1, false, -1, kInFp8>::THREADS), 0, s, a);
 }
 
-template <int DT, int BN, int WAVES_N>
+template <int DT, int BN, int WAVES_N, bool M16 = false>
 fused_launcher pick_f8_act(int act) {
     switch (act) {
-    case FL_ACT_NONE: return launch_f8<DT, FL_ACT_NONE, BN, WAVES_N>;
-    case FL_ACT_RELU: return launch_f8<DT, FL_ACT_RELU, BN, WAVES_N>;
-    case FL_ACT_GELU_TANH: return launch_f8<DT, FL_ACT_GELU_TANH, BN, WAVES_N>;
-    default: return launch_f8<DT, FL_ACT_GLU, BN, WAVES_N>;
+    case FL_ACT_NONE: return launch_f8<DT, FL_ACT_NONE, BN, WAVES_N, M16>;
+    case FL_ACT_RELU: return launch_f8<DT, FL_ACT_RELU, BN, WAVES_N, M16>;
+    case FL_ACT_GELU_TANH: return launch_f8<DT, FL_ACT_GELU_TANH, BN, WAVES_N, M16>;
+    default: return launch_f8<DT, FL_ACT_GLU, BN, WAVES_N, M16>;
     }
 }
 
@@ -38,6 +38,7 @@ fused_launcher pick_fp8_for<FL_INST_DTYPE>(int act, int variant) {
     case kDirect64x256W8: return pick_f8_act<DT, 256, 4>(act);
     case kDirect64x256: return pick_f8_act<DT, 256, 2>(act);
     case kDirect64x128: return pick_f8_act<DT, 128, 2>(act);
+    case kDirect64x128M16: return pick_f8_act<DT, 128, 2, true>(act);
     default: return nullptr;
     }
 }

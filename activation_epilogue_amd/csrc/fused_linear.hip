@@ -236,7 +236,6 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
     if (s != FL_OK) return s;
-    if (fp8_in && !(opt && opt->tile_cfg)) t.variant = family32(t.variant);
     const int64_t tiles_m = (M + t.bm - 1) / t.bm, tiles_n = (N + t.bn - 1) / t.bn;
     if (tiles_m * tiles_n > kMaxDim) return fail(FL_ERR_UNSUPPORTED, "too many output tiles");
     const int es = (int)elem_size(dtype);
@@ -286,7 +285,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (fp8_in) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
                                                      : fl::pick_fp8_for<FL_BF16>(act, t.variant);
-        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2 and 5 only");
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2, 5 and 12 only");
         f(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_fp8");
     }
@@ -420,8 +419,9 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (s != FL_OK) return s;
     s = check_dims(M, N, K);
     if (s != FL_OK) return s;
-    if (K % 16 != 0 || N % 16 != 0)
-        return fail(FL_ERR_UNSUPPORTED, "FP8 inputs need K and N multiples of 16 (whole 16-byte chunks)");
+    // A partial last dword of B may hold its last three codes; they must lie
+    // in its last row, which the kernel's last K stage patches.
+    if (N > 0 && N < 3) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs need N >= 3");
     if (!aligned(A8, 16) || !aligned(B8, 16)) return fail(FL_ERR_INVALID_ARG, "A8 and B8 must be 16-byte aligned");
     if (opt) {
         TileShape t;
@@ -441,8 +441,12 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(FL_F16, M, N, K, &o, t);
-        const int v = family32(t.variant);
-        if (v == fl::kDirect32x128Occ2 || v == fl::kDirect64x192) o.tile_cfg = 2;
+        // 32x32x64 blocks: the 8-wave 256x256 kernel where the forward
+        // choice is 256 wide, 256x128 elsewhere (no 192-wide or two-per-CU
+        // FP8 kernels).  The 16x16x128 kernel (256x128) is an option: as
+        // fast as the 32x32x64 one of the same tile, where 16-bit blocks of
+        // 16x16 gain from their lower power draw.
+        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 1 : 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }

@@ -222,18 +222,22 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
  * operands ("Optimizing GEMM + Activation on CDNA4 with TLX", "Future Work":
  * the projection in FP8, which CDNA4's matrix cores run at twice the 16-bit
  * rate and which halves the operand traffic).  A8 (M,K) and B8 (K,N) are OCP
- * FP8 E4M3 codes, row-major; the products are summed in fp32 by
- * v_mfma_f32_32x32x64_f8f6f4, the sum is multiplied by ab_scale (the product
- * of the two per-tensor scales) in fp32, then bias, activation (the gate with
- * Y), one rounding to out_dtype and one store, as fl_fused_linear.
+ * FP8 E4M3 codes, row-major; the products are summed in fp32 by the
+ * matrix cores' scaled FP8 instructions (32x32x64 or 16x16x128 blocks, no
+ * block scales), the sum is multiplied by ab_scale (the product of the two
+ * per-tensor scales) in fp32, then bias, activation (the gate with Y), one
+ * rounding to out_dtype and one store, as fl_fused_linear.
  *   A8, B8    device pointers to M*K and K*N bytes, 16-byte aligned.
  *   ab_scale  finite fp32.
  *   bias, Y, out  in out_dtype (FL_F16 or FL_BF16; FL_F32 is
  *             FL_ERR_UNSUPPORTED), conventions as fl_fused_linear.
- *   K and N must be multiples of 16 (FL_ERR_UNSUPPORTED otherwise); any M.
+ *   Any M and K; N of 1 or 2 is FL_ERR_UNSUPPORTED (rows of B of 1 or 2
+ *             bytes), any other N is served.
  *   opt       tile_cfg 0 (automatic: the 8-wave 256x256 kernel, or 256x128
  *             where fl_fused_linear would use 128- or 192-wide tiles), 1, 2
- *             or 5; others are FL_ERR_UNSUPPORTED.
+ *             or 5 (32x32x64 blocks, bit-identical to one another) or 12
+ *             (16x16x128 blocks, 256x128 tiles: the same products summed in
+ *             another order); others are FL_ERR_UNSUPPORTED.
  */
 fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               const void *bias, const void *Y, void *out,

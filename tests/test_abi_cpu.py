@@ -231,15 +231,15 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
 @pytest.mark.parametrize("kwargs,status,msg", [
     (dict(ab=float("nan")), INVALID, "ab_scale must be finite"),
     (dict(dt=F32), UNSUPPORTED, "fp16 or bf16"),
-    (dict(K=72), UNSUPPORTED, "multiples of 16"),
-    (dict(N=40), UNSUPPORTED, "multiples of 16"),
+    (dict(N=2), UNSUPPORTED, "N >= 3"),
+    (dict(N=1), UNSUPPORTED, "N >= 3"),
     (dict(A=A_P + 8), INVALID, "16-byte aligned"),
     (dict(A=None), INVALID, "A is NULL"),
     (dict(out=A_P + 64), INVALID, "out overlaps A"),
     (dict(act=GLU), INVALID, "the gate needs Y"),
-    (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5 and 12"),
     (dict(opt=fl.Options(0, 0, 15, 0, None)), UNSUPPORTED, "tile_cfg 15"),
-    (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2 and 5"),
+    (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5 and 12"),
     (dict(K=65536, N=32768), UNSUPPORTED, "B too large"),
 ])
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):

@@ -550,6 +550,7 @@ def test_quant_full_size_whole_output():
 # GEMM + Activation on CDNA4 with TLX", "Future Work": the projection in FP8).
 
 FP8_CODES = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}  # exact small integers in OCP E4M3
+FP8_CFGS = (0, 1, 2, 5, 12)  # automatic; 32x32x64 blocks (1, 2, 5); 16x16x128 blocks (12)
 
 
 def _run_fp8(d, act, out_dtype, **opts):
@@ -577,20 +578,45 @@ def _fp8_integer_inputs(M, N, K, out_dtype, act, seed):
 @pytest.mark.parametrize("shape", [(1, 16, 16), (67, 48, 64), (257, 272, 128), (513, 784, 160), (300, 528, 1008)])
 def test_fp8_integer_inputs_bit_exact(out_dtype, act, shape):
     """Small-integer E4M3 codes, a power-of-two scale: every product and sum is
-    exact in fp32, so the output must match bit for bit (this also pins the
-    operand k-order and the transposed 8-bit reads)."""
+    exact in fp32, so the output of every FP8 kernel (32x32x64 and 16x16x128
+    blocks) must match bit for bit (this also pins the operand k-order and the
+    transposed 8-bit reads)."""
     M, N, K = shape
     d = _fp8_integer_inputs(M, N, K, out_dtype, act, seed=M + N + K)
-    say("fp8 integer", out_dtype, act, shape)
-    out = _run_fp8(d, act, out_dtype)
     ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act, out_dtype=out_dtype)
-    bad = out.view(np.uint16) != ref.view(np.uint16)
-    assert not bad.any(), (np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
+    for cfg in FP8_CFGS:
+        say("fp8 integer", out_dtype, act, shape, "tile_cfg", cfg)
+        out = _run_fp8(d, act, out_dtype, tile_cfg=cfg)
+        bad = out.view(np.uint16) != ref.view(np.uint16)
+        assert not bad.any(), (cfg, np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "glu"])
+@pytest.mark.parametrize("shape", [(1, 3, 1), (7, 5, 2), (5, 17, 3), (67, 49, 65), (130, 131, 129), (257, 273, 131),
+                                   (300, 530, 1009), (513, 259, 127), (769, 21, 255)])
+def test_fp8_ragged_K_and_N_bit_exact(out_dtype, act, shape):
+    """K and N that are not multiples of 16 (rows of A and B not whole 16-byte
+    chunks, chunks that straddle rows, last dwords of A and B that run past
+    the buffers' ends): the last three codes of A and of B are forced to
+    nonzero values, so a code that the kernel reads as zero, or takes from
+    the next row, changes the output."""
+    M, N, K = shape
+    d = _fp8_integer_inputs(M, N, K, out_dtype, act, seed=7 * M + N + K)
+    A8, B8 = d["A8"].reshape(-1), d["B8"].reshape(-1)
+    A8[-min(3, A8.size):] = FP8_CODES[1]
+    B8[-min(3, B8.size):] = FP8_CODES[-2]
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act, out_dtype=out_dtype)
+    for cfg in FP8_CFGS:
+        say("fp8 ragged", out_dtype, act, shape, "tile_cfg", cfg)
+        out = _run_fp8(d, act, out_dtype, tile_cfg=cfg)
+        bad = out.view(np.uint16) != ref.view(np.uint16)
+        assert not bad.any(), (cfg, np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
 
 
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
-@pytest.mark.parametrize("shape", [(300, 528, 1008), (513, 272, 4096)])
+@pytest.mark.parametrize("shape", [(300, 528, 1008), (513, 272, 4096), (257, 1000, 1001)])
 def test_fp8_random_inputs_within_tolerance(out_dtype, act, shape):
     M, N, K = shape
     d = synth.draw_fp8(M, N, K, out_dtype, act, seed=23)
@@ -602,13 +628,16 @@ def test_fp8_random_inputs_within_tolerance(out_dtype, act, shape):
 
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
 def test_fp8_kernel_variants_bit_identical(out_dtype):
+    """Random inputs: the kernels of one MFMA family give the same bits, and
+    every one is within tolerance of the oracle."""
     d = synth.draw_fp8(513, 784, 1024, out_dtype, "relu", seed=24)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act="relu", out_dtype=out_dtype)
     outs = {}
-    for cfg in (0, 1, 2, 5):
+    for cfg in FP8_CFGS:
         say("fp8 variant", cfg, out_dtype)
         outs[cfg] = _run_fp8(d, "relu", out_dtype, tile_cfg=cfg)
-    for cfg, o in outs.items():
-        assert np.array_equal(o.view(np.uint16), outs[2].view(np.uint16)), cfg
+        _assert_close(outs[cfg], ref, out_dtype, f"fp8 tile_cfg {cfg}")
+    _same_family_bits(outs)
 
 
 @pytest.mark.parametrize("name", ["glu_fp8in_f16_1024x21568x4096", "relu_fp8in_f16_4096x4096x4096"])
