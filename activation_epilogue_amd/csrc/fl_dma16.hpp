@@ -134,7 +134,7 @@ struct Dma16 {
     static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
     static_assert(WAVES_N == 2 || WAVES_N == 4, "wave grid");
     static_assert(BN % (32 * WAVES_N) == 0, "whole 32-column MFMA blocks per wave");
-    static_assert(BN != 192 || !F8, "the 192-wide swizzle is for 16-bit B");
+    static_assert(BN != 192 || !F8 || !M16, "the 192-wide FP8 swizzle is for 32x32x64 blocks");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
     static constexpr int RBH = M16 ? 16 : 32;        // output rows of an accumulator block
@@ -231,6 +231,12 @@ struct Dma16 {
     // 128-byte rows (BN = 128) alternate between the two halves of the banks,
     // so fb = r % 8 (with the same bit-5 term) suffices: 4 rows of each half
     // x 2 chunks, or 8 rows of each half x 1 chunk, on 8 different chunks.
+    // 192-byte rows (BN = 192, 32x32x64 blocks only): row r starts 12*r
+    // chunk widths into the banks, so rows 0..3 start on the four quarters
+    // of the bank width and rows 4..7 again on the same ones; fb = 2 on rows
+    // 4..7 of every 8 moves their chunk pair (c, c+1) onto the other pair of
+    // its aligned group of four (an XOR below 4 keeps every chunk inside its
+    // row of 12), which leaves the 16 (row, chunk) pairs on 16 bank groups.
     //
     // 16-bit B, BN = 192: rows of 384 bytes, so odd rows already start half
     // a bank width (128 bytes) over; fb = r & 2 moves rows 2 and 3 of every
@@ -244,7 +250,9 @@ struct Dma16 {
     // rows 8..15 of every 16 by 2 chunks (4 for 192-wide rows), into the
     // bank groups rows 0..7 leave free.
     __device__ __forceinline__ static int fb(int r) {
-        if constexpr (F8)
+        if constexpr (F8 && BN == 192)
+            return (r >> 1) & 2;
+        else if constexpr (F8)
             return (BN == 256 ? (r & 7) << 1 : (r & 7)) ^ (M16 ? ((r >> 5) & 1) : 0);
         else if constexpr (BN == 192)
             return (r & 2) ^ (M16 ? ((r >> 1) & 4) : 0);

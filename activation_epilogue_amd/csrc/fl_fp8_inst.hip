@@ -39,6 +39,7 @@ fused_launcher pick_fp8_for<FL_INST_DTYPE>(int act, int variant) {
     case kDirect64x256: return pick_f8_act<DT, 256, 2>(act);
     case kDirect64x128: return pick_f8_act<DT, 128, 2>(act);
     case kDirect64x128M16: return pick_f8_act<DT, 128, 2, true>(act);
+    case kDirect64x192: return pick_f8_act<DT, 192, 2>(act);
     default: return nullptr;
     }
 }

@@ -285,7 +285,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (fp8_in) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
                                                      : fl::pick_fp8_for<FL_BF16>(act, t.variant);
-        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2, 5 and 12 only");
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2, 5, 7 and 12 only");
         f(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_fp8");
     }
@@ -435,18 +435,17 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (b_bytes >= 0x80000000ull) return fail(FL_ERR_UNSUPPORTED, "B too large (its K x N bytes must span < 2 GiB)");
     if (overlaps(out, o_bytes, A8, a_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps A");
     if (overlaps(out, o_bytes, B8, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
-    // The two-per-CU and 256x192 variants have no FP8 build: where the
-    // automatic choice names them, 256x128 runs.
     fl_options o = opt ? *opt : fl_options{};
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(FL_F16, M, N, K, &o, t);
-        // 32x32x64 blocks: the 8-wave 256x256 kernel where the forward
-        // choice is 256 wide, 256x128 elsewhere (no 192-wide or two-per-CU
-        // FP8 kernels).  The 16x16x128 kernel (256x128) is an option: as
-        // fast as the 32x32x64 one of the same tile, where 16-bit blocks of
-        // 16x16 gain from their lower power draw.
-        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 1 : 2;
+        // 32x32x64 blocks in the forward choice's tile: the 8-wave 256x256
+        // kernel, 256x192, or 256x128 (also where the 16-bit choice is the
+        // two-per-CU kernel, which has no FP8 build).  The 16x16x128 kernel
+        // (256x128) is an option: no faster than the 32x32x64 one of the
+        // same tile, where 16-bit blocks of 16x16 gain from their lower
+        // power draw.
+        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 5 : t.variant == fl::kDirect64x192M16 ? 7 : 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }

@@ -233,11 +233,12 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
  *             FL_ERR_UNSUPPORTED), conventions as fl_fused_linear.
  *   Any M and K; N of 1 or 2 is FL_ERR_UNSUPPORTED (rows of B of 1 or 2
  *             bytes), any other N is served.
- *   opt       tile_cfg 0 (automatic: the 8-wave 256x256 kernel, or 256x128
- *             where fl_fused_linear would use 128- or 192-wide tiles), 1, 2
- *             or 5 (32x32x64 blocks, bit-identical to one another) or 12
- *             (16x16x128 blocks, 256x128 tiles: the same products summed in
- *             another order); others are FL_ERR_UNSUPPORTED.
+ *   opt       tile_cfg 0 (automatic: the tile width fl_fused_linear would
+ *             use, 256, 192 or 128, with 32x32x64 blocks; 256x128 where it
+ *             would use the two-per-CU kernel), 1, 2, 5 or 7 (32x32x64
+ *             blocks, bit-identical to one another) or 12 (16x16x128 blocks,
+ *             256x128 tiles: the same products summed in another order);
+ *             others are FL_ERR_UNSUPPORTED.
  */
 fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               const void *bias, const void *Y, void *out,

@@ -550,7 +550,7 @@ def test_quant_full_size_whole_output():
 # GEMM + Activation on CDNA4 with TLX", "Future Work": the projection in FP8).
 
 FP8_CODES = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}  # exact small integers in OCP E4M3
-FP8_CFGS = (0, 1, 2, 5, 12)  # automatic; 32x32x64 blocks (1, 2, 5); 16x16x128 blocks (12)
+FP8_CFGS = (0, 1, 2, 5, 7, 12)  # automatic; 32x32x64 blocks (1, 2, 5, 7); 16x16x128 blocks (12)
 
 
 def _run_fp8(d, act, out_dtype, **opts):
