@@ -133,7 +133,7 @@ struct Dma16 {
     static_assert(BK * IES == 64 || BK * IES == 128, "stage depth: 64- or 128-byte A rows");
     static_assert(BN == 128 || BN == 192 || BN == 256, "tile width");
     static_assert(WAVES_N == 2 || WAVES_N == 4, "wave grid");
-    static_assert(BN % (32 * WAVES_N) == 0, "whole 32-column MFMA blocks per wave");
+    static_assert(BN % ((M16 ? 16 : 32) * WAVES_N) == 0, "whole MFMA blocks per wave");
     static_assert(BN != 192 || !F8 || !M16, "the 192-wide FP8 swizzle is for 32x32x64 blocks");
     static constexpr int WAVES = 2 * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WN = BN / WAVES_N;          // wave tile: 128 x WN
@@ -815,27 +815,45 @@ struct Dma16 {
         NBUF * BUF_BYTES > (SIDE2 ? 2 : 1) * EPI_BYTES ? NBUF * BUF_BYTES : (SIDE2 ? 2 : 1) * EPI_BYTES;
 
     // This wave's part of the staging area: its own 128 x WN tile, or in
-    // the shared layout BM / WAVES whole rows of the tile.  Rows are EPI_ROW
-    // bytes: the data and one 16-byte pad chunk, which is filled with zeros
-    // (lanes given kOob).  Rows past M and columns past N read zeros.
+    // the shared layout a run of the tile's 1 KB copies (the tile's staged
+    // rows are contiguous: BM * RC chunks, a whole number of copies; with 8
+    // waves on 192-wide rows the runs are 12 or 13 copies long).  Rows are
+    // EPI_ROW bytes: the data and one 16-byte pad chunk, which is filled
+    // with zeros (lanes given kOob).  Rows past M and columns past N read
+    // zeros.
     __device__ __forceinline__ static void stage_side(const GemmArgs &a, const void *src, int m0, int n0, int wave,
                                                       int wm, int wn, int lane, uint32_t lds_addr) {
         constexpr int RC = EPI_ROW / 16;  // 16-byte chunks per staged row, the last one padding
-        constexpr int YR = SHARED_EPI ? BM / WAVES : 128;
         constexpr int YW = SHARED_EPI ? BN : WN;
-        static_assert(EPI_ROW % 16 == 0 && RC == YW / 8 + 1 && (YR * RC) % 64 == 0, "whole copies of padded rows");
-        const int r0 = SHARED_EPI ? wave * YR : wm * 128, c0 = SHARED_EPI ? 0 : wn * WN;
-        const uint32_t base = __builtin_amdgcn_readfirstlane(
-            lds_addr + (SHARED_EPI ? (uint32_t)(r0 * EPI_ROW) : (uint32_t)(wave * EPI_WAVE)));
+        static_assert(EPI_ROW % 16 == 0 && RC == YW / 8 + 1, "padded rows of whole chunks");
         const size_t o_org = (size_t)m0 * a.N + n0;
         const i32x4_t rS = sgpr_rsrc(src ? static_cast<const char *>(src) + o_org * 2 : nullptr,
                                      src ? ((size_t)a.M * a.N - o_org) * 2 : 0);
+        if constexpr (SHARED_EPI) {
+            constexpr int COPIES = BM * RC / 64;
+            static_assert((BM * RC) % 64 == 0, "whole copies of the staged tile");
+            const int g0 = wave * COPIES / WAVES, g1 = (wave + 1) * COPIES / WAVES;
+            const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
 #pragma unroll
-        for (int j = 0; j < YR * RC / 64; ++j) {
-            const int q = 64 * j + lane, row = q / RC, c = q - row * RC;
-            const int col = c0 + c * 8;
-            const bool ok = c < RC - 1 && m0 + r0 + row < a.M && n0 + col < a.N;
-            lds_copy16(rS, ok ? (uint32_t)((r0 + row) * a.N + col) * 2 : kOob, 0, base + j * 1024);
+            for (int j = 0; j < (COPIES + WAVES - 1) / WAVES; ++j) {
+                const int g = g0 + j;
+                if (g < g1) {  // wave-uniform
+                    const int q = 64 * g + lane, row = q / RC, c = q - row * RC;
+                    const bool ok = c < RC - 1 && m0 + row < a.M && n0 + c * 8 < a.N;
+                    lds_copy16(rS, ok ? (uint32_t)(row * a.N + c * 8) * 2 : kOob, 0, base + g * 1024);
+                }
+            }
+        } else {
+            static_assert((128 * RC) % 64 == 0, "whole copies of padded rows");
+            const int r0 = wm * 128, c0 = wn * WN;
+            const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr + (uint32_t)(wave * EPI_WAVE));
+#pragma unroll
+            for (int j = 0; j < 128 * RC / 64; ++j) {
+                const int q = 64 * j + lane, row = q / RC, c = q - row * RC;
+                const int col = c0 + c * 8;
+                const bool ok = c < RC - 1 && m0 + r0 + row < a.M && n0 + col < a.N;
+                lds_copy16(rS, ok ? (uint32_t)((r0 + row) * a.N + col) * 2 : kOob, 0, base + j * 1024);
+            }
         }
     }
 

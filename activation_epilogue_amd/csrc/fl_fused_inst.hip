@@ -21,7 +21,8 @@ template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, bool RES, bool 
 void launch_dma(const GemmArgs &a, int grid, hipStream_t s) {
     if constexpr (DT != FL_F32)
         hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, RES, -1, DT, M16>),
-                           dim3(grid), dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
+                           dim3(grid), dim3(Dma16<DT, ACT, BK, BN, WAVES_N, 1, 1, false, -1, DT, false, M16>::THREADS),
+                           0, s, a);
 }
 
 template <int DT, int BK, int BN, int WAVES_N, int OCC, bool RES, bool M16>
@@ -58,6 +59,7 @@ fused_launcher pick_fused_for<FL_INST_DTYPE>(int act, bool vec, int variant, boo
         case kDirect64x128M16: return pick_dma<DT, 64, 128, 2, 1, true>(act, residual);
         case kDirect32x256M16: return pick_dma<DT, 32, 256, 2, 1, true>(act, residual);
         case kDirect32x256W8M16: return pick_dma<DT, 32, 256, 4, 1, true>(act, residual);
+        case kDirect64x192W8M16: return pick_dma<DT, 64, 192, 4, 1, true>(act, residual);
         default: break;
         }
     }

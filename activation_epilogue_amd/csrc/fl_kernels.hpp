@@ -783,6 +783,7 @@ enum Variant {
     kDirect64x128M16 = 12,    // Dma16 BK 64, 256x128, 4 waves, 16x16x32 MFMA blocks
     kDirect32x256M16 = 13,    // Dma16 BK 32 (five-stage ring), 256x256, 4 waves, 16x16x32 MFMA blocks
     kDirect32x256W8M16 = 14,  // Dma16 BK 32 (five-stage ring), 256x256, 8 waves, 16x16x32 MFMA blocks
+    kDirect64x192W8M16 = 15,  // Dma16 BK 64, 256x192, 8 waves (48 columns each), 16x16x32 MFMA blocks
 };
 
 // Returns the launcher of the fused kernel for (DT, act, variant, residual);

@@ -14,7 +14,8 @@ namespace {
 template <int DT, int ACT, int BK, int BN, int WAVES_N, int OCC, int QF, bool M16>
 void launch_q(const GemmArgs &a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((fused_linear_dma16_kernel<DT, ACT, BK, BN, WAVES_N, kCopySpread, OCC, false, QF, DT, M16>),
-                       dim3(grid), dim3(Dma16<DT, ACT, BK, BN, WAVES_N>::THREADS), 0, s, a);
+                       dim3(grid), dim3(Dma16<DT, ACT, BK, BN, WAVES_N, 1, 1, false, QF, DT, false, M16>::THREADS), 0,
+                       s, a);
 }
 
 template <int DT, int BK, int BN, int WAVES_N, int OCC, int QF, bool M16>
@@ -47,6 +48,7 @@ fused_launcher pick_quant_for<FL_INST_DTYPE>(int act, int variant, int qfmt) {
     case kDirect64x256W8M16: return pick_q<DT, 64, 256, 4, 1, true>(act, qfmt);
     case kDirect64x128M16: return pick_q<DT, 64, 128, 2, 1, true>(act, qfmt);
     case kDirect64x192M16: return pick_q<DT, 64, 192, 2, 1, true>(act, qfmt);
+    case kDirect64x192W8M16: return pick_q<DT, 64, 192, 4, 1, true>(act, qfmt);
     default: return nullptr;
     }
 }

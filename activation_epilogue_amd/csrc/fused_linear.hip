@@ -73,31 +73,30 @@ struct TileShape {
     int variant;  // fl::Variant
 };
 
-// Kernel and tile for a problem.  tile_cfg: 0 automatic, 1 256x256, 2 256x128
-// (fp16/bf16), 3 register-staged 256x256, 4 256x256 with 32-deep K stages
-// (fp16/bf16), 5 256x256 direct with 8 waves (fp16/bf16), 6 256x128 with
-// 32-deep K stages, two workgroups per CU (fp16/bf16), 7 and 8 256x192 with
-// 64- and 32-deep K stages (fp16/bf16).  fp32 always runs the
-// register-staged kernel.
-// Automatic fp16/bf16 choice: the width (256, 192 or 128) with the
-// smallest waves * relative time of a wave, a wave of 256x192 tiles taking
-// 0.79 and one of 256x128 tiles 0.55 of a 256x256 wave (measured at K =
-// 4096); ties go to the wider tile.  256 runs the 8-wave kernel (1.5-14%
-// faster than the 4-wave one on every measured shape).  192 wins where the
-// 256-wide grid leaves its last wave mostly empty and the 192-wide one
-// fills it (measured +3% on 1024x21568x4096, +6% on 4096x4608x4096, +10%
-// on 3072x12288x4096 over the best power-of-two width).  Then, when the
-// 256x128 grid fills both workgroup slots of every CU, short reductions
-// switch to the two-per-CU kernel, whose epilogues and start-ups overlap
-// the other workgroup's K loop: K <= 3072 where 256x128 was chosen
-// (measured +16% to +29% at K 256..1024, +4% at 3072, -2% at 4096 on
-// 1024x21568), K <= 2048 where 256x192 was (+2% at 2048, -3% at 3072), K
-// <= 512 where 256x256 was (+5% at 8192^2 x 512, -3% at 1024).
-constexpr int64_t kOcc2MaxK192 = 2048;
+// Kernel and tile for a problem (tile_cfg values as in fl_options).  fp32
+// always runs the register-staged kernel.
+// Automatic fp16/bf16 choice, all with 16x16x32 MFMA blocks: the width (256,
+// 192 or 128) with the smallest waves * relative time of a wave, a wave of
+// 256x192 tiles taking 0.79 and one of 256x128 tiles 0.55 of a 256x256 wave
+// (measured at K = 4096 with the 32x32 kernels); ties go to the wider tile.
+// 256 and 192 run 8-wave kernels (two waves per SIMD; 256: 1.5-14% faster
+// than 4 waves on every measured shape, 192: +10% at 1024x21568x4096 and
+// x3072).  192 wins where the 256-wide grid leaves its last wave mostly
+// empty and the 192-wide one fills it (measured +3% on 1024x21568x4096, +6%
+// on 4096x4608x4096, +10% on 3072x12288x4096 over the best power-of-two
+// width).  Then, when the 256x128 grid fills both workgroup slots of every
+// CU, short reductions switch to the two-per-CU kernel, whose epilogues and
+// start-ups overlap the other workgroup's K loop: K <= 3072 where 256x128
+// was chosen (measured +16% to +29% at K 256..1024, +4% at 3072, -2% at
+// 4096 on 1024x21568), K <= 1024 where 256x192 was (+2% at 1024, -1% at
+// 1280, -4% at 1536), K <= 256 where 256x256 was (+4% at 8192^2 x 256, -2%
+// to -7% at 384 and 512).
+constexpr int64_t kOcc2MaxK256 = 256;
+constexpr int64_t kOcc2MaxK192 = 1024;
 
 fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
-    if (cfg < 0 || cfg > 14) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
+    if (cfg < 0 || cfg > 15) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d is not available", cfg);
     if (dtype == FL_F32) {
         if (cfg == 2 || cfg == 6) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x128) is fp16/bf16 only", cfg);
         if (cfg == 7 || cfg == 8) return fail(FL_ERR_UNSUPPORTED, "tile_cfg %d (256x192) is fp16/bf16 only", cfg);
@@ -120,6 +119,7 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     case 12: t = {256, 128, fl::kDirect64x128M16}; return FL_OK;
     case 13: t = {256, 256, fl::kDirect32x256M16}; return FL_OK;
     case 14: t = {256, 256, fl::kDirect32x256W8M16}; return FL_OK;
+    case 15: t = {256, 192, fl::kDirect64x192W8M16}; return FL_OK;
     default: break;
     }
     const int64_t cus = cu_count();
@@ -129,21 +129,19 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     const int64_t c256 = waves(256) * 100, c192 = waves(192) * 79, c128 = waves(128) * 55;
     const int bn = (c256 <= c192 && c256 <= c128) ? 256 : (c192 <= c128 ? 192 : 128);
     const bool fills_two = tm * ((N + 127) / 128) >= 2 * cus;
-    if (fills_two && K <= (bn == 256 ? 512 : bn == 192 ? kOcc2MaxK192 : 3072))
+    if (fills_two && K <= (bn == 256 ? kOcc2MaxK256 : bn == 192 ? kOcc2MaxK192 : 3072))
         t = {256, 128, fl::kDirect32x128Occ2};
     else if (bn == 128)
         t = {256, 128, fl::kDirect64x128M16};
     else if (bn == 192)
-        t = {256, 192, fl::kDirect64x192M16};
+        t = {256, 192, fl::kDirect64x192W8M16};
     else
         t = {256, 256, fl::kDirect64x256W8M16};
     return FL_OK;
 }
 
-// The sibling with 32x32 MFMA blocks of a kernel variant (same tile, same
-// copies).  The quantized-output, FP8-operand and backward kernels are built
-// with 32x32 blocks only: where the automatic choice names a 16x16 kernel,
-// they run its sibling.
+// The sibling with 32x32 MFMA blocks of a kernel variant (the same tile):
+// the FP8-operand and backward entry points choose their kernel by it.
 int family32(int v) {
     switch (v) {
     case fl::kDirect64x256M16: return fl::kDirect64x256;
@@ -151,6 +149,7 @@ int family32(int v) {
     case fl::kDirect32x256M16: return fl::kDirect32x256;
     case fl::kDirect32x256W8M16: return fl::kDirect64x256W8;
     case fl::kDirect64x192M16: return fl::kDirect64x192;
+    case fl::kDirect64x192W8M16: return fl::kDirect64x192;
     case fl::kDirect64x128M16: return fl::kDirect64x128;
     default: return v;
     }
@@ -292,7 +291,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (qfmt >= 0) {
         const fl::fused_launcher q = dtype == FL_F16 ? fl::pick_quant_for<FL_F16>(act, t.variant, qfmt)
                                                      : fl::pick_quant_for<FL_BF16>(act, t.variant, qfmt);
-        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12 only");
+        if (!q) return fail(FL_ERR_UNSUPPORTED, "quantized output is built for tile_cfg 0, 2, 5, 6, 7, 10, 11, 12 and 15 only");
         q(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_quant");
     }
@@ -309,12 +308,15 @@ __global__ void zero_f32_kernel(float *p, int64_t n) {
 }
 
 // The tile choice of the transposed-B kernels: the 8-wave 256x256 kernel
-// where the forward choice is 256x256, else 256x128.
+// with 16x16x32 blocks where the forward choice is 256x256, else 256x128
+// with 32x32x16 blocks (16% faster there than its 16x16 sibling, whose
+// accumulators the compiler moves between registers in the K loop:
+// measured on the gate's backward, 1024x21568x4096).
 fl_options bwd_tiles(int dtype, int64_t M, int64_t N, int64_t K) {
     fl_options o{};
     TileShape t;
     tile_shape(dtype, M, N, K, &o, t);
-    o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 12;
+    o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 2;
     return o;
 }
 
@@ -445,7 +447,7 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
         // (256x128) is an option: no faster than the 32x32x64 one of the
         // same tile, where 16-bit blocks of 16x16 gain from their lower
         // power draw.
-        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 5 : t.variant == fl::kDirect64x192M16 ? 7 : 2;
+        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 5 : family32(t.variant) == fl::kDirect64x192 ? 7 : 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }
@@ -489,7 +491,7 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     if (o.tile_cfg == 0) {
         TileShape t;
         tile_shape(dtype, M, N, K, &o, t);
-        o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 12;
+        o.tile_cfg = family32(t.variant) == fl::kDirect64x256W8 ? 10 : 2;
     } else if (o.tile_cfg != 2 && o.tile_cfg != 5 && o.tile_cfg != 10 && o.tile_cfg != 12) {
         return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2, 5, 10 and 12 only");
     }

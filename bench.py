@@ -323,9 +323,9 @@ def main():
         opts["tile_cfg"] = args.tile_cfg
     code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **opts)
-    if (w.in8 or w.bwd) and not args.tile_cfg and bn != 256:
-        # the FP8 and backward entry points run 256x128 where the automatic
-        # choice names the two-per-CU or the 256x192 kernel (not built there)
+    if w.bwd and not args.tile_cfg and bn != 256:
+        # the backward entry point runs 256x128 where the automatic choice
+        # names the two-per-CU or the 256x192 kernel (not built there)
         bm, bn, tiles_m, tiles_n = fl.tile_grid(w.M, w.N, w.K, code, **dict(opts, tile_cfg=2))
     kernel = ("fused_linear_bwd_kernel" if w.bwd else
               "fused_linear_kernel" if (w.dtype == "f32" or args.tile_cfg == 3) else "fused_linear_dma16_kernel")

@@ -101,16 +101,15 @@ typedef struct {
     int32_t tile_cfg;   /* Kernel and tile.  0 = automatic: fp32 runs the
                            register-staged 256x256 kernel; fp16/bf16 run the
                            direct-to-LDS kernel with 16x16x32 MFMA blocks and
-                           256x256 tiles (8 waves, as 10), 256x192 (as 11) or
-                           256x128 (as 12), whichever takes the fewest waves
-                           x relative wave time on this GPU's compute units;
-                           short reductions (K <= 3072 for a 256x128 choice,
-                           K <= 2048 for 256x192, K <= 512 for 256x256)
-                           whose 256x128 grid fills two workgroups per
-                           compute unit run as 6.  The quantized-output,
-                           FP8-operand and backward entry points, which are
-                           built with 32x32 blocks only, run the 32x32
-                           sibling of that choice (5, 7 or 2).
+                           256x256 tiles (8 waves, as 10), 256x192 (8 waves,
+                           as 15) or 256x128 (as 12), whichever takes the
+                           fewest waves x relative wave time on this GPU's
+                           compute units; short reductions (K <= 3072 for a
+                           256x128 choice, K <= 1024 for 256x192, K <= 256
+                           for 256x256) whose 256x128 grid fills two
+                           workgroups per compute unit run as 6.  The
+                           quantized-output, FP8-operand and backward entry
+                           points state their own automatic choices.
                            Variants with 32x32x16 MFMA blocks: 1 = 256x256
                            direct, 4 waves (fp16/bf16; fp32 as 0); 2 =
                            256x128 direct (fp16/bf16 only); 3 =
@@ -124,15 +123,16 @@ typedef struct {
                            of 128x96) with 64- and 32-deep K stages
                            (fp16/bf16 only).  Variants with 16x16x32 MFMA
                            blocks (fp16/bf16 only): 9 = 256x256, 4 waves;
-                           10 = 256x256, 8 waves; 11 = 256x192; 12 =
+                           10 = 256x256, 8 waves; 11 = 256x192, 4 waves; 12 =
                            256x128; 13 and 14 = 256x256 with 4 and 8 waves
-                           and 32-deep K stages in a five-stage ring.  All
-                           variants of one MFMA shape give bit-identical
-                           results; the two shapes sum each output in a
-                           different order (both within the stated
-                           tolerance, and equal wherever the arithmetic is
-                           exact).  Any other value, or a variant the
-                           problem does not allow, is FL_ERR_UNSUPPORTED. */
+                           and 32-deep K stages in a five-stage ring; 15 =
+                           256x192, 8 waves (128x48 each).  All variants of
+                           one MFMA shape give bit-identical results; the
+                           two shapes sum each output in a different order
+                           (both within the stated tolerance, and equal
+                           wherever the arithmetic is exact).  Any other
+                           value, or a variant the problem does not allow,
+                           is FL_ERR_UNSUPPORTED. */
     int32_t no_xcd_remap; /* 0 = place neighbouring tiles on one XCD; 1 = off */
     uint32_t *debug_tile_count; /* NULL, or a device array of tiles_m*tiles_n
                            counters (see fl_tile_grid); each output tile adds
@@ -205,9 +205,9 @@ fl_status fl_fused_linear_residual(const void *A, const void *B,
  *          A, B, bias or Y.
  *   scale  finite fp32 (a per-tensor output scale).
  *   dtype  FL_F16 or FL_BF16 (FL_F32 inputs are FL_ERR_UNSUPPORTED).
- *   opt    as fl_fused_linear_ex, with tile_cfg 0, 2, 5, 6, 7, 10, 11 or 12 (the
- *          kernels the automatic choice uses); other values are
- *          FL_ERR_UNSUPPORTED.
+ *   opt    as fl_fused_linear_ex, with tile_cfg 0 (the automatic choice of
+ *          fl_fused_linear_ex), 2, 5, 6, 7, 10, 11, 12 or 15; other values
+ *          are FL_ERR_UNSUPPORTED.
  * Errors as fl_fused_linear_ex; an unknown qfmt or a non-finite scale is
  * FL_ERR_INVALID_ARG.
  */
@@ -273,9 +273,10 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
  *          not fixed); dX and dY are deterministic.
  *   dtype  FL_F16 or FL_BF16 (FL_F32 is FL_ERR_UNSUPPORTED).
  *   opt    tile_cfg 0 (automatic: the 8-wave 256x256 kernel with 16x16x32
- *          MFMA blocks where the forward choice is 256 wide, its 256x128
- *          sibling elsewhere), 10 and 12 (those two), or 5 and 2 (the same
- *          tiles with 32x32x16 blocks); others are FL_ERR_UNSUPPORTED.
+ *          MFMA blocks (10) where the forward choice is 256 wide, 256x128
+ *          with 32x32x16 blocks (2) elsewhere), 10 and 12 (16x16x32
+ *          blocks), or 5 and 2 (32x32x16 blocks); others are
+ *          FL_ERR_UNSUPPORTED.
  *          group_m, persistent and no_xcd_remap as for fl_fused_linear_ex.
  * Alignment, sizes and errors as fl_fused_linear_ex; M = 0 or N = 0 writes
  * nothing but a zero dbias; K = 0 gives zeros.

@@ -113,7 +113,8 @@ def test_tile_grid(lib):
     assert fl.tile_grid(8192, 14336, 4096, BF16) == (256, 256, 32, 56)
     assert fl.tile_grid(1024, 21568, 4096, F16) == (256, 192, 4, 113)
     assert fl.tile_grid(4096, 4608, 4096, F16) == (256, 192, 16, 24)
-    assert fl.tile_grid(1024, 21568, 2048, F16) == (256, 128, 4, 169)  # two per CU
+    assert fl.tile_grid(1024, 21568, 1024, F16) == (256, 128, 4, 169)  # two per CU
+    assert fl.tile_grid(1024, 21568, 1280, F16) == (256, 192, 4, 113)
     assert fl.tile_grid(1024, 21568, 3072, F16) == (256, 192, 4, 113)
     assert fl.tile_grid(127, 129, 96, F16) == (256, 128, 1, 2)
     assert fl.tile_grid(127, 129, 96, F32) == (256, 256, 1, 1)
@@ -125,8 +126,8 @@ def test_tile_grid(lib):
     assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=6) == (256, 128, 16, 32)
     # short reductions whose 256x128 grid fills two workgroups per CU
     assert fl.tile_grid(1024, 21568, 256, F16) == (256, 128, 4, 169)
-    assert fl.tile_grid(8192, 8192, 512, F16) == (256, 128, 32, 64)
-    assert fl.tile_grid(8192, 8192, 1024, F16) == (256, 256, 32, 32)
+    assert fl.tile_grid(8192, 8192, 256, F16) == (256, 128, 32, 64)
+    assert fl.tile_grid(8192, 8192, 384, F16) == (256, 256, 32, 32)
     with pytest.raises(fl.FusedLinearError):
         fl.tile_grid(64, 64, 64, F32, tile_cfg=6)
     # 256x192 tiles (192 = 3*64, not a power of two): N = 21568 = 112*192 + 64
@@ -142,11 +143,12 @@ def test_tile_grid(lib):
     assert fl.tile_grid(4097, 3071, 1537, BF16, tile_cfg=12) == (256, 128, 17, 24)
     assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=13) == (256, 256, 16, 16)
     assert fl.tile_grid(4096, 4096, 4096, F16, tile_cfg=14) == (256, 256, 16, 16)
-    for cfg in (9, 10, 11, 12, 13, 14):
+    assert fl.tile_grid(1024, 21568, 4096, F16, tile_cfg=15) == (256, 192, 4, 113)
+    for cfg in (9, 10, 11, 12, 13, 14, 15):
         with pytest.raises(fl.FusedLinearError):
             fl.tile_grid(64, 64, 64, F32, tile_cfg=cfg)
     with pytest.raises(fl.FusedLinearError):
-        fl.tile_grid(64, 64, 64, F16, tile_cfg=15)
+        fl.tile_grid(64, 64, 64, F16, tile_cfg=16)
 
 
 def test_host_tile_map_matches_oracle_without_xcd_step(lib):
@@ -210,8 +212,8 @@ def _quant(lib, out=OUT_P, scale=1.0, q=0, dt=F16, act=RELU, Y=None, opt=None, M
     (dict(out=None), INVALID, "out is NULL"),
     (dict(out=A_P + 100), INVALID, "out overlaps A"),
     (dict(act=GLU, Y=Y_P, out=Y_P + 8191), INVALID, "out overlaps Y"),
-    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12"),
-    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11 and 12"),
+    (dict(opt=fl.Options(0, 0, 1, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11, 12 and 15"),
+    (dict(opt=fl.Options(0, 0, 3, 0, None)), UNSUPPORTED, "tile_cfg 0, 2, 5, 6, 7, 10, 11, 12 and 15"),
 ])
 def test_quant_rejects_bad_arguments(lib, kwargs, status, msg):
     assert _quant(lib, **kwargs) == status
@@ -238,7 +240,7 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
     (dict(out=A_P + 64), INVALID, "out overlaps A"),
     (dict(act=GLU), INVALID, "the gate needs Y"),
     (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 7 and 12"),
-    (dict(opt=fl.Options(0, 0, 15, 0, None)), UNSUPPORTED, "tile_cfg 15"),
+    (dict(opt=fl.Options(0, 0, 16, 0, None)), UNSUPPORTED, "tile_cfg 16"),
     (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 7 and 12"),
     (dict(K=65536, N=32768), UNSUPPORTED, "B too large"),
 ])

@@ -283,7 +283,7 @@ def test_npot_tiles_full_gate_shape(cfg):
     _assert_close(h, ref, w.dtype, f"{w.name} tile_cfg {cfg}")
 
 
-@pytest.mark.parametrize("cfg", [0, 2, 3, 5, 6, 7, 9, 10, 11, 12, 14])
+@pytest.mark.parametrize("cfg", [0, 2, 3, 5, 6, 7, 9, 10, 11, 12, 14, 15])
 @pytest.mark.parametrize("dtype,act,shape", [("f16", "relu", (1024, 2048, 1024)), ("bf16", "glu", (513, 770, 1537)),
                                              ("f32", "relu", (300, 260, 200))])
 def test_debug_sync_gives_the_same_bits(cfg, dtype, act, shape):
@@ -342,7 +342,7 @@ def test_y_may_alias_out():
 # (v_mfma_f32_32x32x16) or in 16x16 blocks 32 deep (v_mfma_f32_16x16x32):
 # bit-identical within a family.
 FAMILY_32 = [1, 2, 3, 4, 5, 6, 7, 8]
-FAMILY_16 = [9, 10, 11, 12, 13, 14]
+FAMILY_16 = [9, 10, 11, 12, 13, 14, 15]
 
 
 def _same_family_bits(outs):
@@ -522,14 +522,14 @@ def test_quant_kernel_variants_identical(dtype, qfmt):
     ref, u = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], None, act="relu", dtype=dtype, qfmt=qfmt,
                                        scale=50.0, want_u=True)
     outs = {}
-    for cfg in (0, 2, 5, 6, 7, 10, 11, 12):
+    for cfg in (0, 2, 5, 6, 7, 10, 11, 12, 15):
         say("quant variant", cfg, dtype, qfmt)
         outs[cfg] = _run_quant(d, "relu", dtype, qfmt, 50.0, tile_cfg=cfg)
         res = oracle.compare_quant(outs[cfg], ref, u, qfmt)
         assert res["ok"], (cfg, res)
     for cfg in (5, 6, 7):  # 32x32 blocks
         assert np.array_equal(outs[cfg], outs[2]), cfg
-    for cfg in (11, 12):  # 16x16 blocks
+    for cfg in (11, 12, 15):  # 16x16 blocks
         assert np.array_equal(outs[cfg], outs[10]), cfg
     assert np.array_equal(outs[0], outs[10]) or np.array_equal(outs[0], outs[2])
 
@@ -865,7 +865,7 @@ def _first_cols(d, n, keys_cols, keys_rows=()):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act,residual", [("glu", False), ("relu", True), ("gelu_tanh", True), ("glu", True)])
-@pytest.mark.parametrize("cfg", [0, 5, 6, 7, 10, 11, 13, 14])
+@pytest.mark.parametrize("cfg", [0, 5, 6, 7, 10, 11, 13, 14, 15])
 def test_side_input_paths_bit_identical(dtype, act, residual, cfg):
     M, K = 300, 200
     d = synth.draw(M, 521, K, dtype, act, seed=43)
@@ -917,7 +917,7 @@ def _rne_bf16_bits(x32):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["none", "relu"])
 @pytest.mark.parametrize("N", [520, 521])
-@pytest.mark.parametrize("cfg", [0, 3, 5, 6, 7, 9, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("cfg", [0, 3, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15])
 def test_k1_output_rounding_bit_exact(dtype, act, N, cfg):
     M = 300
     rng = np.random.default_rng(N + 7 * cfg)
