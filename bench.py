@@ -14,6 +14,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -46,6 +47,9 @@ def parse():
     p.add_argument("--group-m", type=int, default=0)
     p.add_argument("--persistent", type=int, default=0)
     p.add_argument("--tile-cfg", type=int, default=0, help="fl_options.tile_cfg (0 = automatic)")
+    p.add_argument("--shape", default="",
+                   help="MxNxK: the workload's kind and data recipe at another size (a study, not a bench line "
+                        "of the named workload)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -291,6 +295,9 @@ def main():
         sys.exit(1)
     fl.load_library()
     w = synth.WORKLOADS[args.workload]
+    if args.shape:
+        M, N, K = (int(x) for x in args.shape.split("x"))
+        w = dataclasses.replace(w, name=f"{w.name}@{M}x{N}x{K}", M=M, N=N, K=K)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     d = synth.draw_workload(w)
 
