@@ -186,8 +186,12 @@ struct Dma16 {
     // one (32 deep), and all its copies go out in the block after the
     // barrier that frees their buffer: the copies of the second half would
     // otherwise have half a stage less to land (measured 1219 -> 1279
-    // TFLOP/s at 4096^3 together with the read placement below).
-    static constexpr int SPR = M16 ? 1 : SPREAD < KK ? SPREAD : KK;
+    // TFLOP/s at 4096^3 together with the read placement below).  FP8
+    // stages take half the MFMA time of 16-bit ones, and the 256- and
+    // 192-wide FP8 kernels issue their copies in one block too (+3% at
+    // 4096^3, +7% on 1024x21568x4096); the 256x128 one, with three
+    // buffers, keeps two (-2% in one).
+    static constexpr int SPR = (M16 || (F8 && BN != 128)) ? 1 : SPREAD < KK ? SPREAD : KK;
     static_assert(SPREAD >= 1, "copies spread over one block at least");
     // Copies [part_lo(p), part_lo(p+1)) of a stage form part p.
     static constexpr int part_lo(int p) { return p * DMA_PER_WAVE / SPR; }
@@ -607,13 +611,15 @@ struct Dma16 {
         }
     }
 
-    // MFMA I of a block.  16x16 blocks run the rows of blocks in snake
-    // order (odd rows right to left), so that consecutive MFMAs always share
-    // one operand: fewer operand bits toggle, which lowers the matrix cores'
-    // power and lets the chip hold a higher clock (+1-2% measured).
+    // MFMA I of a block.  16x16 blocks and FP8 run the rows of blocks in
+    // snake order (odd rows right to left), so that consecutive MFMAs always
+    // share one operand: fewer operand bits toggle, which lowers the matrix
+    // cores' power and lets the chip hold a higher clock (+1-2% measured
+    // with 16x16 blocks, +0.5% with FP8).  The order of the MFMAs of one
+    // output block, and so every result bit, is unchanged.
     template <int I>
     __device__ __forceinline__ static void mma_one(const Frags &f, acc_t (&acc)[NRB][NI]) {
-        constexpr int mi = I / NI, ni = (M16 && (mi & 1)) ? NI - 1 - I % NI : I % NI;
+        constexpr int mi = I / NI, ni = ((M16 || F8) && (mi & 1)) ? NI - 1 - I % NI : I % NI;
         if constexpr (F8) {
             const i32x4_t b01 = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3);
             const i32x4_t b23 = __builtin_shufflevector(f.b[ni][2], f.b[ni][3], 0, 1, 2, 3);
