@@ -1,31 +1,34 @@
-// fl_dma16.hpp -- fp16/bf16 fused GEMM with direct-to-LDS loads.
+// fl_dma16.hpp -- the fused GEMM with direct-to-LDS loads: fp16/bf16 (or
+// FP8 E4M3) operands, fp32 accumulation, the fused epilogue.
 //
 // Same contract and epilogue as FusedTile (fl_kernels.hpp); this variant
-// serves every fp16/bf16 problem.  Pointers need only element alignment:
-// 16-byte buffer loads and the 8-byte epilogue accesses may be unaligned on
-// gfx950.  With N % 8 != 0 (16 for FP8 codes) a B chunk that crosses N
-// brings in the next row's first values, which only reach output columns
-// >= N (never stored); with K % 8 != 0 (16) the straddling A chunk is zeroed
-// in LDS (fix_k_tail) and B's rows >= K are read as zeros.  Differences from the register-staged kernel:
+// serves every fp16/bf16 and FP8-operand problem.  Pointers need only
+// element alignment: 16-byte buffer loads and the 8-byte epilogue accesses
+// may be unaligned on gfx950.  With N % 8 != 0 (16 for FP8 codes) a B chunk
+// that crosses N brings in the next row's first values, which only reach
+// output columns >= N (never stored); with K % 8 != 0 (16) the straddling A
+// chunk is masked in LDS (fix_k_tail) and B's rows >= K are read as zeros.
+// Differences from the register-staged kernel:
 //
 //   * Global -> LDS copies use buffer_load_dwordx4 with the LDS bit: each
 //     instruction moves 64 x 16 bytes straight into 1 KB of LDS at
 //     M0 + lane*16, so no staging registers, no ds_write and no VALU
 //     transposes.  The XOR swizzle is applied on the global side: lane l of
 //     an instruction fetches the chunk that belongs at LDS position l.
-//   * B stays N-contiguous in LDS ([k][n] rows of 512 bytes) and its MFMA
-//     operand is read with ds_read_b64_tr_b16: within each 16-lane group,
-//     lane i receives element 16*j + i (j = 0..3) of the group's lane-major
-//     64 values, so 16 lanes that point at 4 k-rows x 16 columns (4 columns
-//     per lane) receive one column each with 4 consecutive k values -- the
-//     K-contiguous B operand of v_mfma_f32_32x32x16_{f16,bf16}.
-//   * A K stage of BK values (BK = 64: A rows are whole 128-byte lines)
-//     occupies one of NBUF LDS buffers (NBUF * BK KB = 128 KB).  The copies
-//     of a stage are issued right after the barrier that frees its buffer,
-//     so NBUF-1 stages are in flight while MFMAs run ("Optimizing GEMM +
-//     Activation on CDNA4 with TLX", "Version 3": a deeper buffer ring lets
-//     the wait keep loads in flight instead of draining them).
-//   * Each stage is BK/16 blocks of 16 MFMAs; the operand reads of the next
+//   * B stays N-contiguous in LDS ([k][n] rows) and its MFMA operand is read
+//     with ds_read_b64_tr_b16 (or _tr_b8 for FP8): within each 16-lane
+//     group, lane i receives element 16*j + i (j = 0..3) of the group's
+//     lane-major 64 values, so 16 lanes that point at 4 k-rows x 16 columns
+//     (4 columns per lane) receive one column each with 4 consecutive k
+//     values -- the K-contiguous B operand of the MFMA.
+//   * A K stage of BK values (64 for 16-bit operands, 128 for FP8: A rows
+//     are whole 128-byte lines; or 32) occupies one of NBUF LDS buffers.
+//     The copies of a stage are issued right after the barrier that frees
+//     its buffer, so NBUF-1 stages are in flight while MFMAs run
+//     ("Optimizing GEMM + Activation on CDNA4 with TLX", "Version 3": a
+//     deeper buffer ring lets the wait keep loads in flight instead of
+//     draining them).
+//   * Each stage is BK/KPM blocks of MFMAs; the operand reads of the next
 //     block are slotted between the MFMAs of the current one, and the one
 //     barrier per stage sits before the last block, whose MFMA slots also
 //     carry the copies of the stage NBUF ahead.
@@ -115,10 +118,11 @@ __device__ __forceinline__ uint32_t load_u8_now(i32x4_t rsrc, uint32_t voffset) 
 // staged and read exactly like A's, and a lane's 16-byte read of a row is
 // already the MFMA's B fragment (8 consecutive k of one column).  M16:
 // the product runs as 16x16 output blocks 32 deep (v_mfma_f32_16x16x32_
-// {f16,bf16}) instead of 32x32 blocks 16 deep; same flops per operand read
-// from LDS for the wave's tile, but on random data the matrix cores hold a
-// higher clock under the 16x16 form (measured with operands in registers:
-// 1838 against 1645 TFLOP/s, 2.29 against 2.01 GHz, 8 waves per CU).
+// {f16,bf16}; FP8: 16x16x128) instead of 32x32 blocks 16 deep (32x32x64);
+// same flops per operand read from LDS for the wave's tile, but on random
+// data the matrix cores hold a higher clock under the 16x16 form (measured
+// with operands in registers: 1838 against 1645 TFLOP/s, 2.29 against 2.01
+// GHz, 8 waves per CU).
 template <int DT, int ACT, int BK_, int BN_ = 256, int WAVES_N = 2, int SPREAD = 1, int OCC = 1, bool RES = false,
           int QF = -1, int IN = DT, bool BWD = false, bool M16 = false>
 struct Dma16 {

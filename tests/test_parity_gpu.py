@@ -259,13 +259,14 @@ def test_tile_order_does_not_change_bits(name):
             assert np.array_equal(h, base), opts
 
 
-@pytest.mark.parametrize("cfg", [7, 8])
-def test_npot_tiles_full_gate_shape(cfg):
+@pytest.mark.parametrize("cfg,cfg256", [(7, 1), (8, 1), (11, 10), (15, 10)])
+def test_npot_tiles_full_gate_shape(cfg, cfg256):
     """256x192 tiles (a width that is not a power of two; "Optimizing GEMM +
     Activation on CDNA4 with TLX", "Future Work") on the gate workload
     M=1024, N=21568, K=4096: 4 x 113 tiles, the last column of tiles 64
     wide.  Each tile is written exactly once, the whole output matches the
-    oracle and is bit-identical to the 256x256 kernel's."""
+    oracle and is bit-identical to the 256x256 kernel's of the same MFMA
+    shape (32x32x16: 7, 8; 16x16x32: 11, 15)."""
     w = synth.WORKLOADS["glu_f16_1024x21568x4096"]
     d = synth.draw_workload(w)
     A, B, bias, Y = (to_dev(d[k], w.dtype) for k in ("A", "B", "bias", "Y"))
@@ -274,7 +275,7 @@ def test_npot_tiles_full_gate_shape(cfg):
     say("npot full", cfg)
     counts = torch.zeros(tm * tn, dtype=torch.int32, device="cuda")
     out = fl.fused_linear(A, B, bias, Y, act=w.act, tile_cfg=cfg, debug_tile_count=counts)
-    ref256 = fl.fused_linear(A, B, bias, Y, act=w.act, tile_cfg=1)
+    ref256 = fl.fused_linear(A, B, bias, Y, act=w.act, tile_cfg=cfg256)
     torch.cuda.synchronize()
     assert bool((counts == 1).all().item())
     h = to_host(out, w.dtype)
