@@ -47,10 +47,13 @@
  *              and the whole of B (K*N elements; not the transposed operand
  *              of the backward entries) must each span less than 2 GiB, else
  *              FL_ERR_UNSUPPORTED.
- *   Alignment  Pointers must be aligned to the element size.  16-byte aligned
- *              pointers with K and N multiples of 16 bytes / element size take
- *              the vector-load path; everything else takes the element path.
- *              Both produce the same results.
+ *   Alignment  Pointers must be aligned to the element size.  The
+ *              direct-to-LDS kernels (fp16/bf16, FP8 operands) take any such
+ *              pointers and any K and N with the same code.  The
+ *              register-staged kernel (fp32, tile_cfg 3) takes its
+ *              vector-load path for 16-byte aligned pointers with K and N
+ *              multiples of 16 bytes / element size, its element path
+ *              otherwise; both produce the same results.
  *   Errors     Arguments are validated before any HIP call; a bad argument
  *              returns FL_ERR_INVALID_ARG (or FL_ERR_UNSUPPORTED for a
  *              well-formed request the library does not implement) with no
