@@ -616,6 +616,31 @@ def test_fp8_ragged_K_and_N_bit_exact(out_dtype, act, shape):
 
 
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
+def test_fp8_k0_and_empty(out_dtype, act):
+    """K = 0 at 127 x 129: act(bias) on every row, from every FP8 kernel; M = 0
+    or N = 0 launches nothing and writes nothing."""
+    d = _fp8_integer_inputs(127, 129, 0, out_dtype, act, seed=3)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act, out_dtype=out_dtype)
+    for cfg in FP8_CFGS:
+        say("fp8 K=0", out_dtype, act, "tile_cfg", cfg)
+        out = _run_fp8(d, act, out_dtype, tile_cfg=cfg)
+        _assert_close(out, ref, out_dtype, f"fp8 K=0 {act} tile_cfg {cfg}")
+        if act == "relu":
+            assert np.array_equal(out.view(np.uint16), ref.view(np.uint16)), cfg
+    tdt = TORCH_DT[out_dtype]
+    for M, N in ((0, 129), (127, 0)):
+        A8 = torch.zeros((M, 64), dtype=torch.uint8, device="cuda")
+        B8 = torch.zeros((64, N), dtype=torch.uint8, device="cuda")
+        bias = torch.zeros((N,), dtype=tdt, device="cuda")
+        Y = torch.zeros((M, N), dtype=tdt, device="cuda") if act == "glu" else None
+        out = torch.full((M, N), 7.0, dtype=tdt, device="cuda")
+        fl.fused_linear_fp8(A8, B8, 1.0, bias, Y, act=act, out_dtype=tdt, out=out)
+        torch.cuda.synchronize()
+        assert out.numel() == 0
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
 @pytest.mark.parametrize("shape", [(300, 528, 1008), (513, 272, 4096), (257, 1000, 1001)])
 def test_fp8_random_inputs_within_tolerance(out_dtype, act, shape):
