@@ -164,10 +164,12 @@ fl_status fl_fused_linear(const void *A, const void *B, const void *bias,
                           int64_t K, fl_act act, fl_dtype dtype, void *stream);
 
 /* As fl_fused_linear, with explicit options (opt may be NULL = defaults).
- * Results are bitwise identical for every group_m, persistent and
- * no_xcd_remap setting: they change which workgroup computes a tile, never
- * the arithmetic of the tile; every tile_cfg sums each output in the same
- * order too, so results are bit-identical across all options. */
+ * Results are bitwise identical for every group_m, persistent,
+ * no_xcd_remap and debug_sync setting: they change which workgroup computes
+ * a tile, or when, never the arithmetic of the tile.  The tile_cfg variants
+ * of one MFMA shape sum each output in the same order and give the same
+ * bits; the 32x32x16 and 16x16x32 shapes sum in different orders (see
+ * tile_cfg). */
 fl_status fl_fused_linear_ex(const void *A, const void *B, const void *bias,
                              const void *Y, void *out, int64_t M, int64_t N,
                              int64_t K, fl_act act, fl_dtype dtype,
