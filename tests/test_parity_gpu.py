@@ -615,6 +615,18 @@ def test_fp8_ragged_K_and_N_bit_exact(out_dtype, act, shape):
         assert not bad.any(), (cfg, np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 5, 7, 12])
+def test_fp8_debug_sync_gives_the_same_bits(cfg):
+    """The FP8 kernels under the debugging schedule (an extra full wait for
+    the copies and an extra barrier in every K stage), on a ragged shape
+    whose last stage is fixed up: the same bits."""
+    d = synth.draw_fp8(513, 781, 1001, "f16", "glu", seed=63)
+    say("fp8 debug sync", cfg)
+    fast = _run_fp8(d, "glu", "f16", tile_cfg=cfg)
+    slow = _run_fp8(d, "glu", "f16", tile_cfg=cfg, debug_sync=1)
+    assert np.array_equal(fast.view(np.uint16), slow.view(np.uint16))
+
+
 @pytest.mark.parametrize("out_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("act", ["relu", "gelu_tanh", "glu"])
 def test_fp8_k0_and_empty(out_dtype, act):
