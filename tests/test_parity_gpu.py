@@ -104,6 +104,32 @@ def test_k0_gives_act_of_bias(dtype, act, shape):
     _assert_close(out, ref, dtype, f"K=0 {act}")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_seeded_random_shapes(seed):
+    """Seeded random shapes (ragged M, N and K up to a few hundred, every
+    activation and dtype, a residual now and then) through the automatic
+    choice and through one random kernel variant of the dtype: the whole
+    output against the oracle, and the variant bit-identical to the
+    automatic choice wherever both use the same MFMA shape."""
+    rng = np.random.default_rng(1000 + seed)
+    for case in range(8):
+        M, N, K = (int(rng.integers(1, 700)) for _ in range(3))
+        dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+        act = ["none", "relu", "gelu_tanh", "glu"][int(rng.integers(0, 4))]
+        residual = bool(rng.integers(0, 4) == 0)
+        cfgs = [3] if dtype == "f32" else FAMILY_32 + FAMILY_16
+        cfg = cfgs[int(rng.integers(0, len(cfgs)))]
+        d = synth.draw(M, N, K, dtype, act, seed=seed * 8 + case, residual=residual)
+        say("random shape", seed, case, M, N, K, dtype, act, "residual" if residual else "", "tile_cfg", cfg)
+        auto = _run_fused(d, act, dtype)
+        var = _run_fused(d, act, dtype, tile_cfg=cfg)
+        ref = oracle.fused_linear(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, R=d.get("R"))
+        _assert_close(auto, ref, dtype, f"random {M}x{N}x{K} {dtype} {act} auto")
+        _assert_close(var, ref, dtype, f"random {M}x{N}x{K} {dtype} {act} tile_cfg {cfg}")
+        if dtype == "f32" or cfg in FAMILY_16:
+            assert np.array_equal(auto.view(np.uint8), var.view(np.uint8)), (M, N, K, dtype, act, cfg)
+
+
 # --------------------------------------------------- K=1 / K=3 and the chain
 
 @pytest.mark.parametrize("dtype", DTYPES)
