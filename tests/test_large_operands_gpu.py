@@ -3,7 +3,8 @@
 The kernels address an operand through a descriptor based at the tile's
 first row (or column), with 32-bit offsets that stay below 256 rows of it.
 In the last K stage the lane whose 16-byte chunk holds the operand's very
-last element reloads that element on its own; these tests check that this
+last element reloads that element on its own (FP8 codes: up to the last
+three, the ones its partial last dword holds); these tests check that this
 reload is right when the whole operand spans more than 2^31 bytes.
 
 Small integers make every value exact, so the rows (or columns) that carry
@@ -67,6 +68,43 @@ def test_forward_A_over_2GiB(tile_cfg):
     assert np.array_equal(h[live].view(np.uint16), ref_live.view(np.uint16)), \
         oracle.compare(h[live], ref_live, dtype)
     ref_zero = oracle.fused_linear(np.zeros((1, K), dtype=np.float16), b_s, bias_s, act="relu", dtype=dtype)
+    dead = np.ones(M, dtype=bool)
+    dead[live] = False
+    assert (h[dead].view(np.uint16) == ref_zero.view(np.uint16)).all()
+
+
+E4M3 = {-1: 0xB8, 0: 0x00, 1: 0x38}  # exact small integers as OCP FP8 E4M3 codes
+
+
+@pytest.mark.parametrize("tile_cfg", [0, 2, 12])
+def test_fp8_A_over_2GiB(tile_cfg):
+    """FP8 codes: A of M*K bytes > 2^31 with K % 16 != 0, so the last chunk of
+    each row straddles K and the buffer's last dword is partial; the last
+    three codes of A are nonzero and must be reloaded."""
+    Kf = 1021                      # K % 16 == 13
+    M, N = 2_104_003, 64          # M*K % 4 == 3: the last dword of A holds three codes
+    assert M * Kf > 2 ** 31
+    rng = np.random.default_rng(70 + tile_cfg)
+    live = _live(M)
+    lut = np.array([E4M3[v] for v in (-1, 0, 1)], dtype=np.uint8)
+    a_live = lut[rng.integers(0, 3, (live.size, Kf))]
+    a_live[-1, Kf - 3:] = E4M3[1]                   # the last three codes of A
+    b = lut[rng.integers(0, 3, (Kf, N))]
+    b[Kf - 3:] = np.where(rng.integers(0, 2, (3, N)) == 0, E4M3[-1], E4M3[1])
+    bias = synth.to_storage(rng.integers(-3, 4, N).astype(np.float64), "f16")
+    say("FP8 A over 2 GiB", M, N, Kf, "tile_cfg", tile_cfg)
+    A = torch.zeros((M, Kf), dtype=torch.uint8, device="cuda")
+    A[torch.from_numpy(live).to("cuda")] = torch.from_numpy(a_live).to("cuda")
+    out = fl.fused_linear_fp8(A, torch.from_numpy(b).to("cuda"), 0.5, to_dev(bias, "f16"), None, act="relu",
+                              out_dtype=torch.float16, tile_cfg=tile_cfg)
+    torch.cuda.synchronize()
+    del A
+    h = to_host(out, "f16")
+    ref_live = oracle.fused_linear_fp8(a_live, b, 0.5, bias, None, act="relu", out_dtype="f16")
+    assert np.array_equal(h[live].view(np.uint16), ref_live.view(np.uint16)), \
+        oracle.compare(h[live], ref_live, "f16")
+    ref_zero = oracle.fused_linear_fp8(np.zeros((1, Kf), dtype=np.uint8), b, 0.5, bias, None, act="relu",
+                                       out_dtype="f16")
     dead = np.ones(M, dtype=bool)
     dead[live] = False
     assert (h[dead].view(np.uint16) == ref_zero.view(np.uint16)).all()
