@@ -113,3 +113,13 @@ def test_parity_stats_report_errors_and_violations():
 def test_cpu_model_names_the_host():
     info = bench.cpu_model()
     assert info["logical_cpus"] >= 1
+
+
+def test_more_than_one_gpu_is_refused():
+    """One GPU only: --gpus 2 exits with a message before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
