@@ -93,6 +93,24 @@ struct TileShape {
 // to -7% at 384 and 512).
 constexpr int64_t kOcc2MaxK256 = 256;
 constexpr int64_t kOcc2MaxK192 = 1024;
+constexpr int64_t kOcc2MaxK256Fp8 = 1024;  // FP8 operands (fl_fused_linear_fp8)
+
+// The automatic tile width (waves x relative wave time, below) and whether
+// the 256x128 grid fills both workgroup slots of every CU.
+struct AutoTile {
+    int bn;
+    bool fills_two;
+};
+
+AutoTile auto_tile(int64_t M, int64_t N) {
+    const int64_t cus = cu_count();
+    const int64_t tm = (M + 255) / 256;
+    auto waves = [&](int64_t bn) { return (tm * ((N + bn - 1) / bn) + cus - 1) / cus; };
+    // waves x time of one wave of tiles, in hundredths of a 256x256 wave
+    const int64_t c256 = waves(256) * 100, c192 = waves(192) * 79, c128 = waves(128) * 55;
+    const int bn = (c256 <= c192 && c256 <= c128) ? 256 : (c192 <= c128 ? 192 : 128);
+    return {bn, tm * ((N + 127) / 128) >= 2 * cus};
+}
 
 fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_options *opt, TileShape &t) {
     const int cfg = opt ? opt->tile_cfg : 0;
@@ -122,14 +140,9 @@ fl_status tile_shape(int dtype, int64_t M, int64_t N, int64_t K, const fl_option
     case 15: t = {256, 192, fl::kDirect64x192W8M16}; return FL_OK;
     default: break;
     }
-    const int64_t cus = cu_count();
-    const int64_t tm = (M + 255) / 256;
-    auto waves = [&](int64_t bn) { return (tm * ((N + bn - 1) / bn) + cus - 1) / cus; };
-    // waves x time of one wave of tiles, in hundredths of a 256x256 wave
-    const int64_t c256 = waves(256) * 100, c192 = waves(192) * 79, c128 = waves(128) * 55;
-    const int bn = (c256 <= c192 && c256 <= c128) ? 256 : (c192 <= c128 ? 192 : 128);
-    const bool fills_two = tm * ((N + 127) / 128) >= 2 * cus;
-    if (fills_two && K <= (bn == 256 ? kOcc2MaxK256 : bn == 192 ? kOcc2MaxK192 : 3072))
+    const AutoTile at = auto_tile(M, N);
+    const int bn = at.bn;
+    if (at.fills_two && K <= (bn == 256 ? kOcc2MaxK256 : bn == 192 ? kOcc2MaxK192 : 3072))
         t = {256, 128, fl::kDirect32x128Occ2};
     else if (bn == 128)
         t = {256, 128, fl::kDirect64x128M16};
@@ -284,7 +297,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     if (fp8_in) {
         const fl::fused_launcher f = dtype == FL_F16 ? fl::pick_fp8_for<FL_F16>(act, t.variant)
                                                      : fl::pick_fp8_for<FL_BF16>(act, t.variant);
-        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2, 5, 7 and 12 only");
+        if (!f) return fail(FL_ERR_UNSUPPORTED, "FP8 inputs are built for tile_cfg 0, 1, 2, 5, 6, 7 and 12 only");
         f(a, grid, static_cast<hipStream_t>(stream));
         return check_launch("fused_linear_fp8");
     }
@@ -439,15 +452,21 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     if (overlaps(out, o_bytes, B8, b_bytes)) return fail(FL_ERR_INVALID_ARG, "out overlaps B");
     fl_options o = opt ? *opt : fl_options{};
     if (o.tile_cfg == 0) {
-        TileShape t;
-        tile_shape(FL_F16, M, N, K, &o, t);
-        // 32x32x64 blocks in the forward choice's tile: the 8-wave 256x256
-        // kernel, 256x192, or 256x128 (also where the 16-bit choice is the
-        // two-per-CU kernel, which has no FP8 build).  The 16x16x128 kernel
-        // (256x128) is an option: no faster than the 32x32x64 one of the
-        // same tile, where 16-bit blocks of 16x16 gain from their lower
-        // power draw.
-        o.tile_cfg = t.variant == fl::kDirect64x256W8M16 ? 5 : family32(t.variant) == fl::kDirect64x192 ? 7 : 2;
+        // 32x32x64 blocks in the forward choice's width: the 8-wave 256x256
+        // kernel, 256x192, or 256x128.  An FP8 K loop takes about half the
+        // time of a 16-bit one of the same K, so the two-per-CU kernel, whose
+        // epilogues overlap the other workgroup's K loop, pays off up to
+        // longer reductions than in 16 bits: K <= 1024 where the width is
+        // 256 (measured on 8192^2: +27% at K 256, +6% at 1024, -5% at
+        // 2048), K <= 3072 where it is 192 (on 1024x21568: +17% at 512, +4%
+        // at 3072, -3% at 4096) or 128.  The 16x16x128 kernel (256x128) is
+        // an option: no faster than the 32x32x64 one of the same tile, where
+        // 16-bit blocks of 16x16 gain from their lower power draw.
+        const AutoTile at = auto_tile(M, N);
+        if (at.fills_two && K <= (at.bn == 256 ? kOcc2MaxK256Fp8 : 3072))
+            o.tile_cfg = 6;
+        else
+            o.tile_cfg = at.bn == 256 ? 5 : at.bn == 192 ? 7 : 2;
     }
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }

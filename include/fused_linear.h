@@ -239,11 +239,14 @@ fl_status fl_fused_linear_quant(const void *A, const void *B,
  *   Any M and K; N of 1 or 2 is FL_ERR_UNSUPPORTED (rows of B of 1 or 2
  *             bytes), any other N is served.
  *   opt       tile_cfg 0 (automatic: the tile width fl_fused_linear would
- *             use, 256, 192 or 128, with 32x32x64 blocks; 256x128 where it
- *             would use the two-per-CU kernel), 1, 2, 5 or 7 (32x32x64
- *             blocks, bit-identical to one another) or 12 (16x16x128 blocks,
- *             256x128 tiles: the same products summed in another order);
- *             others are FL_ERR_UNSUPPORTED.
+ *             choose, 256, 192 or 128, with 32x32x64 blocks; where the
+ *             256x128 grid fills two workgroups per compute unit and K <=
+ *             1024 (width 256) or K <= 3072 (192 or 128), the two-per-CU
+ *             256x128 kernel), 1, 2, 5, 6 or 7 (32x32x64 blocks,
+ *             bit-identical to one another; 6 is the two-per-CU kernel with
+ *             64-deep stages) or 12 (16x16x128 blocks, 256x128 tiles: the
+ *             same products summed in another order); others are
+ *             FL_ERR_UNSUPPORTED.
  */
 fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
                               const void *bias, const void *Y, void *out,

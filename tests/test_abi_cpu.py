@@ -239,9 +239,9 @@ def _fp8(lib, A=A_P, B=B_P, ab=1.0, out=OUT_P, dt=F16, M=64, N=64, K=64, act=REL
     (dict(A=None), INVALID, "A is NULL"),
     (dict(out=A_P + 64), INVALID, "out overlaps A"),
     (dict(act=GLU), INVALID, "the gate needs Y"),
-    (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 7 and 12"),
+    (dict(opt=fl.Options(0, 0, 4, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 6, 7 and 12"),
     (dict(opt=fl.Options(0, 0, 16, 0, None)), UNSUPPORTED, "tile_cfg 16"),
-    (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 7 and 12"),
+    (dict(opt=fl.Options(0, 0, 10, 0, None)), UNSUPPORTED, "tile_cfg 0, 1, 2, 5, 6, 7 and 12"),
     (dict(K=65536, N=32768), UNSUPPORTED, "B too large"),
 ])
 def test_fp8_rejects_bad_arguments(lib, kwargs, status, msg):

@@ -577,7 +577,7 @@ def test_quant_full_size_whole_output():
 # GEMM + Activation on CDNA4 with TLX", "Future Work": the projection in FP8).
 
 FP8_CODES = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}  # exact small integers in OCP E4M3
-FP8_CFGS = (0, 1, 2, 5, 7, 12)  # automatic; 32x32x64 blocks (1, 2, 5, 7); 16x16x128 blocks (12)
+FP8_CFGS = (0, 1, 2, 5, 6, 7, 12)  # automatic; 32x32x64 blocks (1, 2, 5, 6, 7); 16x16x128 blocks (12)
 
 
 def _run_fp8(d, act, out_dtype, **opts):
@@ -641,7 +641,24 @@ def test_fp8_ragged_K_and_N_bit_exact(out_dtype, act, shape):
         assert not bad.any(), (cfg, np.argwhere(bad)[:5], oracle.compare(out, ref, out_dtype))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 5, 7, 12])
+@pytest.mark.parametrize("K", [300, 1021])
+def test_fp8_two_per_cu_automatic_choice(K):
+    """Where the 256x128 grid fills two workgroups per CU and K is short, the
+    automatic FP8 choice is the two-per-CU kernel (64-deep stages): integer
+    codes, a ragged K, bit-exact against the oracle and bit-identical to
+    tile_cfg 6 and to the one-per-CU 256x128 kernel."""
+    M, N = 1024, 16384 + 37                      # 4 x 129 tiles of 256x128
+    d = _fp8_integer_inputs(M, N, K, "f16", "glu", seed=K)
+    ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act="glu", out_dtype="f16")
+    outs = {}
+    for cfg in (0, 6, 2):
+        say("fp8 two per CU", K, "tile_cfg", cfg)
+        outs[cfg] = _run_fp8(d, "glu", "f16", tile_cfg=cfg)
+        bad = outs[cfg].view(np.uint16) != ref.view(np.uint16)
+        assert not bad.any(), (cfg, np.argwhere(bad)[:5])
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5, 6, 7, 12])
 def test_fp8_debug_sync_gives_the_same_bits(cfg):
     """The FP8 kernels under the debugging schedule (an extra full wait for
     the copies and an extra barrier in every K stage), on a ragged shape
