@@ -22,7 +22,8 @@
 //     (4 columns per lane) receive one column each with 4 consecutive k
 //     values -- the K-contiguous B operand of the MFMA.
 //   * A K stage of BK values (64 for 16-bit operands, 128 for FP8: A rows
-//     are whole 128-byte lines; or 32) occupies one of NBUF LDS buffers.
+//     are whole 128-byte lines; 32 or 64 where A rows are 64 bytes)
+//     occupies one of NBUF LDS buffers.
 //     The copies of a stage are issued right after the barrier that frees
 //     its buffer, so NBUF-1 stages are in flight while MFMAs run
 //     ("Optimizing GEMM + Activation on CDNA4 with TLX", "Version 3": a
