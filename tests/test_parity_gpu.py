@@ -1062,3 +1062,58 @@ def test_side_input_unaligned_bit_identical(dtype):
         assert np.array_equal(to_host(gX, dtype).view(np.uint16), to_host(rX, dtype).view(np.uint16)), act
         if act == "glu":
             assert np.array_equal(to_host(gY, dtype).view(np.uint16), to_host(rY, dtype).view(np.uint16))
+
+
+# ------------------------------ seeded random shapes, the other entry points
+
+QUANT_CFGS = (0, 2, 5, 6, 7, 10, 11, 12, 15)
+BWD_CFGS = (0, 2, 5, 10, 12)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_seeded_random_shapes_fp8_quant_bwd(seed):
+    """Seeded random ragged shapes (M, K up to 700, N from 3) through the
+    FP8-operand, quantized-output and backward entry points, each through
+    the automatic choice and one random kernel variant of its own list.
+    Small-integer inputs keep every fp32 sum exact, so the whole output (and
+    dbias) must equal the oracle's bits whatever the kernel's order of
+    summation."""
+    rng = np.random.default_rng(3000 + seed)
+    for case in range(6):
+        M, N, K = int(rng.integers(1, 700)), int(rng.integers(3, 700)), int(rng.integers(1, 700))
+        dtype = ["f16", "bf16"][int(rng.integers(0, 2))]
+        act = ["none", "relu", "glu"][int(rng.integers(0, 3))]
+        s = 100 * seed + case
+        kind = ("fp8", "quant", "bwd")[case % 3]
+        if kind == "fp8":
+            cfg = FP8_CFGS[int(rng.integers(1, len(FP8_CFGS)))]
+            d = _fp8_integer_inputs(M, N, K, dtype, act, seed=s)
+            ref = oracle.fused_linear_fp8(d["A8"], d["B8"], d["ab_scale"], d["bias"], d["Y"], act=act,
+                                          out_dtype=dtype)
+            for c in (0, cfg):
+                say("random fp8", seed, case, M, N, K, dtype, act, "tile_cfg", c)
+                out = _run_fp8(d, act, dtype, tile_cfg=c)
+                bad = out.view(np.uint16) != ref.view(np.uint16)
+                assert not bad.any(), (M, N, K, dtype, act, c, np.argwhere(bad)[:5])
+        elif kind == "quant":
+            cfg = QUANT_CFGS[int(rng.integers(1, len(QUANT_CFGS)))]
+            qfmt = ["fp8_e4m3", "int8"][int(rng.integers(0, 2))]
+            scale = 0.25 if qfmt == "fp8_e4m3" else 8.0
+            d = synth.draw_integer(M, N, K, dtype, act, seed=s, amax=1, bias_max=3)
+            ref = oracle.fused_linear_quant(d["A"], d["B"], d["bias"], d["Y"], act=act, dtype=dtype, qfmt=qfmt,
+                                            scale=scale)
+            for c in (0, cfg):
+                say("random quant", seed, case, M, N, K, dtype, act, qfmt, "tile_cfg", c)
+                got = _run_quant(d, act, dtype, qfmt, scale, tile_cfg=c)
+                assert np.array_equal(got, ref), (M, N, K, dtype, act, qfmt, c, np.argwhere(got != ref)[:5])
+        else:
+            cfg = BWD_CFGS[int(rng.integers(1, len(BWD_CFGS)))]
+            d = synth.draw_bwd_integer(M, N, K, dtype, act, seed=s)
+            rX, rY, rdb = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act=act, dtype=dtype)
+            for c in (0, cfg):
+                say("random bwd", seed, case, M, N, K, dtype, act, "tile_cfg", c)
+                dX, dY, db = _run_bwd(d, act, dtype, tile_cfg=c)
+                assert np.array_equal(dX.view(np.uint8), rX.view(np.uint8)), (M, N, K, dtype, act, c)
+                if act == "glu":
+                    assert np.array_equal(dY.view(np.uint8), rY.view(np.uint8)), (M, N, K, dtype, act, c)
+                assert np.array_equal(db, rdb), (M, N, K, dtype, act, c)
