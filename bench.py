@@ -30,6 +30,9 @@ DEFAULT_WORKLOAD = "relu_f16_4096x4096x4096"
 # 2.4 GHz; fp16/bf16 4096 flop/clk/CU, fp32 256 flop/clk/CU.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20      # MI355X last-level cache (Infinity Cache) in front of HBM
+MALL_NOTE = ("the passes' (M,N) arrays fit in the 256 MB MALL and stay there between passes, so their GB/s "
+             "can exceed the HBM peak (frac_hbm > 1)")
 ES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
@@ -446,6 +449,8 @@ def main():
             # writes dX (+dY); the chain also writes and re-reads D and re-reads dX
             "epilogue_traffic_bytes": {"fused": (2 + 2 * glu) * mn * es, "unfused": (5 + 2 * glu) * mn * es},
         }
+        if ag_bytes <= MALL_BYTES:
+            result["unfused"]["note"] = MALL_NOTE
     elif w.residual or w.qfmt or w.in8 or w.bwd:
         result["unfused"] = None  # the unfused chain has no residual, quantizing or FP8 form
     elif not args.no_unfused:
@@ -474,6 +479,8 @@ def main():
             "activation_traffic_bytes": activation_traffic_bytes(w.M, w.N, es, w.act),
             "activation_traffic_bytes_two_kernels": activation_traffic_bytes(w.M, w.N, es, w.act, kernels=2),
         }
+        if act_bytes <= MALL_BYTES:
+            result["unfused"]["note"] = MALL_NOTE
 
     if (w.act == "glu" and not w.bwd and not w.in8 and not w.residual and w.dtype == "f16"
             and (w.M, w.N) == (1024, 21568) and w.K in PAGES_GATE_MI350X):
