@@ -34,7 +34,8 @@ LIB_PATH = os.path.join(PKG, "libfused_linear.so")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
 EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
-           "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_gemm", "fl_gemm_nt", "fl_activation_grad",
+           "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_fused_linear_bwd_ws", "fl_bwd_workspace_bytes",
+           "fl_gemm", "fl_gemm_nt", "fl_activation_grad",
            "fl_column_sum", "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
 
@@ -80,6 +81,9 @@ def load_library():
                                         ctypes.POINTER(Options)]
     lib.fl_fused_linear_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
                                         ctypes.POINTER(Options)]
+    lib.fl_fused_linear_bwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
+                                           ctypes.POINTER(Options), vp, ctypes.c_size_t]
+    lib.fl_bwd_workspace_bytes.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_activation_grad.argtypes = [vp, vp, vp, vp, vp, i64, i64, c_int, c_int, vp]
@@ -229,12 +233,16 @@ def fused_linear_fp8(A8, B8, ab_scale, bias=None, Y=None, act="relu", out_dtype=
     return out
 
 
-def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, *, stream=None, **options):
+def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, *, stream=None, workspace=None,
+                     **options):
     """The backward epilogue (fl_fused_linear_bwd): D = G @ W^T with G (M,K)
     and W (N,K), then dX = D * act'(X) at the saved pre-activation X (M,N),
     for the gate also dY = D * X, and dbias = column sums of dX (fp32).
     dbias=True allocates the (N,) fp32 result, a tensor is overwritten,
-    None/False skips it.  Returns (dX, dY or None, dbias or None)."""
+    None/False skips it.  workspace: a device tensor of at least
+    bwd_workspace_bytes(M, N, K, dtype) bytes, or True to allocate one with
+    torch: then fl_fused_linear_bwd_ws runs and dbias is reproducible to the
+    bit.  Returns (dX, dY or None, dbias or None)."""
     import torch
     lib = load_library()
     if G.dim() != 2 or W.dim() != 2 or G.shape[1] != W.shape[1]:
@@ -251,11 +259,29 @@ def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, 
     elif dbias is False:
         dbias = None
     opt = _options(**options)
-    _check(lib.fl_fused_linear_bwd(
-        _dev_ptr(G, "G", dt), _dev_ptr(W, "W", dt, (N, K)), _dev_ptr(X, "X", dt, (M, N)), _dev_ptr(Y, "Y", dt, (M, N)),
-        _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)), _dev_ptr(dbias, "dbias", torch.float32, (N,)),
-        M, N, K, ACTS[act], _dtype_code(dt), _stream(G, stream), ctypes.byref(opt)))
+    args = (_dev_ptr(G, "G", dt), _dev_ptr(W, "W", dt, (N, K)), _dev_ptr(X, "X", dt, (M, N)),
+            _dev_ptr(Y, "Y", dt, (M, N)), _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)),
+            _dev_ptr(dbias, "dbias", torch.float32, (N,)), M, N, K, ACTS[act], _dtype_code(dt), _stream(G, stream),
+            ctypes.byref(opt))
+    if workspace is None:
+        _check(lib.fl_fused_linear_bwd(*args))
+        return dX, dY, dbias
+    if workspace is True:
+        workspace = torch.empty((max(bwd_workspace_bytes(M, N, K, dt), 1),), dtype=torch.uint8, device=G.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check(lib.fl_fused_linear_bwd_ws(*args, ctypes.c_void_p(workspace.data_ptr()),
+                                      workspace.numel() * workspace.element_size()))
     return dX, dY, dbias
+
+
+def bwd_workspace_bytes(M, N, K, dtype):
+    """Bytes of workspace fl_fused_linear_bwd_ws needs (fl_bwd_workspace_bytes)."""
+    lib = load_library()
+    n = ctypes.c_size_t()
+    _check(lib.fl_bwd_workspace_bytes(M, N, K, _dtype_code(dtype) if not isinstance(dtype, int) else dtype,
+                                      ctypes.byref(n)))
+    return n.value
 
 
 def gemm_nt(A, Bt, D=None, *, stream=None):

@@ -1161,14 +1161,16 @@ struct Dma16 {
                 }
             }
         }
-        if (BWD && a.dbias) {
+        if (BWD && (a.dbias || a.dbias_part)) {
             // Column sums of dX for dbias: the lanes' sums over their 4 rows
             // meet in the wave's LDS area (row lrow, phase 2 has read it
-            // already), lane t adds up column t over the 32 rows, and one
-            // fp32 atomic per column and wave adds that into dbias (so the
-            // order of the additions across tiles is not fixed).  Rows past
-            // M and columns past N contribute zeros (A and B^T read as zero
-            // there).
+            // already) and lane t adds up column t over the 32 rows.  With a
+            // partial-sum buffer that value goes to its row 2*tile_row + wm
+            // (a later pass adds the rows in order, so dbias is the same to
+            // the bit whatever order the tiles ran in); else one fp32 atomic
+            // per column and wave adds it into dbias (the order of those
+            // additions across tiles is not fixed).  Rows past M and columns
+            // past N contribute zeros (A and B^T read as zero there).
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int c = gcol(g, lane);
@@ -1181,7 +1183,12 @@ struct Dma16 {
 #pragma unroll 8
             for (int r = 0; r < RBH; ++r) sum += *(const FL_LDS float *)(wbuf + r * DB_ROW + lane * 4);
             const int col = n0 + wn * WN + lane;
-            if (col < a.N) unsafeAtomicAdd(a.dbias + col, sum);
+            if (col < a.N) {
+                if (a.dbias_part)
+                    a.dbias_part[(size_t)(2 * (m0 / BM) + wm) * a.N + col] = sum;
+                else
+                    unsafeAtomicAdd(a.dbias + col, sum);
+            }
         }
     }
 

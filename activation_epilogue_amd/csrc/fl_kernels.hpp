@@ -249,6 +249,8 @@ struct GemmArgs {
     const void *Xs;    // backward: the saved pre-activation X (M,N); B is then (N,K) row-major
     void *dY;          // backward, gate: the second output D*X (M,N)
     float *dbias;      // backward: column sums of dX (N,), fp32, added to atomically
+    float *dbias_part; // backward, or null: per (tile row, wave row) column sums of dX, (2*tiles_m, N)
+                       // fp32, written instead of the atomics (dbias is left alone then)
     void *out;
     int M, N, K;
     int tiles_m, tiles_n, group;

@@ -243,7 +243,8 @@ fl_status validate_gemm(const void *A, const void *B, const void *bias, const vo
 fl_status launch_gemm(const void *A, const void *B, const void *bias, const void *R, const void *Y, void *out,
                       int64_t M, int64_t N, int64_t K, int act, int dtype, void *stream, const fl_options *opt,
                       int qfmt = -1, float scale = 1.0f, bool fp8_in = false, float ab_scale = 1.0f,
-                      const void *Xs = nullptr, void *dY = nullptr, float *dbias = nullptr, bool bwd = false) {
+                      const void *Xs = nullptr, void *dY = nullptr, float *dbias = nullptr, bool bwd = false,
+                      float *dbias_part = nullptr) {
     if (M == 0 || N == 0) return FL_OK;
     TileShape t;
     fl_status s = tile_shape(dtype, M, N, K, opt, t);
@@ -270,6 +271,7 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     a.Xs = Xs;
     a.dY = dY;
     a.dbias = dbias;
+    a.dbias_part = dbias_part;
     a.out = out;
     a.M = (int)M;
     a.N = (int)N;
@@ -311,6 +313,17 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
     const bool use_vec = t.variant != fl::kRegStaged || aligned_rows;
     pick_fused(dtype, act, use_vec, t.variant, R != nullptr)(a, grid, static_cast<hipStream_t>(stream));
     return check_launch("fused_linear");
+}
+
+// out[c] = the sum of column c of the rows x n partial sums, added in row
+// order from 0 (the bias gradient from the backward tiles' partial column
+// sums: the same bits whatever order the tiles ran in).
+__global__ void sum_rows_f32_kernel(const float *part, int64_t rows, int64_t n, float *out) {
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x) {
+        float acc = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) acc += part[r * n + c];
+        out[c] = acc;
+    }
 }
 
 // Zeroes n floats (the bias gradient before the tiles add into it); a
@@ -471,10 +484,21 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale, co
     return launch_gemm(A8, B8, bias, nullptr, Y, out, M, N, K, act, out_dtype, stream, &o, -1, 1.0f, true, ab_scale);
 }
 
-fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY,
-                              float *dbias, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
-                              void *stream, const fl_options *opt) {
-    clear_error();
+// Bytes of the backward's partial column sums: two rows (one per wave row
+// of a tile) per 256-row tile row, N fp32 values each.
+size_t bwd_part_bytes(int64_t M, int64_t N) {
+    if (M <= 0 || N <= 0) return 0;
+    return (size_t)2 * (size_t)((M + 255) / 256) * (size_t)N * sizeof(float);
+}
+
+// The backward epilogue; with `part` (bwd_part_bytes of device memory) the
+// tiles write partial column sums there and one more pass adds them into
+// dbias in a fixed order, else the tiles add into a zeroed dbias with
+// atomics.  `ws` is the workspace argument as the caller gave it (checked
+// here when part is used).
+fl_status bwd_impl(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY, float *dbias,
+                   int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream, const fl_options *opt,
+                   bool deterministic, void *ws, size_t ws_bytes) {
     if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for fp16 and bf16");
     // G plays A (M,K) and W (N,K) has B's size; X is checked as a residual
     // would be (it may be dX itself), Y as the gate's operand.
@@ -514,6 +538,32 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     } else if (o.tile_cfg != 2 && o.tile_cfg != 5 && o.tile_cfg != 10 && o.tile_cfg != 12) {
         return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2, 5, 10 and 12 only");
     }
+    float *part = nullptr;
+    const size_t need = bwd_part_bytes(M, N);
+    if (deterministic && dbias && need) {
+        if (!ws) return fail(FL_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", need);
+        if (ws_bytes < need)
+            return fail(FL_ERR_INVALID_ARG, "workspace of %zu bytes is too small (%zu bytes needed)", ws_bytes, need);
+        if (!aligned(ws, 4)) return fail(FL_ERR_INVALID_ARG, "workspace is not 4-byte aligned");
+        const size_t es = elem_size(dtype);
+        const size_t g_bytes = (size_t)M * K * es, w_bytes = (size_t)N * K * es, o_bytes = (size_t)M * N * es;
+        const void *others[7] = {G, W, X, Y, dX, dY, dbias};
+        const size_t sizes[7] = {g_bytes, w_bytes, o_bytes, Y ? o_bytes : 0, o_bytes, dY ? o_bytes : 0,
+                                 (size_t)N * 4};
+        for (int i = 0; i < 7; ++i)
+            if (overlaps(ws, need, others[i], sizes[i])) return fail(FL_ERR_INVALID_ARG, "workspace overlaps an operand");
+        part = static_cast<float *>(ws);
+    }
+    if (part) {
+        // the tiles write every partial sum; one pass then adds them in order
+        fl_status s2 = launch_gemm(G, W, nullptr, nullptr, Y, dX, M, N, K, act, dtype, stream, &o, -1, 1.0f, false,
+                                   1.0f, X, dY, dbias, true, part);
+        if (s2 != FL_OK) return s2;
+        hipLaunchKernelGGL(sum_rows_f32_kernel, dim3(grid_elementwise(N)), dim3(fl::kThreads), 0,
+                           static_cast<hipStream_t>(stream), part, (int64_t)(need / ((size_t)N * 4)), (int64_t)N,
+                           dbias);
+        return check_launch("fused_linear_bwd (dbias sum)");
+    }
     // dbias is a sum over every tile row: zero it first (a fill kernel on
     // the same stream), then the tiles add into it.
     if (dbias && N > 0) {
@@ -526,6 +576,33 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const
     if (M == 0 || N == 0) return FL_OK;
     return launch_gemm(G, W, nullptr, nullptr, Y, dX, M, N, K, act, dtype, stream, &o, -1, 1.0f, false, 1.0f, X, dY,
                        dbias, true);
+}
+
+fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY,
+                              float *dbias, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
+                              void *stream, const fl_options *opt) {
+    clear_error();
+    return bwd_impl(G, W, X, Y, dX, dY, dbias, M, N, K, act, dtype, stream, opt, false, nullptr, 0);
+}
+
+fl_status fl_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, fl_dtype dtype, size_t *bytes) {
+    clear_error();
+    if (!bytes) return fail(FL_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    if (dtype != FL_F16 && dtype != FL_BF16)
+        return fail(dtype == FL_F32 ? FL_ERR_UNSUPPORTED : FL_ERR_INVALID_ARG,
+                    "the backward epilogue is built for fp16 and bf16");
+    const fl_status s = check_dims(M, N, K);
+    if (s != FL_OK) return s;
+    *bytes = bwd_part_bytes(M, N);
+    return FL_OK;
+}
+
+fl_status fl_fused_linear_bwd_ws(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY,
+                                 float *dbias, int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype,
+                                 void *stream, const fl_options *opt, void *workspace, size_t workspace_bytes) {
+    clear_error();
+    return bwd_impl(G, W, X, Y, dX, dY, dbias, M, N, K, act, dtype, stream, opt, true, workspace, workspace_bytes);
 }
 
 fl_status fl_gemm_nt(const void *A, const void *Bt, void *D, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

@@ -66,6 +66,7 @@
 #ifndef FUSED_LINEAR_H
 #define FUSED_LINEAR_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -278,7 +279,8 @@ fl_status fl_fused_linear_fp8(const void *A8, const void *B8, float ab_scale,
  *          overwritten: a fill kernel zeroes it on `stream`, then every
  *          output tile adds its column sums with fp32 atomics, so its last
  *          bits may differ from run to run (the order of the additions is
- *          not fixed); dX and dY are deterministic.
+ *          not fixed; fl_fused_linear_bwd_ws fixes it); dX and dY are
+ *          deterministic.
  *   dtype  FL_F16 or FL_BF16 (FL_F32 is FL_ERR_UNSUPPORTED).
  *   opt    tile_cfg 0 (automatic: the 8-wave 256x256 kernel with 16x16x32
  *          MFMA blocks (10) where the forward choice is 256 wide, 256x128
@@ -294,6 +296,41 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X,
                               float *dbias, int64_t M, int64_t N, int64_t K,
                               fl_act act, fl_dtype dtype, void *stream,
                               const fl_options *opt);
+
+/* The backward epilogue with a bias gradient that is the same to the bit
+ * from run to run and whatever order the tiles run in (fl_fused_linear_bwd's
+ * atomics fix neither).  Same arguments, outputs and errors as
+ * fl_fused_linear_bwd, plus a caller-owned device workspace: each 256-row
+ * tile row writes two rows of fp32 partial column sums of dX (one per
+ * 128-row half, each summed in a fixed order) into
+ * workspace[(2*tile_row + half) * N + column], then one more launch on
+ * `stream` sets dbias[c] to those rows added in row order.  dX and dY are
+ * bit-identical to fl_fused_linear_bwd's; dbias agrees with it within the
+ * rounding of an fp32 sum (the tolerance fl_fused_linear_bwd states) and
+ * is bit-identical between tile_cfg values of one MFMA shape (10 and 12;
+ * 5 and 2).
+ *   workspace        device memory of at least fl_bwd_workspace_bytes(M,
+ *                    N, K, dtype) bytes, 4-byte aligned, overlapping no
+ *                    operand; only read and written by this call's
+ *                    launches on `stream` (its contents afterwards are
+ *                    unspecified).  Unused (may be NULL) when dbias is
+ *                    NULL or M or N is 0.
+ *   workspace_bytes  its size; FL_ERR_INVALID_ARG (no launch) when smaller
+ *                    than needed, NULL, misaligned or overlapping.
+ */
+fl_status fl_fused_linear_bwd_ws(const void *G, const void *W, const void *X,
+                                 const void *Y, void *dX, void *dY,
+                                 float *dbias, int64_t M, int64_t N, int64_t K,
+                                 fl_act act, fl_dtype dtype, void *stream,
+                                 const fl_options *opt, void *workspace,
+                                 size_t workspace_bytes);
+
+/* Bytes of workspace fl_fused_linear_bwd_ws needs for an (M,N) output:
+ * 2 * ceil(M/256) * N * 4 (0 when M or N is 0).  FL_ERR_INVALID_ARG for a
+ * NULL `bytes`, negative sizes or an unknown dtype, FL_ERR_UNSUPPORTED for
+ * fp32 and sizes above 2^31-1. */
+fl_status fl_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                 fl_dtype dtype, size_t *bytes);
 
 /* The unfused backward chain, for comparison with fl_fused_linear_bwd: one
  * launch per step, each storing its result in dtype (so D and dX round-trip

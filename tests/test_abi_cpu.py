@@ -284,6 +284,57 @@ def test_bwd_rejects_bad_arguments(lib, kwargs, status, msg):
     assert msg in lib.fl_last_error().decode()
 
 
+WS_P = 0x9000000   # backward workspace
+
+
+def _bwd_ws(lib, ws=WS_P, ws_bytes=1 << 20, **kw):
+    G, W, X, Y, dX, dY, db = (kw.pop(k, d) for k, d in (("G", A_P), ("W", B_P), ("X", X_P), ("Y", None),
+                                                         ("dX", OUT_P), ("dY", None), ("db", DB_P)))
+    M, N, K = kw.pop("M", 64), kw.pop("N", 64), kw.pop("K", 64)
+    assert not kw
+    return lib.fl_fused_linear_bwd_ws(G, W, X, Y, dX, dY, db, M, N, K, RELU, F16, None, None, ws, ws_bytes)
+
+
+def _ws_bytes(lib, M, N, K=64, dt=F16):
+    n = ctypes.c_size_t(12345)
+    st = lib.fl_bwd_workspace_bytes(M, N, K, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_bwd_workspace_bytes():
+    """Two fp32 rows of partial column sums per 256-row tile row."""
+    lib = fl.load_library()
+    assert _ws_bytes(lib, 8192, 14336) == (0, 2 * 32 * 14336 * 4)
+    assert _ws_bytes(lib, 257, 10) == (0, 2 * 2 * 10 * 4)
+    assert _ws_bytes(lib, 1, 1) == (0, 8)
+    assert _ws_bytes(lib, 0, 100) == (0, 0) and _ws_bytes(lib, 100, 0) == (0, 0)
+    assert _ws_bytes(lib, 64, 64, dt=F32)[0] == UNSUPPORTED
+    assert _ws_bytes(lib, -1, 64)[0] == INVALID
+    assert lib.fl_bwd_workspace_bytes(64, 64, 64, F16, None) == INVALID
+
+
+@pytest.mark.parametrize("kwargs,msg", [
+    (dict(ws=None), "workspace is NULL (512 bytes needed)"),
+    (dict(ws_bytes=511), "workspace of 511 bytes is too small (512 bytes needed)"),
+    (dict(ws=WS_P + 2), "workspace is not 4-byte aligned"),
+    (dict(ws=DB_P + 128), "workspace overlaps an operand"),
+    (dict(ws=X_P + 64), "workspace overlaps an operand"),
+    (dict(ws=A_P), "workspace overlaps an operand"),
+])
+def test_bwd_ws_rejects_bad_workspace(lib, kwargs, msg):
+    assert _bwd_ws(lib, **kwargs) == INVALID
+    assert msg in lib.fl_last_error().decode()
+
+
+def test_bwd_ws_checks_the_rest_as_the_plain_entry(lib):
+    """The workspace entry validates its other arguments exactly as
+    fl_fused_linear_bwd (same status and message, no launch)."""
+    assert _bwd_ws(lib, X=None) == INVALID
+    assert "X (the saved pre-activation) is NULL" in lib.fl_last_error().decode()
+    assert _bwd_ws(lib, db=DB_P + 2) == INVALID
+    assert "dbias is not 4-byte aligned" in lib.fl_last_error().decode()
+
+
 def test_unfused_bwd_chain_rejects_bad_arguments(lib):
     D_P, X2_P, DX_P = 0x7000000, 0x7800000, OUT_P
     assert lib.fl_gemm_nt(A_P, B_P, OUT_P, 64, 64, 64, F32, None) == UNSUPPORTED

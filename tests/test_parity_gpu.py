@@ -878,6 +878,61 @@ def test_bwd_full_size(name):
         _assert_close(dY, rY, w.dtype, name + " dY")
     res = oracle.compare_dbias(db, rdb, np.abs(rdx).sum(axis=0), w.M)
     assert res["ok"], res
+    say("bwd full size, workspace entry", name)
+    wX, wY, wdb = _run_bwd(d, w.act, w.dtype, workspace=True)
+    assert np.array_equal(wX.view(np.uint8), dX.view(np.uint8))
+    if w.act == "glu":
+        assert np.array_equal(wY.view(np.uint8), dY.view(np.uint8))
+    res = oracle.compare_dbias(wdb, rdb, np.abs(rdx).sum(axis=0), w.M)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "glu"])
+def test_bwd_ws_dbias_reproducible_and_order_free(dtype, act):
+    """fl_fused_linear_bwd_ws: dbias is the same to the bit over repeated
+    calls, tile orders (band height, persistent grid, XCD step) and the two
+    widths of one MFMA shape; dX and dY equal the plain entry point's bits;
+    dbias passes the oracle check."""
+    M, N, K = 1100, 700, 300   # 5 tile rows (the last one short), ragged N
+    d = synth.draw_bwd(M, N, K, dtype, act, seed=23)
+    for fam in ((10, 12), (5, 2)):
+        ref = None
+        for opts in [dict(tile_cfg=fam[0]), dict(tile_cfg=fam[0]), dict(tile_cfg=fam[1]),
+                     dict(tile_cfg=fam[0], group_m=1, persistent=1), dict(tile_cfg=fam[1], group_m=8, no_xcd_remap=1)]:
+            say("bwd workspace", dtype, act, opts)
+            got = _run_bwd(d, act, dtype, workspace=True, **opts)
+            _check_bwd(*got, d, act, dtype, f"bwd workspace {opts}")
+            plain = _run_bwd(d, act, dtype, **opts)
+            assert np.array_equal(got[0].view(np.uint8), plain[0].view(np.uint8)), opts
+            if act == "glu":
+                assert np.array_equal(got[1].view(np.uint8), plain[1].view(np.uint8)), opts
+            if ref is None:
+                ref = got[2]
+            assert np.array_equal(got[2].view(np.uint32), ref.view(np.uint32)), (opts, np.abs(got[2] - ref).max())
+
+
+@pytest.mark.parametrize("dtype", BWD_DTYPES)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 17, 7), (257, 264, 5), (513, 770, 3), (600, 300, 64)])
+def test_bwd_ws_integer_inputs_bit_exact(dtype, shape):
+    """Integer inputs: dbias from the workspace entry equals the oracle's
+    exact column sums; a workspace larger than needed and a second, smaller
+    call on the same workspace change nothing."""
+    M, N, K = shape
+    d = synth.draw_bwd_integer(M, N, K, dtype, "glu", seed=M + N + K)
+    rX, rY, rdb = oracle.fused_linear_bwd(d["G"], d["W"], d["X"], d["Y"], act="glu", dtype=dtype)
+    ws = torch.full((fl.bwd_workspace_bytes(M, N, K, TORCH_DT[dtype]) + 4096,), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(2):
+        say("bwd workspace integer", dtype, shape)
+        dX, dY, db = _run_bwd(d, "glu", dtype, workspace=ws)
+        assert np.array_equal(dX.view(np.uint8), rX.view(np.uint8))
+        assert np.array_equal(dY.view(np.uint8), rY.view(np.uint8))
+        assert np.array_equal(db, rdb)
+    small = synth.draw_bwd_integer(5, 9, 3, dtype, "glu", seed=1)
+    sX, sY, sdb = oracle.fused_linear_bwd(small["G"], small["W"], small["X"], small["Y"], act="glu", dtype=dtype)
+    dX, dY, db = _run_bwd(small, "glu", dtype, workspace=ws)
+    assert np.array_equal(db, sdb) and np.array_equal(dX.view(np.uint8), sX.view(np.uint8))
 
 
 @pytest.mark.parametrize("dtype", BWD_DTYPES)
