@@ -35,6 +35,7 @@ ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "glu": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "launch failed"}
 EXPORTS = ("fl_fused_linear", "fl_fused_linear_ex", "fl_fused_linear_residual", "fl_fused_linear_quant",
            "fl_fused_linear_fp8", "fl_fused_linear_bwd", "fl_fused_linear_bwd_ws", "fl_bwd_workspace_bytes",
+           "fl_fused_linear_bwd_noalloc",
            "fl_gemm", "fl_gemm_nt", "fl_activation_grad",
            "fl_column_sum", "fl_bias_add", "fl_activation",
            "fl_tile_grid", "fl_tile_of_program", "fl_status_string", "fl_last_error", "fl_version")
@@ -84,6 +85,8 @@ def load_library():
     lib.fl_fused_linear_bwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
                                            ctypes.POINTER(Options), vp, ctypes.c_size_t]
     lib.fl_bwd_workspace_bytes.argtypes = [i64, i64, i64, c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fl_fused_linear_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, vp,
+                                                ctypes.POINTER(Options)]
     lib.fl_gemm.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_gemm_nt.argtypes = [vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.fl_activation_grad.argtypes = [vp, vp, vp, vp, vp, i64, i64, c_int, c_int, vp]
@@ -272,6 +275,35 @@ def fused_linear_bwd(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, 
         raise ValueError("workspace must be a contiguous device tensor")
     _check(lib.fl_fused_linear_bwd_ws(*args, ctypes.c_void_p(workspace.data_ptr()),
                                       workspace.numel() * workspace.element_size()))
+    return dX, dY, dbias
+
+
+def fused_linear_bwd_noalloc(G, W, X, Y=None, act="relu", dX=None, dY=None, dbias=True, *, stream=None,
+                             **options):
+    """fl_fused_linear_bwd_noalloc: fused_linear_bwd with a reproducible dbias
+    whose partial sums go to the library's fixed per-GPU array (nothing is
+    allocated by the call; outputs not given are allocated here with torch).
+    Calls that may overlap on one GPU must be serialized."""
+    import torch
+    lib = load_library()
+    if G.dim() != 2 or W.dim() != 2 or G.shape[1] != W.shape[1]:
+        raise ValueError("G must be (M,K) and W (N,K)")
+    M, K = G.shape
+    N = W.shape[0]
+    dt = G.dtype
+    if dX is None:
+        dX = torch.empty((M, N), dtype=dt, device=G.device)
+    if act == "glu" and dY is None:
+        dY = torch.empty((M, N), dtype=dt, device=G.device)
+    if dbias is True:
+        dbias = torch.empty((N,), dtype=torch.float32, device=G.device)
+    elif dbias is False:
+        dbias = None
+    opt = _options(**options)
+    _check(lib.fl_fused_linear_bwd_noalloc(
+        _dev_ptr(G, "G", dt), _dev_ptr(W, "W", dt, (N, K)), _dev_ptr(X, "X", dt, (M, N)), _dev_ptr(Y, "Y", dt, (M, N)),
+        _dev_ptr(dX, "dX", dt, (M, N)), _dev_ptr(dY, "dY", dt, (M, N)), _dev_ptr(dbias, "dbias", torch.float32, (N,)),
+        M, N, K, ACTS[act], _dtype_code(dt), _stream(G, stream), ctypes.byref(opt)))
     return dX, dY, dbias
 
 

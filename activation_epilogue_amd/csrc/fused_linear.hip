@@ -495,10 +495,11 @@ size_t bwd_part_bytes(int64_t M, int64_t N) {
 // tiles write partial column sums there and one more pass adds them into
 // dbias in a fixed order, else the tiles add into a zeroed dbias with
 // atomics.  `ws` is the workspace argument as the caller gave it (checked
-// here when part is used).
+// here when part is used).  check_only: validate every other argument and
+// return before any launch.
 fl_status bwd_impl(const void *G, const void *W, const void *X, const void *Y, void *dX, void *dY, float *dbias,
                    int64_t M, int64_t N, int64_t K, fl_act act, fl_dtype dtype, void *stream, const fl_options *opt,
-                   bool deterministic, void *ws, size_t ws_bytes) {
+                   bool deterministic, void *ws, size_t ws_bytes, bool check_only = false) {
     if (dtype == FL_F32) return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for fp16 and bf16");
     // G plays A (M,K) and W (N,K) has B's size; X is checked as a residual
     // would be (it may be dX itself), Y as the gate's operand.
@@ -538,6 +539,7 @@ fl_status bwd_impl(const void *G, const void *W, const void *X, const void *Y, v
     } else if (o.tile_cfg != 2 && o.tile_cfg != 5 && o.tile_cfg != 10 && o.tile_cfg != 12) {
         return fail(FL_ERR_UNSUPPORTED, "the backward epilogue is built for tile_cfg 0, 2, 5, 10 and 12 only");
     }
+    if (check_only) return FL_OK;  // the caller checks or supplies the workspace itself
     float *part = nullptr;
     const size_t need = bwd_part_bytes(M, N);
     if (deterministic && dbias && need) {
@@ -603,6 +605,66 @@ fl_status fl_fused_linear_bwd_ws(const void *G, const void *W, const void *X, co
                                  void *stream, const fl_options *opt, void *workspace, size_t workspace_bytes) {
     clear_error();
     return bwd_impl(G, W, X, Y, dX, dY, dbias, M, N, K, act, dtype, stream, opt, true, workspace, workspace_bytes);
+}
+
+// The partial column sums of fl_fused_linear_bwd_noalloc live here: one
+// fixed array per GPU, held until the process ends.  In host code this name
+// is only a stand-in for the symbol; the device address of each GPU's copy
+// comes from hipGetSymbolAddress (scratch_on_current_device) and only that
+// address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+fl_status scratch_on_current_device(void **addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FL_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(FL_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FL_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return FL_OK;
+}
+}  // namespace
+
+fl_status fl_fused_linear_bwd_noalloc(const void *G, const void *W, const void *X, const void *Y, void *dX,
+                                      void *dY, float *dbias, int64_t M, int64_t N, int64_t K, fl_act act,
+                                      fl_dtype dtype, void *stream, const fl_options *opt) {
+    clear_error();
+    const fl_status s = check_dims(M, N, K);
+    if (s != FL_OK) return s;
+    const size_t need = dbias ? bwd_part_bytes(M, N) : 0;
+    if (need > kNoAllocScratchBytes)
+        return fail(FL_ERR_UNSUPPORTED,
+                    "fl_fused_linear_bwd_noalloc: dbias of this shape needs %zu bytes of scratch; the static scratch "
+                    "holds %zu (2 * ceil(M/256) * N * 4 bytes must fit)",
+                    need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need) {
+        // every other argument is checked before the first HIP call
+        const fl_status v = bwd_impl(G, W, X, Y, dX, dY, dbias, M, N, K, act, dtype, nullptr, opt, true, nullptr,
+                                     0, /*check_only=*/true);
+        if (v != FL_OK) return v;
+        const fl_status a = scratch_on_current_device(&ws);
+        if (a != FL_OK) return a;
+    }
+    return bwd_impl(G, W, X, Y, dX, dY, dbias, M, N, K, act, dtype, stream, opt, true, ws, kNoAllocScratchBytes);
 }
 
 fl_status fl_gemm_nt(const void *A, const void *Bt, void *D, int64_t M, int64_t N, int64_t K, fl_dtype dtype,

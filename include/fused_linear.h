@@ -325,6 +325,26 @@ fl_status fl_fused_linear_bwd_ws(const void *G, const void *W, const void *X,
                                  const fl_options *opt, void *workspace,
                                  size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc):
+ * fl_fused_linear_bwd_ws with the library's own workspace, a fixed 8 MiB
+ * device array per GPU (held until the process ends), so nothing is
+ * allocated, here or by the caller.  Same arguments, results and errors as
+ * fl_fused_linear_bwd_ws without the workspace; a dbias whose partial sums
+ * need more than 8 MiB (2 * ceil(M/256) * N * 4 bytes, e.g. M = 16384 with
+ * N = 16384 still fits) is FL_ERR_UNSUPPORTED with no launch.  On its first
+ * call on a device the library looks up that device's copy of the array
+ * (FL_ERR_LAUNCH if the lookup fails).  Every call on one GPU uses the same
+ * array, so calls that may overlap on one GPU (two streams, two threads)
+ * race and must be serialized by the caller.
+ */
+fl_status fl_fused_linear_bwd_noalloc(const void *G, const void *W,
+                                      const void *X, const void *Y, void *dX,
+                                      void *dY, float *dbias, int64_t M,
+                                      int64_t N, int64_t K, fl_act act,
+                                      fl_dtype dtype, void *stream,
+                                      const fl_options *opt);
+
 /* Bytes of workspace fl_fused_linear_bwd_ws needs for an (M,N) output:
  * 2 * ceil(M/256) * N * 4 (0 when M or N is 0).  FL_ERR_INVALID_ARG for a
  * NULL `bytes`, negative sizes or an unknown dtype, FL_ERR_UNSUPPORTED for

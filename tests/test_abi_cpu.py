@@ -335,6 +335,23 @@ def test_bwd_ws_checks_the_rest_as_the_plain_entry(lib):
     assert "dbias is not 4-byte aligned" in lib.fl_last_error().decode()
 
 
+def test_bwd_noalloc_checks_before_any_launch(lib):
+    """The no-allocation entry: a dbias whose partial sums exceed the 8 MiB
+    static scratch, and the plain entry's argument errors, are reported
+    with no HIP call (this host has no GPU)."""
+    na = lib.fl_fused_linear_bwd_noalloc
+    big = dict(M=65536, N=8192, K=64)     # 2 * 256 * 8192 * 4 = 16 MiB of partial sums
+    assert na(A_P, B_P, X_P, None, OUT_P, None, DB_P, big["M"], big["N"], big["K"], RELU, F16, None, None) \
+        == UNSUPPORTED
+    assert "needs 16777216 bytes of scratch; the static scratch holds 8388608" in lib.fl_last_error().decode()
+    assert na(A_P, B_P, None, None, OUT_P, None, DB_P, 64, 64, 64, RELU, F16, None, None) == INVALID
+    assert "X (the saved pre-activation) is NULL" in lib.fl_last_error().decode()
+    assert na(A_P, B_P, X_P, None, OUT_P, None, DB_P, 64, 64, 64, RELU, F32, None, None) == UNSUPPORTED
+    assert na(A_P, B_P, X_P, None, OUT_P, None, DB_P + 2, 64, 64, 64, RELU, F16, None, None) == INVALID
+    assert "dbias is not 4-byte aligned" in lib.fl_last_error().decode()
+    assert na(A_P, B_P, X_P, None, OUT_P, None, DB_P, -1, 64, 64, RELU, F16, None, None) == INVALID
+
+
 def test_unfused_bwd_chain_rejects_bad_arguments(lib):
     D_P, X2_P, DX_P = 0x7000000, 0x7800000, OUT_P
     assert lib.fl_gemm_nt(A_P, B_P, OUT_P, 64, 64, 64, F32, None) == UNSUPPORTED
