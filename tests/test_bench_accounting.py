@@ -123,3 +123,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_committed_traffic_records_match_the_sources():
+    """Every profiles/traffic_<workload>.json was taken on the kernel sources
+    as they are now (its recorded hash of the listed files, comments and
+    whitespace removed, matches), names a known workload and a summary page
+    that exists, so the bench line's roofline.traffic is never null for a
+    profiled workload and never stale."""
+    import glob
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    recs = sorted(glob.glob(os.path.join(root, "profiles", "traffic_*.json")))
+    assert recs, "no traffic records"
+    for path in recs:
+        rec = json.load(open(path))
+        name = os.path.basename(path)[len("traffic_"):-len(".json")]
+        assert rec["workload"] == name and name in synth.WORKLOADS, path
+        assert rec["source_hash"] == bench.source_hash(rec["sources"]), f"{path} is stale: profile again"
+        assert os.path.exists(os.path.join(root, "profiles", rec["summary"])), rec["summary"]
+        assert bench.measured_traffic(name) == rec["bytes_per_launch"] > 0
