@@ -88,3 +88,54 @@ def test_graph_replays_match_eager():
         rX, _, _ = oracle.fused_linear_bwd(b["G"], b["W"], b["X"], None, act="gelu_tanh", dtype="bf16")
         res = oracle.compare(got_dX, rX, "bf16")
         assert res["ok"], f"replay {r}: dX against the oracle {res}"
+
+
+def test_graph_reproducible_dbias_replays_bit_exact():
+    """The reproducible-dbias backward under capture: fl_fused_linear_bwd_ws
+    with a workspace allocated before the capture, and
+    fl_fused_linear_bwd_noalloc (its partial sums in the library's fixed
+    array; its one-time address lookup happens in the warm-up, before the
+    capture).  Every replay's dX and dbias equal an eager call's bit for bit."""
+    b = synth.draw_bwd(300, 520, 136, "bf16", "glu", seed=81)
+    bw = {k: to_dev(b[k], "bf16") for k in ("G", "W", "X", "Y")}
+    ws = torch.empty(fl.bwd_workspace_bytes(300, 520, 136, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    outs = {name: (torch.empty(300, 520, dtype=torch.bfloat16, device="cuda"),
+                   torch.empty(300, 520, dtype=torch.bfloat16, device="cuda"),
+                   torch.empty(520, dtype=torch.float32, device="cuda")) for name in ("ws", "noalloc")}
+
+    def work():
+        dX, dY, db = outs["ws"]
+        fl.fused_linear_bwd(bw["G"], bw["W"], bw["X"], bw["Y"], act="glu", dX=dX, dY=dY, dbias=db, workspace=ws)
+        dX, dY, db = outs["noalloc"]
+        fl.fused_linear_bwd_noalloc(bw["G"], bw["W"], bw["X"], bw["Y"], act="glu", dX=dX, dY=dY, dbias=db)
+
+    say("graph (reproducible dbias): warm-up on a side stream, then capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+
+    for r in range(3):
+        b = synth.draw_bwd(300, 520, 136, "bf16", "glu", seed=90 + r)
+        for k in bw:
+            bw[k].copy_(to_dev(b[k], "bf16"))
+        rX, rY, rdb = fl.fused_linear_bwd(bw["G"], bw["W"], bw["X"], bw["Y"], act="glu", workspace=True)
+        torch.cuda.synchronize()
+        ref = (to_host(rX, "bf16"), to_host(rY, "bf16"), rdb.cpu().numpy())
+        for t in outs.values():
+            for x in t:
+                x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say("graph replay (reproducible dbias)", r)
+        g.replay()
+        torch.cuda.synchronize()
+        for name, (dX, dY, db) in outs.items():
+            assert np.array_equal(to_host(dX, "bf16").view(np.uint16), ref[0].view(np.uint16)), (r, name, "dX")
+            assert np.array_equal(to_host(dY, "bf16").view(np.uint16), ref[1].view(np.uint16)), (r, name, "dY")
+            assert np.array_equal(db.cpu().numpy().view(np.uint32), ref[2].view(np.uint32)), (r, name, "dbias")
