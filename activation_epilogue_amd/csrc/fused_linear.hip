@@ -890,6 +890,6 @@ const char *fl_status_string(fl_status s) {
 
 const char *fl_last_error(void) { return g_err; }
 
-int fl_version(void) { return 10000; }
+int fl_version(void) { return 10100; }
 
 }  // extern "C"

@@ -36,7 +36,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fl_version() == 10000
+    assert lib.fl_version() == 10100
     assert lib.fl_status_string(0) == b"ok"
     assert lib.fl_status_string(1) == b"invalid argument"
     assert lib.fl_status_string(3) == b"launch failed"
