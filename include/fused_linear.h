@@ -297,9 +297,10 @@ fl_status fl_fused_linear_bwd(const void *G, const void *W, const void *X,
                               fl_act act, fl_dtype dtype, void *stream,
                               const fl_options *opt);
 
-/* The backward epilogue with a bias gradient that is the same to the bit
- * from run to run and whatever order the tiles run in (fl_fused_linear_bwd's
- * atomics fix neither).  Same arguments, outputs and errors as
+/* The backward epilogue ("Optimizing GEMM + Activation on CDNA4 with TLX",
+ * "Future Work", as fl_fused_linear_bwd) with a bias gradient that is the
+ * same to the bit from run to run and whatever order the tiles run in
+ * (fl_fused_linear_bwd's atomics fix neither).  Same arguments, outputs and errors as
  * fl_fused_linear_bwd, plus a caller-owned device workspace: each 256-row
  * tile row writes two rows of fp32 partial column sums of dX (one per
  * 128-row half, each summed in a fixed order) into
