@@ -336,8 +336,10 @@ fl_status fl_fused_linear_bwd_ws(const void *G, const void *W, const void *X,
  * N = 16384 still fits) is FL_ERR_UNSUPPORTED with no launch.  On its first
  * call on a device the library looks up that device's copy of the array
  * (FL_ERR_LAUNCH if the lookup fails).  Every call on one GPU uses the same
- * array, so calls that may overlap on one GPU (two streams, two threads)
- * race and must be serialized by the caller.
+ * array and leaves its partial sums there; a call writes every partial sum
+ * it reads before reading it, so nothing needs clearing between calls.
+ * Calls that may overlap on one GPU (two streams, two threads) race on the
+ * array and must be serialized by the caller.
  */
 fl_status fl_fused_linear_bwd_noalloc(const void *G, const void *W,
                                       const void *X, const void *Y, void *dX,
