@@ -318,10 +318,20 @@ fl_status launch_gemm(const void *A, const void *B, const void *bias, const void
 // out[c] = the sum of column c of the rows x n partial sums, added in row
 // order from 0 (the bias gradient from the backward tiles' partial column
 // sums: the same bits whatever order the tiles ran in).
+// Rows are loaded 16 at a time ahead of their additions, so a thread waits
+// for memory once per 16 rows instead of once per row.
 __global__ void sum_rows_f32_kernel(const float *part, int64_t rows, int64_t n, float *out) {
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x) {
         float acc = 0.0f;
-        for (int64_t r = 0; r < rows; ++r) acc += part[r * n + c];
+        int64_t r = 0;
+        for (; r + 16 <= rows; r += 16) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = part[(r + j) * n + c];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc += v[j];
+        }
+        for (; r < rows; ++r) acc += part[r * n + c];
         out[c] = acc;
     }
 }
